@@ -208,11 +208,15 @@ def _summary_keys(k_pool, st, cfg, gen, device):
     return out.to(TORCH_DTYPE[cfg["dtype"]])
 
 
-def make_workload(cfg_id, seed=None, device="cpu", overrides=None, seq_lens=None) -> Workload:
+def make_workload(cfg_id, seed=None, device="cpu", overrides=None, seq_lens=None,
+                  value_seed=None) -> Workload:
     """Build workload ``cfg_id`` (a key of CONFIGS, or a dict) with ``seed``.
 
     ``overrides`` replaces entries of the recipe (used by the tests to shrink a
-    workload while keeping its structure)."""
+    workload while keeping its structure). ``value_seed`` (default ``seed``)
+    seeds the tensor values only, so several layers can share one structure
+    (lengths, thoughts, block table, planted thoughts) with their own K, V,
+    summary keys and queries."""
     cfg = dict(CONFIGS[cfg_id]) if not isinstance(cfg_id, dict) else dict(cfg_id)
     if overrides:
         cfg.update(overrides)
@@ -221,7 +225,7 @@ def make_workload(cfg_id, seed=None, device="cpu", overrides=None, seq_lens=None
     st = make_structure(cfg, seed, seq_lens=seq_lens)
     device = torch.device(device)
     gen = torch.Generator(device=device)
-    gen.manual_seed(int(seed) * 7919 + 17)
+    gen.manual_seed(int(seed if value_seed is None else value_seed) * 7919 + 17)
     dt = TORCH_DTYPE[cfg["dtype"]]
     shape = (st["num_blocks"], cfg["Hkv"], BLOCK_SIZE, cfg["d"])
     k_pool = torch.randn(shape, generator=gen, device=device, dtype=torch.float32).to(dt)

@@ -1,0 +1,242 @@
+"""ctypes binding of libzr (C ABI in include/zr.h).
+
+The functions named like the C entry points (``zr_coarse_score`` ...) only
+marshal arguments: device pointers come from ``torch.Tensor.data_ptr()``, the
+stream from ``torch.cuda.current_stream()``; every step of the decode path
+runs in the library's HIP kernels. There is no fallback: if libzr.so is
+missing or fails to load, ``lib()`` raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libzr.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "zr.h")
+
+ZR_OK, ZR_E_NULL, ZR_E_SHAPE, ZR_E_UNSUPPORTED, ZR_E_WORKSPACE, ZR_E_LAUNCH, ZR_E_ALIGN = range(7)
+ZR_F32, ZR_BF16 = 0, 1
+DTYPE_CODE = {torch.float32: ZR_F32, torch.bfloat16: ZR_BF16}
+
+
+class ZrError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn} -> {status} ({status_string(status)})")
+
+
+class zr_geom(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
+                ("num_blocks", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class zr_thoughts(ctypes.Structure):
+    _fields_ = [("seq_ptr", ctypes.c_void_p), ("start", ctypes.c_void_p),
+                ("len", ctypes.c_void_p), ("summary_keys", ctypes.c_void_p),
+                ("n_total", ctypes.c_int32), ("max_per_seq", ctypes.c_int32)]
+
+
+_P = ctypes.c_void_p
+_G = ctypes.POINTER(zr_geom)
+_T = ctypes.POINTER(zr_thoughts)
+_SIGS = {
+    "zr_coarse_score": (ctypes.c_int, [_G, _P, _T, _P, _P]),
+    "zr_select_topk": (ctypes.c_int, [_G, _T, _P, ctypes.c_int32, _P, _P]),
+    "zr_sparse_decode_attn": (ctypes.c_int, [_G, _P, _P, _P, _P, _P, _T, _P, ctypes.c_int32,
+                                             ctypes.c_int32, ctypes.c_float, ctypes.c_int32,
+                                             _P, _P, ctypes.c_size_t, _P]),
+    "zr_dense_paged_decode_attn": (ctypes.c_int, [_G, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P,
+                                                  ctypes.c_size_t, _P]),
+    "zr_workspace_bytes": (ctypes.c_size_t, [_G, ctypes.c_int32]),
+    "zr_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libzr.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m hierarchical_sparse_kv_amd.build`")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(l, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = l
+    return _lib
+
+
+def header_symbols() -> list[str]:
+    """Entry points declared in include/zr.h."""
+    with open(HEADER) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:zr_status|size_t|const char\*)\s+(zr_\w+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def status_string(status: int) -> str:
+    return lib().zr_status_string(int(status)).decode()
+
+
+# --------------------------------------------------------------------------
+# The entry points, same names as the C ABI. Pointer arguments are ints
+# (device addresses) or None; geom/thoughts are the ctypes structs.
+# --------------------------------------------------------------------------
+def zr_coarse_score(geom, q, th, scores, stream=None) -> int:
+    return lib().zr_coarse_score(ctypes.byref(geom), q, ctypes.byref(th), scores, stream)
+
+
+def zr_select_topk(geom, th, scores, k, sel, stream=None) -> int:
+    return lib().zr_select_topk(ctypes.byref(geom), ctypes.byref(th), scores, int(k), sel, stream)
+
+
+def zr_sparse_decode_attn(geom, q, k_pool, v_pool, block_table, seq_lens, th, sel, k, window,
+                          scale, max_attended, out, workspace, ws_bytes, stream=None) -> int:
+    return lib().zr_sparse_decode_attn(ctypes.byref(geom), q, k_pool, v_pool, block_table,
+                                       seq_lens, ctypes.byref(th), sel, int(k), int(window),
+                                       float(scale), int(max_attended), out, workspace,
+                                       int(ws_bytes), stream)
+
+
+def zr_dense_paged_decode_attn(geom, q, k_pool, v_pool, block_table, seq_lens, scale, out,
+                               workspace, ws_bytes, stream=None) -> int:
+    return lib().zr_dense_paged_decode_attn(ctypes.byref(geom), q, k_pool, v_pool, block_table,
+                                            seq_lens, float(scale), out, workspace,
+                                            int(ws_bytes), stream)
+
+
+def zr_workspace_bytes(geom, max_attended) -> int:
+    return int(lib().zr_workspace_bytes(ctypes.byref(geom), int(max_attended)))
+
+
+# --------------------------------------------------------------------------
+# Torch-side marshalling helpers
+# --------------------------------------------------------------------------
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def check(fn, status):
+    if status != ZR_OK:
+        raise ZrError(fn, status)
+
+
+class DeviceStep:
+    """Device-resident inputs of one decode step plus the structs the C ABI
+    takes. Holds references to every tensor whose address is passed."""
+
+    def __init__(self, q, k_pool, v_pool, block_table, seq_lens, seq_ptr, th_start, th_len,
+                 summary_keys, max_per_seq, k, window, scale, max_attended):
+        dev = q.device
+        i32 = lambda x: torch.as_tensor(np.asarray(x, np.int32) if not torch.is_tensor(x) else x,
+                                        dtype=torch.int32, device=dev).contiguous()
+        self.q = q.contiguous()
+        self.k_pool, self.v_pool = k_pool.contiguous(), v_pool.contiguous()
+        self.block_table = i32(block_table)
+        self.seq_lens = i32(seq_lens)
+        n_total = int(np.asarray(seq_ptr)[-1]) if not torch.is_tensor(seq_ptr) else int(seq_ptr[-1])
+        pad1 = lambda t: t if t.numel() > 0 else torch.zeros(1, dtype=t.dtype, device=dev)
+        self.seq_ptr = i32(seq_ptr)
+        self.th_start, self.th_len = pad1(i32(th_start)), pad1(i32(th_len))
+        self.summary_keys = summary_keys.contiguous()
+        if self.summary_keys.numel() == 0:  # no thoughts at all: a valid, unread buffer
+            self.summary_keys = torch.zeros(16, dtype=summary_keys.dtype, device=dev)
+        B, Hq, d = self.q.shape
+        nb, Hkv = self.k_pool.shape[0], self.k_pool.shape[1]
+        self.geom = zr_geom(B, Hq, Hkv, d, 16, self.block_table.shape[1], nb,
+                            DTYPE_CODE[self.q.dtype])
+        self.th = zr_thoughts(_ptr(self.seq_ptr), _ptr(self.th_start), _ptr(self.th_len),
+                              _ptr(self.summary_keys), n_total, int(max_per_seq))
+        self.k, self.window, self.scale = int(k), int(window), float(scale)
+        self.max_attended = int(max_attended)
+        self.n_total = n_total
+        self.scores = torch.empty((max(self.n_total, 1), Hkv), dtype=torch.float32, device=dev)
+        self.sel = torch.empty((B, Hkv, max(self.k, 0)), dtype=torch.int32, device=dev)
+        self.out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+        ws = max(zr_workspace_bytes(self.geom, self.max_attended),
+                 zr_workspace_bytes(self.geom, self.geom.max_blocks_per_seq * 16))
+        self.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=dev)
+
+    # one call per entry point; all on the current stream
+    def coarse_score(self):
+        check("zr_coarse_score", zr_coarse_score(self.geom, _ptr(self.q), self.th,
+                                                 _ptr(self.scores), _stream()))
+
+    def select_topk(self):
+        check("zr_select_topk", zr_select_topk(self.geom, self.th, _ptr(self.scores), self.k,
+                                               _ptr(self.sel) if self.k else None, _stream()))
+
+    def sparse_attn(self, sel=None, out=None):
+        sel = self.sel if sel is None else sel
+        out = self.out if out is None else out
+        check("zr_sparse_decode_attn", zr_sparse_decode_attn(
+            self.geom, _ptr(self.q), _ptr(self.k_pool), _ptr(self.v_pool),
+            _ptr(self.block_table), _ptr(self.seq_lens), self.th,
+            _ptr(sel) if self.k else None, self.k, self.window, self.scale, self.max_attended,
+            _ptr(out), _ptr(self.workspace), self.workspace.numel(), _stream()))
+
+    def dense_attn(self, out=None):
+        out = self.out if out is None else out
+        check("zr_dense_paged_decode_attn", zr_dense_paged_decode_attn(
+            self.geom, _ptr(self.q), _ptr(self.k_pool), _ptr(self.v_pool),
+            _ptr(self.block_table), _ptr(self.seq_lens), self.scale, _ptr(out),
+            _ptr(self.workspace), self.workspace.numel(), _stream()))
+
+    def step(self):
+        """One sparse decode step: score, select, attend (+ combine)."""
+        self.coarse_score()
+        self.select_topk()
+        self.sparse_attn()
+
+
+def max_attended_bound(seq_lens, seq_ptr, th_len, k, window):
+    """Upper bound on attended tokens per (sequence, KV head): the window plus
+    the k longest thoughts of the sequence, at most the sequence length."""
+    best = 0
+    for b in range(len(seq_lens)):
+        lens = np.sort(np.asarray(th_len[seq_ptr[b]:seq_ptr[b + 1]]))[::-1]
+        best = max(best, min(int(seq_lens[b]), int(window) + int(lens[:k].sum())))
+    return best
+
+
+def step_from_workload(w, k=None):
+    """DeviceStep for a synth.Workload (tensors already on the GPU)."""
+    k = w.k if k is None else k
+    return DeviceStep(w.q, w.k_pool, w.v_pool, w.block_table, w.seq_lens, w.seq_ptr, w.th_start,
+                      w.th_len, w.summary_keys, max(w.max_per_seq, 1), k, w.window, w.scale,
+                      max_attended_bound(w.seq_lens, w.seq_ptr, w.th_len, k, w.window))
+
+
+def attended_counts(sel, seq_lens, seq_ptr, th_start, th_len, window):
+    """Tokens the sparse kernel gathers per (sequence, KV head), from a
+    selection read back to the host: the window [T - W, T) plus each selected
+    thought's span clipped below T - W (every token once). Used for byte
+    accounting; int64 [B][Hkv]."""
+    sel = np.asarray(sel)
+    B, Hkv = sel.shape[0], sel.shape[1]
+    n = np.zeros((B, Hkv), dtype=np.int64)
+    for b in range(B):
+        T = int(seq_lens[b])
+        tw = max(0, T - int(window))
+        lo, hi = int(seq_ptr[b]), int(seq_ptr[b + 1])
+        st = np.asarray(th_start[lo:hi], np.int64)
+        en = st + np.asarray(th_len[lo:hi], np.int64)
+        for g in range(Hkv):
+            idx = sel[b, g][(sel[b, g] >= 0) & (sel[b, g] < hi - lo)]
+            n[b, g] = (T - tw) + int(np.maximum(0, np.minimum(en[idx], tw) - np.maximum(st[idx], 0)).sum())
+    return n

@@ -1,0 +1,179 @@
+/*
+ * zr.h - C ABI of libzr, the MI355X (gfx950) library for one decode step of
+ * hierarchical sparse KV attention ("zoom-in" over reasoning thoughts).
+ *
+ * One step, for every sequence b of a batch and every KV head g:
+ *   1. zr_coarse_score   score the decode query against one mean summary key
+ *                        per generated thought (ZoomR, Sec. 3.3 "Per-Head
+ *                        Importance Scoring", eq. alpha).
+ *   2. zr_select_topk    keep the k best-scoring thoughts (ZoomR, Sec. 3.3,
+ *                        eq. I_top-k).
+ *   3. zr_sparse_decode_attn
+ *                        exact softmax attention over the tokens of the kept
+ *                        thoughts plus a recent window (ZoomR, Sec. 3.3 eq. I_f,
+ *                        Sec. 2 eq. A), read from a paged block pool through a
+ *                        per-sequence block table (KV-cache management page,
+ *                        "Paged KV cache (PagedAttention)").
+ *   zr_dense_paged_decode_attn is the dense baseline: attention over every
+ *   cached token through the same block table (same page, eq. 4).
+ *
+ * Conventions shared by every entry point
+ *   - All array arguments are DEVICE pointers (memory of the current HIP
+ *     device); the zr_geom / zr_thoughts structs themselves are host memory
+ *     and are read during the call only.
+ *   - The caller owns every buffer. The library never allocates, frees or
+ *     synchronizes; each call only enqueues kernels on `stream` (a hipStream_t
+ *     passed as void*, NULL = the legacy default stream) and returns.
+ *   - Host-visible arguments are validated before anything is enqueued; on a
+ *     non-ZR_OK status nothing was enqueued and no output was touched.
+ *     ZR_E_LAUNCH reports a HIP launch error (work may be partially enqueued).
+ *   - Device-resident integer data is the caller's contract (block ids in
+ *     [0, num_blocks), thought spans inside [0, seq_len), seq_len <=
+ *     16 * max_blocks_per_seq, sel entries in [-1, N_b)). The kernels clamp
+ *     or skip entries outside these ranges so that no access leaves the
+ *     buffers, but the result for such entries is unspecified.
+ *   - Calls on one stream run in order; calls that write the same buffers on
+ *     different streams race.
+ *
+ * Data layouts (row-major, innermost last; dtype = zr_geom.dtype)
+ *   q            [batch][n_q_heads][head_dim]                    dtype
+ *   k_pool/v_pool[num_blocks][n_kv_heads][block_size=16][head_dim] dtype
+ *                token j of sequence b, KV head g is row
+ *                pool[block_table[b][j/16]][g][j%16][:]
+ *   block_table  [batch][max_blocks_per_seq]                     int32
+ *   seq_lens     [batch]  cached tokens T_b                      int32
+ *   thoughts     CSR by sequence: thoughts of sequence b are rows
+ *                seq_ptr[b] .. seq_ptr[b+1]-1; a thought is the logical
+ *                token span [start, start+len) (ZoomR's regular segment R_i)
+ *   summary_keys [n_total][n_kv_heads][head_dim]                 dtype
+ *   scores       [n_total][n_kv_heads]                           float32
+ *   sel          [batch][n_kv_heads][k] local thought index, ascending,
+ *                -1 padded                                       int32
+ *   out          [batch][n_q_heads][head_dim]                    float32
+ * Query head h reads KV head h / (n_q_heads / n_kv_heads).
+ */
+#ifndef ZR_H
+#define ZR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ZR_OK = 0,
+  ZR_E_NULL = 1,        /* a required pointer is NULL */
+  ZR_E_SHAPE = 2,       /* sizes inconsistent or out of range */
+  ZR_E_UNSUPPORTED = 3, /* valid request this build has no kernel for */
+  ZR_E_WORKSPACE = 4,   /* workspace NULL or smaller than zr_workspace_bytes() */
+  ZR_E_LAUNCH = 5,      /* the HIP runtime reported an error */
+  ZR_E_ALIGN = 6        /* q, pools or summary keys not 16-byte aligned */
+} zr_status;
+
+typedef enum { ZR_F32 = 0, ZR_BF16 = 1 } zr_dtype;
+
+/* Built limits. */
+#define ZR_BLOCK_SIZE 16
+#define ZR_MAX_K 4096                 /* k of zr_select_topk / zr_sparse_decode_attn */
+#define ZR_MAX_THOUGHTS_PER_SEQ 8192  /* zr_thoughts.max_per_seq */
+#define ZR_MAX_SPLITS 1024            /* split-K partitions per (sequence, KV head) */
+
+typedef struct {
+  int32_t batch;              /* B >= 0 (B = 0: every call is a no-op) */
+  int32_t n_q_heads;          /* Hq > 0, multiple of n_kv_heads */
+  int32_t n_kv_heads;         /* Hkv > 0; Hq / Hkv in {1, 2, 4, 8} */
+  int32_t head_dim;           /* 64 or 128 */
+  int32_t block_size;         /* must be ZR_BLOCK_SIZE (16) */
+  int32_t max_blocks_per_seq; /* columns of block_table, >= 1 */
+  int32_t num_blocks;         /* physical blocks in each pool, >= 1 */
+  int32_t dtype;              /* zr_dtype of q, pools and summary keys */
+} zr_geom;
+
+typedef struct {
+  const int32_t* seq_ptr;     /* device [batch + 1], non-decreasing, seq_ptr[0] = 0 */
+  const int32_t* start;       /* device [n_total] first logical token of each thought */
+  const int32_t* len;         /* device [n_total] tokens in each thought (>= 1) */
+  const void* summary_keys;   /* device [n_total][n_kv_heads][head_dim], dtype */
+  int32_t n_total;            /* = seq_ptr[batch] */
+  int32_t max_per_seq;        /* >= max_b (seq_ptr[b+1] - seq_ptr[b]) */
+} zr_thoughts;
+
+/*
+ * Coarse scorer (ZoomR, Sec. 3.3, eq. alpha, with grouped-query heads):
+ *   scores[i][g] = sum over the query heads h of KV group g of q[b][h] . kbar[i][g]
+ * for every thought i of sequence b. The sum over the group is the plain
+ * GQA reading of a per-head score (one score per KV head). Accumulated in
+ * float64, rounded once to float32. Reads q and summary keys; writes every
+ * row of `scores`.
+ * Errors: ZR_E_NULL (geom, q, th or its pointers, scores), ZR_E_SHAPE,
+ * ZR_E_UNSUPPORTED, ZR_E_ALIGN, ZR_E_LAUNCH.
+ */
+zr_status zr_coarse_score(const zr_geom* geom, const void* q, const zr_thoughts* th,
+                          float* scores, void* stream);
+
+/*
+ * Per-(sequence, KV head) top-k (ZoomR, Sec. 3.3, eq. I_top-k): among the
+ * thoughts of sequence b, keep the min(k, N_b) best under the order
+ * (score descending, then thought index ascending; NaN below every number,
+ * -0 equal to +0), written in ascending thought index to sel[b][g][0..),
+ * the rest of the row filled with -1. k >= N_b keeps every thought; k = 0
+ * writes nothing (sel may then be NULL).
+ * Errors: ZR_E_NULL, ZR_E_SHAPE (k < 0 or > ZR_MAX_K, max_per_seq out of
+ * range), ZR_E_LAUNCH.
+ */
+zr_status zr_select_topk(const zr_geom* geom, const zr_thoughts* th, const float* scores,
+                         int32_t k, int32_t* sel, void* stream);
+
+/*
+ * Zoomed-in sparse decode attention (ZoomR, Sec. 3.3 eq. I_f restricted to
+ * the recent window and the selected thoughts' full-resolution spans; Sec. 2
+ * eq. A). For sequence b, KV head g the attended tokens are
+ *   [T_b - window, T_b)  union  [start_i, start_i + len_i) for i in sel[b][g]
+ * each token once (window clipped at 0). Every query head h of group g gets
+ *   out[b][h] = softmax(scale * q[b][h] . K_j) weighted sum of V_j
+ * over those tokens, with float32 accumulation; an empty token set gives 0.
+ * `sel` rows are read as written by zr_select_topk (k columns, -1 = none);
+ * k = 0 means window only (sel may be NULL).
+ * Split-K: each (b, g) is cut into partitions of the attended token list;
+ * `max_attended` is the caller's bound on tokens per (b, g) used to size the
+ * grid (a larger count is still handled correctly, just with fewer
+ * partitions). `workspace` holds per-partition partial results and must be at
+ * least zr_workspace_bytes(geom, max_attended) bytes (16-byte aligned).
+ * Errors: ZR_E_NULL, ZR_E_SHAPE (k, window, max_attended < 0; k > ZR_MAX_K),
+ * ZR_E_UNSUPPORTED, ZR_E_WORKSPACE, ZR_E_ALIGN, ZR_E_LAUNCH.
+ */
+zr_status zr_sparse_decode_attn(const zr_geom* geom, const void* q, const void* k_pool,
+                                const void* v_pool, const int32_t* block_table,
+                                const int32_t* seq_lens, const zr_thoughts* th,
+                                const int32_t* sel, int32_t k, int32_t window, float scale,
+                                int32_t max_attended, float* out, void* workspace,
+                                size_t ws_bytes, void* stream);
+
+/*
+ * Dense paged decode attention (the baseline): softmax attention of every
+ * query head over all T_b cached tokens of its sequence, read block by block
+ * through the block table (KV-cache management page, eq. 4; ZoomR Sec. 2
+ * eq. A). Same split-K scheme as the sparse call with max_attended =
+ * 16 * max_blocks_per_seq; workspace >= zr_workspace_bytes(geom,
+ * 16 * max_blocks_per_seq).
+ * Errors: as zr_sparse_decode_attn.
+ */
+zr_status zr_dense_paged_decode_attn(const zr_geom* geom, const void* q, const void* k_pool,
+                                     const void* v_pool, const int32_t* block_table,
+                                     const int32_t* seq_lens, float scale, float* out,
+                                     void* workspace, size_t ws_bytes, void* stream);
+
+/* Workspace bytes the attention calls need for a grid sized for
+ * `max_attended` tokens per (sequence, KV head). 0 if geom is invalid. */
+size_t zr_workspace_bytes(const zr_geom* geom, int32_t max_attended);
+
+/* Static, NUL-terminated description of a status code. */
+const char* zr_status_string(zr_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZR_H */

@@ -62,7 +62,7 @@ def gather_logical(pool: np.ndarray, table_row: np.ndarray, n_tokens: int) -> np
     blocks = np.asarray(table_row)[j // BLOCK_SIZE]
     slots = j % BLOCK_SIZE
     # pool[blocks[t], :, slots[t], :] for every t -> [n_tokens][Hkv][d]
-    return np.asarray(pool, dtype=np.float64)[blocks, :, slots, :]
+    return np.asarray(pool)[blocks, :, slots, :].astype(np.float64)
 
 
 # --------------------------------------------------------------------------

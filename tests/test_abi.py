@@ -1,0 +1,111 @@
+"""The C-ABI library loads, exports every entry point include/zr.h declares,
+and rejects bad host-side arguments before enqueuing anything (these calls
+return during validation, so they need no GPU)."""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+from hierarchical_sparse_kv_amd import zr
+
+FAKE = 0x10000  # a 16-byte-aligned non-null address; never dereferenced on error paths
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(zr.LIB_PATH):
+        from hierarchical_sparse_kv_amd import build
+        build.build()
+    return zr.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    declared = zr.header_symbols()
+    assert declared == sorted(["zr_coarse_score", "zr_select_topk", "zr_sparse_decode_attn",
+                               "zr_dense_paged_decode_attn", "zr_workspace_bytes",
+                               "zr_status_string"])
+    out = subprocess.run(["nm", "-D", "--defined-only", zr.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = sorted(l.split()[-1] for l in out.splitlines() if l.split()[-2] == "T")
+    assert exported == declared
+    for name in declared:
+        assert hasattr(L, name)
+
+
+def test_status_strings(L):
+    for s in range(7):
+        assert zr.status_string(s)
+    assert zr.status_string(99) == "unknown zr_status"
+
+
+def _geom(**kw):
+    d = dict(batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, block_size=16,
+             max_blocks_per_seq=4, num_blocks=8, dtype=zr.ZR_BF16)
+    d.update(kw)
+    return zr.zr_geom(**d)
+
+
+def _th(**kw):
+    d = dict(seq_ptr=FAKE, start=FAKE, len=FAKE, summary_keys=FAKE, n_total=5, max_per_seq=3)
+    d.update(kw)
+    return zr.zr_thoughts(**d)
+
+
+def test_workspace_bytes(L):
+    g = _geom()
+    n = zr.zr_workspace_bytes(g, 1000)
+    # 1000 tokens at 256 per partition -> 4 partitions; rows = B*Hkv*S*G
+    rows = 2 * 2 * 4 * 4
+    assert n == ((2 * rows * 4 + 15) // 16) * 16 + rows * 128 * 4
+    assert zr.zr_workspace_bytes(_geom(head_dim=96), 10) == 0
+    assert zr.zr_workspace_bytes(g, -1) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_q_heads=6, n_kv_heads=4), zr.ZR_E_SHAPE),
+    (dict(n_q_heads=48, n_kv_heads=2), zr.ZR_E_UNSUPPORTED),
+    (dict(head_dim=96), zr.ZR_E_UNSUPPORTED),
+    (dict(block_size=32), zr.ZR_E_UNSUPPORTED),
+    (dict(dtype=7), zr.ZR_E_UNSUPPORTED),
+    (dict(batch=-1), zr.ZR_E_SHAPE),
+    (dict(num_blocks=0), zr.ZR_E_SHAPE),
+])
+def test_geometry_rejected(L, kw, code):
+    g = _geom(**kw)
+    assert zr.zr_coarse_score(g, FAKE, _th(), FAKE) == code
+    assert zr.zr_sparse_decode_attn(g, FAKE, FAKE, FAKE, FAKE, FAKE, _th(), FAKE, 2, 16, 0.1,
+                                    100, FAKE, FAKE, 1 << 20) == code
+    assert zr.zr_dense_paged_decode_attn(g, FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, FAKE,
+                                         1 << 20) == code
+
+
+def test_null_and_range_errors(L):
+    g = _geom()
+    assert zr.lib().zr_coarse_score(None, FAKE, ctypes.byref(_th()), FAKE, None) == zr.ZR_E_NULL
+    assert zr.zr_coarse_score(g, None, _th(), FAKE) == zr.ZR_E_NULL
+    assert zr.zr_coarse_score(g, FAKE, _th(summary_keys=None), FAKE) == zr.ZR_E_NULL
+    assert zr.zr_coarse_score(g, FAKE + 4, _th(), FAKE) == zr.ZR_E_ALIGN
+    assert zr.zr_coarse_score(g, FAKE, _th(max_per_seq=100000), FAKE) == zr.ZR_E_UNSUPPORTED
+    assert zr.zr_select_topk(g, _th(), FAKE, -1, FAKE) == zr.ZR_E_SHAPE
+    assert zr.zr_select_topk(g, _th(), FAKE, 5000, FAKE) == zr.ZR_E_SHAPE
+    assert zr.zr_select_topk(g, _th(), FAKE, 3, None) == zr.ZR_E_NULL
+    assert zr.zr_select_topk(g, _th(seq_ptr=None), FAKE, 3, FAKE) == zr.ZR_E_NULL
+    args = lambda **kw: dict(dict(geom=g, q=FAKE, k_pool=FAKE, v_pool=FAKE, block_table=FAKE,
+                                  seq_lens=FAKE, th=_th(), sel=FAKE, k=2, window=16, scale=0.1,
+                                  max_attended=100, out=FAKE, workspace=FAKE,
+                                  ws_bytes=1 << 20), **kw)
+    sp = lambda **kw: zr.zr_sparse_decode_attn(**args(**kw))
+    assert sp(k=-1) == zr.ZR_E_SHAPE
+    assert sp(window=-1) == zr.ZR_E_SHAPE
+    assert sp(max_attended=-5) == zr.ZR_E_SHAPE
+    assert sp(scale=float("nan")) == zr.ZR_E_SHAPE
+    assert sp(sel=None) == zr.ZR_E_NULL
+    assert sp(out=None) == zr.ZR_E_NULL
+    assert sp(v_pool=FAKE + 8) == zr.ZR_E_ALIGN
+    assert sp(workspace=None) == zr.ZR_E_WORKSPACE
+    assert sp(ws_bytes=16) == zr.ZR_E_WORKSPACE
+    need = zr.zr_workspace_bytes(g, 100)
+    assert sp(ws_bytes=need - 1) == zr.ZR_E_WORKSPACE
+    assert zr.zr_dense_paged_decode_attn(g, FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, FAKE, 64) \
+        == zr.ZR_E_WORKSPACE

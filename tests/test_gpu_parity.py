@@ -1,0 +1,197 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Every workload is generated on the GPU from its seed, copied to the host for
+the oracle, and run through zr_coarse_score -> zr_select_topk ->
+zr_sparse_decode_attn (and zr_dense_paged_decode_attn) with the same launch
+configuration the benchmark uses. Bars: scores within one float32 ulp (bit
+exact for bf16 inputs, where the float64 sums are exact), selection bit-exact
+apart from logged near-ties, outputs within max-abs 1e-5 (fp32 inputs) or
+2e-3 (bf16 inputs).
+"""
+import json
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from hierarchical_sparse_kv_amd import synth, zr
+from oracle import zr_oracle as O
+from tests import parity_helpers as P
+
+pytestmark = pytest.mark.gpu
+
+OUT_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out")
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    zr.lib()  # raises if the HIP library was not built
+    yield
+    torch.cuda.synchronize()
+
+
+def _log_events(name, events):
+    if not events:
+        return
+    os.makedirs(OUT_DIR, exist_ok=True)
+    with open(os.path.join(OUT_DIR, "near_ties.jsonl"), "a") as f:
+        for e in events:
+            f.write(json.dumps({"case": name, **e}) + "\n")
+    say(f"[near-tie] {name}: {len(events)} events logged")
+
+
+def run_and_check(w, name, k=None, check_dense=False):
+    """Full sparse step on the GPU vs the oracle (all outputs)."""
+    k = w.k if k is None else k
+    st = zr.step_from_workload(w, k=k)
+    say(f"[gpu] {name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} d={w.d} {w.dtype} k={k} W={w.window} "
+        f"n_total={w.n_total} max_attended={st.max_attended}")
+    st.step()
+    torch.cuda.synchronize()
+    scores = st.scores.cpu().numpy()[:w.n_total]
+    sel = st.sel.cpu().numpy()
+    out = st.out.cpu().numpy()
+    h = P.host(w)
+    ref = P.oracle_step(w, h, k=k)
+    # scores: within one ulp (float64 sums differ only in rounding order)
+    ulp = np.spacing(np.abs(ref["scores"]).astype(np.float32))
+    assert np.all(np.abs(scores - ref["scores"]) <= ulp), name
+    if w.dtype == "bf16":
+        assert np.array_equal(scores, ref["scores"]), name
+    events = P.compare_selection(sel, ref["scores"], w.seq_ptr, k, w.Hkv)
+    _log_events(name, events)
+    if events:
+        ref = P.oracle_step(w, h, sel=sel, k=k)  # outputs on the GPU's own selection
+    err = np.max(np.abs(out - ref["out"]))
+    say(f"[gpu] {name}: max|out-oracle| = {err:.3e} (tol {P.TOL[w.dtype]})")
+    assert err <= P.TOL[w.dtype], name
+    if check_dense:
+        st.dense_attn()
+        torch.cuda.synchronize()
+        dense = st.out.cpu().numpy()
+        ref_d = O.dense_decode_step(h["q"], h["k_pool"], h["v_pool"], w.block_table, w.seq_lens,
+                                    w.scale)
+        err_d = np.max(np.abs(dense - ref_d))
+        say(f"[gpu] {name}: dense max|out-oracle| = {err_d:.3e}")
+        assert err_d <= P.TOL[w.dtype], name
+    return st, ref, events
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 3])
+def test_workload_parity(cfg):
+    w = synth.make_workload(cfg, device="cuda")
+    run_and_check(w, f"cfg{cfg}", check_dense=(cfg == 0))
+
+
+def test_dense_workload_parity_and_sparse_all_equals_dense():
+    """k = all thoughts through the sparse path, the dense kernel, and the
+    oracle's dense attention all agree (config 2: config 1's cache)."""
+    w = synth.make_workload(2, device="cuda")
+    st, ref, _ = run_and_check(w, "cfg2", check_dense=True)
+    sparse = st.out.clone()
+    st.dense_attn()
+    torch.cuda.synchronize()
+    assert torch.max(torch.abs(sparse - st.out)).item() <= 1e-4
+    assert np.all(ref["n_attended"] == w.seq_lens[:, None])
+
+
+def test_long_output_near_ties():
+    """64K tokens, k = 16, with exact and near-tied distractors at the 16th score."""
+    w = synth.make_workload(4, device="cuda")
+    counts = P.plant_near_ties(w)
+    say(f"[gpu] cfg4 planted ties: {counts}")
+    assert counts["exact"] >= 16 and counts["tiny"] >= 8 and counts["small"] >= 8
+    run_and_check(w, "cfg4")
+
+
+def test_physical_block_permutation_is_bit_identical():
+    """Same logical cache, different physical placement: identical outputs
+    (partition boundaries depend on logical positions only)."""
+    w = synth.make_workload(1, device="cuda", overrides=dict(B=2, seq_len=("fixed", 4096)))
+    st = zr.step_from_workload(w)
+    st.step()
+    out1 = st.out.clone()
+    rng = np.random.default_rng(123)
+    perm = rng.permutation(w.num_blocks)
+    inv = np.argsort(perm)
+    kp = torch.empty_like(w.k_pool)
+    vp = torch.empty_like(w.v_pool)
+    pt = torch.as_tensor(perm, device="cuda")
+    kp[pt] = w.k_pool
+    vp[pt] = w.v_pool
+    table = np.where(w.block_table >= 0, perm[np.maximum(w.block_table, 0)], -1).astype(np.int32)
+    assert np.array_equal(inv[perm], np.arange(w.num_blocks))
+    st2 = zr.DeviceStep(w.q, kp, vp, table, w.seq_lens, w.seq_ptr, w.th_start, w.th_len,
+                        w.summary_keys, w.max_per_seq, w.k, w.window, w.scale, st.max_attended)
+    st2.step()
+    torch.cuda.synchronize()
+    assert torch.equal(st.sel, st2.sel)
+    assert torch.equal(out1, st2.out)
+
+
+# ------------------------------------------------------------------ edge cases
+def _small(cfg, **over):
+    base = dict(B=3, seq_len=("uniform", 200, 900), thought=("uniform", 8, 120))
+    base.update(over)
+    return synth.make_workload(cfg if cfg != 0 else 0, device="cuda", overrides=base)
+
+
+@pytest.mark.parametrize("dtype,d,Hq,Hkv", [("bf16", 128, 32, 8), ("bf16", 64, 8, 8),
+                                             ("bf16", 128, 16, 8), ("f32", 128, 8, 1),
+                                             ("f32", 64, 16, 2), ("bf16", 64, 4, 2)])
+def test_shapes_and_dtypes(dtype, d, Hq, Hkv):
+    w = _small(1, dtype=dtype, d=d, Hq=Hq, Hkv=Hkv)
+    run_and_check(w, f"shape-{dtype}-d{d}-G{Hq // Hkv}", check_dense=True)
+
+
+@pytest.mark.parametrize("k,window", [(0, 32), (3, 0), (0, 5000), (50, 16), (1, 1)])
+def test_k_and_window_edges(k, window):
+    w = _small(1, window=window, k=k)
+    run_and_check(w, f"k{k}-W{window}", k=k)
+
+
+def test_ragged_tiny_sequences_and_empty_sets():
+    """T = 0, 1, 15, 16, 17 and a long one; window 0 with k = 0 gives an
+    empty token set (zero output)."""
+    w = synth.make_workload(1, device="cuda", seq_lens=[0, 1, 15, 16, 17, 700],
+                            overrides=dict(B=6, thought=("uniform", 1, 40)))
+    run_and_check(w, "ragged-tiny", check_dense=True)
+    w0 = synth.make_workload(1, device="cuda", seq_lens=[0, 1, 40],
+                             overrides=dict(B=3, thought=("uniform", 1, 9), window=0))
+    st, _, _ = run_and_check(w0, "empty-set", k=0)
+    assert torch.count_nonzero(st.out).item() == 0
+
+
+def test_many_thoughts_per_sequence_and_exact_ties():
+    """Thousands of 1-4 token thoughts (a long radix select) and summary keys
+    duplicated so that scores tie exactly (lower index must win)."""
+    w = synth.make_workload(1, device="cuda", overrides=dict(B=2, seq_len=("fixed", 6000),
+                                                             thought=("uniform", 1, 4), k=37))
+    kb = w.summary_keys
+    for b in range(w.B):
+        lo, hi = int(w.seq_ptr[b]), int(w.seq_ptr[b + 1])
+        kb[lo + 1:hi:3] = kb[lo:hi - 1:3][: len(range(lo + 1, hi, 3))]
+    run_and_check(w, "many-thoughts-ties")
+
+
+def test_small_grid_loops_over_chunks():
+    """A max_attended far below the real count: each workgroup walks several
+    chunks (online softmax across chunks) and the result is unchanged."""
+    w = _small(1)
+    st = zr.step_from_workload(w)
+    st.step()
+    torch.cuda.synchronize()
+    full = st.out.clone()
+    st.max_attended = 1
+    st.sparse_attn()
+    torch.cuda.synchronize()
+    assert torch.max(torch.abs(full - st.out)).item() <= 1e-5
