@@ -19,7 +19,8 @@ zr_status check_geom(const zr_geom* g) {
     return ZR_E_SHAPE;
   if (g->n_q_heads % g->n_kv_heads != 0) return ZR_E_SHAPE;
   const int G = g->n_q_heads / g->n_kv_heads;
-  if (G != 1 && G != 2 && G != 4 && G != 8) return ZR_E_UNSUPPORTED;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return ZR_E_UNSUPPORTED;
+  if (G == 16 && g->dtype != ZR_BF16) return ZR_E_UNSUPPORTED;
   if (g->head_dim != 64 && g->head_dim != 128) return ZR_E_UNSUPPORTED;
   if (g->block_size != ZR_BLOCK_SIZE) return ZR_E_UNSUPPORTED;
   if (g->dtype != ZR_F32 && g->dtype != ZR_BF16) return ZR_E_UNSUPPORTED;
@@ -41,52 +42,30 @@ zr_status check_thoughts(const zr_thoughts* th, bool need_keys) {
   return ZR_OK;
 }
 
-int splits_for(const zr_geom& g, int32_t max_attended) {
-  const int per = zr::attn_tokens_per_split(g);
-  int64_t s = (static_cast<int64_t>(max_attended) + per - 1) / per;
-  if (s < 1) s = 1;
-  if (s > ZR_MAX_SPLITS) s = ZR_MAX_SPLITS;
-  return static_cast<int>(s);
-}
-
-size_t workspace_for(const zr_geom& g, int splits) {
-  const size_t G = static_cast<size_t>(g.n_q_heads / g.n_kv_heads);
-  const size_t rows = static_cast<size_t>(g.batch) * g.n_kv_heads * splits * G;
-  // m, l, then acc [rows][head_dim]; the acc region starts 16-byte aligned
-  size_t ml = 2 * rows * sizeof(float);
-  ml = (ml + 15) & ~static_cast<size_t>(15);
-  return ml + rows * g.head_dim * sizeof(float);
-}
-
 zr_status attention_common(const zr_geom* geom, const void* q, const void* k_pool,
                            const void* v_pool, const int32_t* block_table,
                            const int32_t* seq_lens, float scale, float* out, void* workspace,
-                           size_t ws_bytes, int32_t max_attended, zr::AttnArgs* a,
-                           int* splits) {
+                           size_t ws_bytes, int32_t max_attended, zr::AttnArgs* a) {
   zr_status st = check_geom(geom);
   if (st != ZR_OK) return st;
   if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !out) return ZR_E_NULL;
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool)) return ZR_E_ALIGN;
   if (max_attended < 0) return ZR_E_SHAPE;
   if (!isfinite(scale)) return ZR_E_SHAPE;
-  *splits = splits_for(*geom, max_attended);
-  const size_t need = workspace_for(*geom, *splits);
+  if (static_cast<int64_t>(geom->batch) * geom->n_kv_heads > ZR_MAX_PAIRS)
+    return ZR_E_UNSUPPORTED;
+  const int nwg = zr::attn_workgroups(*geom, max_attended);
+  const size_t need = zr::attn_workspace(*geom, nwg, nullptr, nullptr);
   if (geom->batch > 0 && (!workspace || ws_bytes < need || !aligned16(workspace)))
     return ZR_E_WORKSPACE;
-  const size_t G = static_cast<size_t>(geom->n_q_heads / geom->n_kv_heads);
-  const size_t rows = static_cast<size_t>(geom->batch) * geom->n_kv_heads * (*splits) * G;
-  size_t ml = 2 * rows * sizeof(float);
-  ml = (ml + 15) & ~static_cast<size_t>(15);
-  char* ws = static_cast<char*>(workspace);
+  zr::attn_workspace(*geom, nwg, workspace, a);
   a->q = q;
   a->k_pool = k_pool;
   a->v_pool = v_pool;
   a->block_table = block_table;
   a->seq_lens = seq_lens;
-  a->ws_m = reinterpret_cast<float*>(ws);
-  a->ws_l = reinterpret_cast<float*>(ws) + rows;
-  a->ws_acc = reinterpret_cast<float*>(ws + ml);
   a->out = out;
+  a->B = geom->batch;
   a->Hq = geom->n_q_heads;
   a->Hkv = geom->n_kv_heads;
   a->max_blocks = geom->max_blocks_per_seq;
@@ -112,7 +91,8 @@ ZR_API const char* zr_status_string(zr_status s) {
 
 ZR_API size_t zr_workspace_bytes(const zr_geom* geom, int32_t max_attended) {
   if (check_geom(geom) != ZR_OK || max_attended < 0) return 0;
-  return workspace_for(*geom, splits_for(*geom, max_attended));
+  if (static_cast<int64_t>(geom->batch) * geom->n_kv_heads > ZR_MAX_PAIRS) return 0;
+  return zr::attn_workspace(*geom, zr::attn_workgroups(*geom, max_attended), nullptr, nullptr);
 }
 
 ZR_API zr_status zr_coarse_score(const zr_geom* geom, const void* q, const zr_thoughts* th,
@@ -155,10 +135,10 @@ ZR_API zr_status zr_sparse_decode_attn(const zr_geom* geom, const void* q, const
   if (st != ZR_OK) return st;
   if (k < 0 || k > ZR_MAX_K || window < 0) return ZR_E_SHAPE;
   if (k > 0 && !sel) return ZR_E_NULL;
+  if (!zr::attn_lds_ok(*geom, k, false)) return ZR_E_UNSUPPORTED;
   zr::AttnArgs a{};
-  int splits = 1;
   st = attention_common(geom, q, k_pool, v_pool, block_table, seq_lens, scale, out, workspace,
-                        ws_bytes, max_attended, &a, &splits);
+                        ws_bytes, max_attended, &a);
   if (st != ZR_OK) return st;
   a.seq_ptr = th->seq_ptr;
   a.th_start = th->start;
@@ -167,7 +147,7 @@ ZR_API zr_status zr_sparse_decode_attn(const zr_geom* geom, const void* q, const
   a.n_total = th->n_total;
   a.k = k;
   a.window = window;
-  if (zr::launch_attention(*geom, a, splits, false, static_cast<hipStream_t>(stream)) !=
+  if (zr::launch_attention(*geom, a, false, static_cast<hipStream_t>(stream)) !=
       hipSuccess)
     return ZR_E_LAUNCH;
   return ZR_OK;
@@ -180,12 +160,12 @@ ZR_API zr_status zr_dense_paged_decode_attn(const zr_geom* geom, const void* q,
                                             size_t ws_bytes, void* stream) {
   zr_status st = check_geom(geom);
   if (st != ZR_OK) return st;
+  if (!zr::attn_lds_ok(*geom, 0, true)) return ZR_E_UNSUPPORTED;
   zr::AttnArgs a{};
-  int splits = 1;
   st = attention_common(geom, q, k_pool, v_pool, block_table, seq_lens, scale, out, workspace,
-                        ws_bytes, geom->max_blocks_per_seq * ZR_BLOCK_SIZE, &a, &splits);
+                        ws_bytes, geom->max_blocks_per_seq * ZR_BLOCK_SIZE, &a);
   if (st != ZR_OK) return st;
-  if (zr::launch_attention(*geom, a, splits, true, static_cast<hipStream_t>(stream)) !=
+  if (zr::launch_attention(*geom, a, true, static_cast<hipStream_t>(stream)) !=
       hipSuccess)
     return ZR_E_LAUNCH;
   return ZR_OK;

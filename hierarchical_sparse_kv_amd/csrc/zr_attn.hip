@@ -1,272 +1,385 @@
 // Split-K decode attention over a paged KV pool, sparse ("zoomed-in") and dense.
 //
-// The attended token list of one (sequence b, KV head g) is
-//   sparse: the selected thoughts' spans [start, start+len) clipped below
-//           T - window, in the order of `sel`, followed by the window
-//           [T - window, T)  (ZoomR Sec. 3.3 eq. I_f restricted to I_w and R_i;
-//           clipping makes the union count every token once);
+// Attended tokens of one (sequence b, KV head g), a "pair":
+//   sparse: each selected thought's span [start, start+len) clipped below
+//           T - window, then the window [T - window, T)  (ZoomR Sec. 3.3,
+//           eq. I_f restricted to the window and the full-resolution spans;
+//           the clip makes the union count each token once);
 //   dense:  [0, T).
-// Each token j is read through the block table, row
-// pool[block_table[b][j / 16]][g][j % 16][:] (KV-cache management page,
-// paged KV cache, eq. 4), so only the attended rows are fetched: the gather
-// reads the kept entries instead of masking the full cache.
+// The spans are cut at the 16-token block boundaries of the paged cache
+// (KV-cache management page, paged KV cache, eq. 4: attention as a sum over
+// blocks fetched through the block table). A pair's work list is the sequence
+// of (logical block, 16-bit slot mask) entries over its spans; only attended
+// slots are fetched (the gather reads kept entries, it does not mask a full
+// read).
 //
-// Work split. The list is cut into chunks of 4 * CW positions; workgroup
-// (split, g, b) handles chunks split, split + S, ... and keeps a running
-// (max, sum, weighted V) per query head (online softmax across chunks, a
-// two-pass softmax inside a chunk). Each of its four waves resolves CW
-// positions (one per lane: binary search of the span prefix sums, block
-// table lookup), then loads the K and V rows with 16-byte loads, LPR lanes
-// per row (LPR = head_dim * elem_bytes / 16), so a row is one contiguous,
-// coalesced segment. Logits are reduced across the row's lanes with lane
-// shuffles. The waves merge in LDS and write one partial per workgroup; the
-// combine kernel merges the S partials of each (b, g) by log-sum-exp.
-// Exponentials use base 2 with the scale folded into q (exp(x) = 2^(x log2 e)).
+// Work split. The grid is sized once for the whole GPU (about `nwg`
+// workgroups). Every workgroup stages the plan inputs (sequence lengths,
+// selections, thought spans) in LDS with one round of independent loads,
+// counts every pair's blocks (one item per (pair, span), LDS atomics), and
+// gives pair p a number of workgroups proportional to its block count,
+// S_p = max(1, round(n_p / per)), per = ceil(total / nwg). Each workgroup
+// thus serves exactly one pair with about `per` blocks, however ragged the
+// pairs are. Its 4 waves take chunks of NBW blocks in turn: a wave resolves
+// all its block-table entries at once (one lane per entry), then streams its
+// chunks with the next chunk's K/V loads in flight while the current one is
+// computed, keeping a running (max, sum, weighted V) per query head (online
+// softmax across chunks, two-pass inside one). The waves merge in LDS into
+// one partial per workgroup; a combine kernel merges each pair's partials by
+// log-sum-exp. (Merging inside the attention kernel would need a device-scope
+// release/acquire per workgroup, which on this GPU writes back and
+// invalidates the whole L2; the kernel boundary is far cheaper.)
+//
+// bf16 kernel (matrix cores). With the block's 16 slots as the rows:
+//   S^T[slot][head] = K_block (16 x d) . Q^T (d x 16 heads, zero padded)
+// on v_mfma_f32_16x16x32_bf16. In the output layout each lane holds four
+// consecutive slots of one head, which is exactly the A-operand layout of
+//   O[head][dim] += P[head][slot] . V[slot][dim]
+// on v_mfma_f32_16x16x16_bf16, so P never leaves the lane. V blocks are stored
+// dimension-major, so each lane's B operand (4 slots of one dimension) is one
+// 8-byte load and a wave reads a block's values as contiguous 512-byte
+// segments. P is split into bf16 hi + lo parts (p - hi rounded again), so the
+// probabilities keep ~16 significant bits; products accumulate in fp32.
+//
+// fp32 kernel (vector ALU): key rows are read with 16-byte loads, LPR lanes per
+// row, logits reduced across the row's lanes with shuffles; probabilities go
+// through LDS and each lane accumulates the values of its own dimensions.
+//
+// Exponentials are base 2 with the scale folded in (exp(x) = 2^(x log2 e)).
 #include <math.h>
 
 #include "zr_internal.h"
 
 namespace zr {
 
-constexpr int kAttnThreads = 256;
-constexpr int kWaves = kAttnThreads / 64;
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr float kNegInf = -INFINITY;
+constexpr int kTargetWorkgroups = 512;  // two per CU on MI355X: one resident round
+constexpr int kMinBlocksPerWg = 8;
+constexpr int kStageCap = 8192;         // ints of selections / spans staged in LDS
 
-template <typename E, int D>
-struct AttnShape {
-  static constexpr int VPL = 16 / E::kBytes;     // values per 16-byte lane load
-  static constexpr int LPR = D / VPL;            // lanes per K/V row
-  static constexpr int RPW = 64 / LPR;           // rows per wave load
-  static constexpr int CW = LPR <= 16 ? 64 : 32; // positions per wave per chunk
-  static constexpr int NRG = CW / RPW;           // wave loads per chunk (each of K, V)
-  static constexpr int CWG = kWaves * CW;        // positions per workgroup chunk
+typedef short bf16x8 __attribute__((vector_size(16)));
+typedef short bf16x4 __attribute__((vector_size(8)));
+typedef float f32x4 __attribute__((vector_size(16)));
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------------------
+// Plan inputs (LDS copies when they fit, else global memory)
+// ---------------------------------------------------------------------------
+struct Stage {
+  const int32_t* seq_ptr;
+  const int32_t* seq_lens;
+  const int32_t* sel;
+  const int32_t* th_s;
+  const int32_t* th_l;
 };
 
-// Sum over the LPR consecutive lanes that hold one row.
-template <int LPR>
-__device__ __forceinline__ float row_sum(float v) {
-#pragma unroll
-  for (int o = LPR / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+// Dynamic LDS layout (int32): cnt[P+1] prefS[P+1] seq_ptr[B+1] seq_lens[B]
+// [sel[P*k] th_s[n] th_l[n] when staged] plan s/e/pref[3*(k+2)]
+// [block-table row[max_blocks] when row_lds].
+__host__ __device__ inline size_t lds_ints(int B, int Hkv, int k, int n_total, bool dense,
+                                           bool staged, int row_ints) {
+  const size_t P = static_cast<size_t>(B) * Hkv;
+  size_t n = 2 * (P + 1) + 2 * static_cast<size_t>(B) + 1;
+  if (!dense && staged) n += P * k + 2 * static_cast<size_t>(n_total);
+  n += 3 * static_cast<size_t>((dense ? 0 : k) + 2);
+  n += static_cast<size_t>(row_ints);
+  return n;
 }
 
-// Sum / max over the row slots: lanes that hold the same columns of
-// different rows (lane, lane + LPR, lane + 2 LPR, ...).
-template <int LPR>
-__device__ __forceinline__ float slot_sum(float v) {
-#pragma unroll
-  for (int o = LPR; o < 64; o <<= 1) v += __shfl_xor(v, o);
-  return v;
+struct LdsLayout {
+  int32_t* cnt;    // [P]; cnt[P] accumulates the total
+  int32_t* prefS;
+  Stage st;
+  int32_t* plan_s;
+  int32_t* plan_e;
+  int32_t* plan_pref;
+  int32_t* row;    // this workgroup's block-table row (when a.row_lds)
+};
+
+template <bool DENSE, bool STAGED>
+__device__ LdsLayout stage_inputs(const AttnArgs& a, int32_t* dyn) {
+  const int P = a.B * a.Hkv;
+  const int t = threadIdx.x;
+  LdsLayout L;
+  int32_t* c = dyn;
+  L.cnt = c;
+  c += P + 1;
+  L.prefS = c;
+  c += P + 1;
+  int32_t* sp = c;
+  c += a.B + 1;
+  int32_t* sl = c;
+  c += a.B;
+  for (int i = t; i <= a.B; i += kThreads) sp[i] = DENSE ? 0 : a.seq_ptr[i];
+  for (int i = t; i < a.B; i += kThreads) sl[i] = a.seq_lens[i];
+  for (int p = t; p <= P; p += kThreads) L.cnt[p] = 0;
+  L.st.seq_ptr = sp;
+  L.st.seq_lens = sl;
+  L.st.sel = a.sel;
+  L.st.th_s = a.th_start;
+  L.st.th_l = a.th_len;
+  if (!DENSE && STAGED) {
+    const int n = P * a.k;
+    for (int i = t; i < n; i += kThreads) c[i] = a.sel[i];
+    L.st.sel = c;
+    c += n;
+    for (int i = t; i < a.n_total; i += kThreads) {
+      c[i] = a.th_start[i];
+      c[a.n_total + i] = a.th_len[i];
+    }
+    L.st.th_s = c;
+    L.st.th_l = c + a.n_total;
+    c += 2 * a.n_total;
+  }
+  const int cap = (DENSE ? 0 : a.k) + 2;
+  L.plan_s = c;
+  L.plan_e = c + cap;
+  L.plan_pref = c + 2 * cap;
+  L.row = c + 3 * cap;
+  return L;
 }
 
-template <int LPR>
-__device__ __forceinline__ float slot_max(float v) {
-#pragma unroll
-  for (int o = LPR; o < 64; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+// ---------------------------------------------------------------------------
+// Spans of a pair
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int blocks_of(int s, int e) {
+  return e > s ? ((e - 1) >> 4) - (s >> 4) + 1 : 0;
 }
 
-template <typename E, int D, int G, bool DENSE>
-__global__ void __launch_bounds__(kAttnThreads)
-attn_partial_kernel(AttnArgs a) {
-  using Sh = AttnShape<E, D>;
-  using St = typename E::storage;
-  constexpr int VPL = Sh::VPL, LPR = Sh::LPR, RPW = Sh::RPW, CW = Sh::CW, NRG = Sh::NRG,
-                CWG = Sh::CWG;
-  constexpr float kNegInf = -INFINITY;
+__device__ __forceinline__ int cached_len(const AttnArgs& a, const Stage& st, int b) {
+  const int T = st.seq_lens[b];
+  const int cap = a.max_blocks * kBlock;
+  return T < 0 ? 0 : (T > cap ? cap : T);
+}
 
-  extern __shared__ int32_t span_mem[];  // starts [k + 2] then prefix sums [k + 2]
-  __shared__ float red_m[kWaves][G];
-  __shared__ float red_l[kWaves][G];
-  __shared__ float red_acc[kWaves][G][D];
-  __shared__ int sh_nspans;
+// Span i (< k: selected thought i, == k: the window) of pair (b, g), clipped.
+__device__ __forceinline__ void pair_span(const AttnArgs& a, const Stage& st, int b, int g,
+                                          int i, int T, int tw, int* s, int* e) {
+  if (i == a.k) {
+    *s = tw;
+    *e = T;
+    return;
+  }
+  *s = 0;
+  *e = 0;
+  const int lo = st.seq_ptr[b];
+  int hi = st.seq_ptr[b + 1];
+  hi = hi < a.n_total ? hi : a.n_total;
+  const int t = st.sel[(static_cast<size_t>(b) * a.Hkv + g) * a.k + i];
+  if (t < 0 || t >= hi - lo) return;
+  int ss = st.th_s[lo + t];
+  int ee = ss + st.th_l[lo + t];
+  ss = ss > 0 ? ss : 0;
+  ee = ee < tw ? ee : tw;
+  *s = ss;
+  *e = ee > ss ? ee : ss;
+}
 
-  const int b = blockIdx.z, g = blockIdx.y, split = blockIdx.x, nsplit = gridDim.x;
+// Exclusive prefix sum across the workgroup (one value per thread).
+__device__ int wg_exclusive_scan(int v, int* tmp, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int T = a.seq_lens[b];
-  T = T < 0 ? 0 : (T > a.max_blocks * kBlock ? a.max_blocks * kBlock : T);
-  const int tw = T - a.window > 0 ? T - a.window : 0;
-  int32_t* sp_start = span_mem;
-  int32_t* sp_pref = span_mem + (DENSE ? 2 : a.k + 2);
-
-  // ---- attended spans of (b, g) and their exclusive prefix sums ----
-  if (DENSE) {
-    if (threadIdx.x == 0) {
-      sp_start[0] = 0;
-      sp_pref[0] = 0;
-      sp_pref[1] = T;
-      sh_nspans = 1;
-    }
-  } else if (wave == 0) {
-    const int lo = a.seq_ptr[b];
-    int hi = a.seq_ptr[b + 1];
-    hi = hi < a.n_total ? hi : a.n_total;
-    const int n_b = hi - lo > 0 ? hi - lo : 0;
-    const int32_t* srow = a.sel + (static_cast<size_t>(b) * a.Hkv + g) * a.k;
-    int run = 0;
-    for (int base = 0; base < a.k; base += 64) {
-      const int i = base + lane;
-      int s = 0, len = 0;
-      if (i < a.k) {
-        const int t = srow[i];
-        if (t >= 0 && t < n_b) {
-          s = a.th_start[lo + t];
-          int e = s + a.th_len[lo + t];
-          s = s > 0 ? s : 0;
-          e = e < tw ? e : tw;
-          len = e - s > 0 ? e - s : 0;
-        }
-      }
-      int incl = len;
+  int incl = v;
 #pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int v = __shfl_up(incl, o);
-        if (lane >= o) incl += v;
-      }
-      if (i < a.k) {
-        sp_start[i] = s;
-        sp_pref[i] = run + incl - len;
-      }
-      run += __shfl(incl, 63);
-    }
-    if (lane == 0) {
-      sp_start[a.k] = tw;
-      sp_pref[a.k] = run;
-      sp_pref[a.k + 1] = run + (T - tw);
-      sh_nspans = a.k + 1;
-    }
+  for (int o = 1; o < 64; o <<= 1) {
+    const int x = __shfl_up(incl, o);
+    if (lane >= o) incl += x;
+  }
+  if (lane == 63) tmp[wave] = incl;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    before += w < wave ? tmp[w] : 0;
+    all += tmp[w];
   }
   __syncthreads();
-  const int nspans = sh_nspans;
-  const int total = sp_pref[nspans];
+  *total = all;
+  return before + incl - v;
+}
 
-  const St* kp = static_cast<const St*>(a.k_pool);
-  const St* vp = static_cast<const St*>(a.v_pool);
-  const int cl = lane % LPR;  // which 16-byte chunk of a row this lane holds
-  const int rs = lane / LPR;  // which row of a wave load
+struct Assign {
+  int p;       // pair
+  int lo, hi;  // blocks [lo, hi) of the pair's list
+};
 
-  float qf[G][VPL];
-  {
-    const St* qb = static_cast<const St*>(a.q) + (static_cast<size_t>(b) * a.Hq + g * G) * D;
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const uint4 u = *reinterpret_cast<const uint4*>(qb + h * D + cl * VPL);
-      unpack16<E>(u, qf[h]);
-#pragma unroll
-      for (int v = 0; v < VPL; ++v) qf[h][v] *= a.scale_log2;
+// Block counts of every pair, workgroups per pair, and this workgroup's share.
+// Returns false when this workgroup has no work. Workgroup 0 publishes the
+// first workgroup of every pair for the combine kernel. Expects L.cnt zeroed.
+template <bool DENSE>
+__device__ bool assign_work(const AttnArgs& a, const LdsLayout& L, int* scan_tmp, Assign* as) {
+  const int P = a.B * a.Hkv;
+  const int t = threadIdx.x;
+  int mine_blocks = 0;
+  if (DENSE) {
+    for (int p = t; p < P; p += kThreads) {
+      const int n = blocks_of(0, cached_len(a, L.st, p / a.Hkv));
+      L.cnt[p] = n;
+      mine_blocks += n;
+    }
+  } else {
+    // one item per (pair, span); spans of a pair on a power-of-two stride.
+    // A rolled loop: this runs once per launch from a cold instruction
+    // cache, where compact code is faster than unrolled code.
+    const int sh = 32 - __clz(a.k);  // 2^sh > k, so spans 0..k fit
+    const int items = P << sh;
+#pragma unroll 1
+    for (int it = t; it < items; it += kThreads) {
+      const int p = it >> sh, i = it & ((1 << sh) - 1);
+      if (i > a.k) continue;
+      const int b = p / a.Hkv, g = p - b * a.Hkv;
+      const int T = cached_len(a, L.st, b);
+      const int tw = T - a.window > 0 ? T - a.window : 0;
+      int s0, e0;
+      pair_span(a, L.st, b, g, i, T, tw, &s0, &e0);
+      const int n = blocks_of(s0, e0);
+      if (n > 0) atomicAdd(&L.cnt[p], n);
+      mine_blocks += n;
     }
   }
-
-  float m_run[G], l_run[G], acc[G][VPL];
+  // total blocks: wave sums, one atomic per wave
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m_run[h] = kNegInf;
-    l_run[h] = 0.f;
-#pragma unroll
-    for (int v = 0; v < VPL; ++v) acc[h][v] = 0.f;
+  for (int o = 32; o >= 1; o >>= 1) mine_blocks += __shfl_xor(mine_blocks, o);
+  if ((t & 63) == 0) atomicAdd(&L.cnt[P], mine_blocks);
+  __syncthreads();
+  const int total = L.cnt[P];
+  const int per = total > 0 ? (total + a.nwg - 1) / a.nwg : 1;
+  // workgroups per pair and their prefix (thread t owns a contiguous run)
+  const int per_t = (P + kThreads - 1) / kThreads;
+  const int p0 = t * per_t, p1 = p0 + per_t < P ? p0 + per_t : P;
+  int ms = 0;
+  for (int p = p0; p < p1; ++p) {
+    const int n = L.cnt[p];
+    ms += n > 0 ? max(1, (n + per / 2) / per) : 0;
   }
-
-  for (int chunk = split; chunk * CWG < total; chunk += nsplit) {
-    const int wbase = chunk * CWG + wave * CW;
-    // One position per lane -> pool row index (or -1).
-    int row = -1;
-    {
-      const int p = wbase + lane;
-      if (lane < CW && p < total) {
-        int lo = 0, hi = nspans - 1;
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (sp_pref[mid] <= p) lo = mid;
-          else hi = mid - 1;
-        }
-        const int j = sp_start[lo] + (p - sp_pref[lo]);
-        if (j >= 0 && j < T) {
-          const int blk = a.block_table[static_cast<size_t>(b) * a.max_blocks + (j >> 4)];
-          if (blk >= 0 && blk < a.num_blocks) row = (blk * a.Hkv + g) * kBlock + (j & 15);
-        }
-      }
-    }
-    int rr[NRG];
-#pragma unroll
-    for (int r = 0; r < NRG; ++r) rr[r] = __shfl(row, r * RPW + rs);
-    uint4 kr[NRG], vr[NRG];
-#pragma unroll
-    for (int r = 0; r < NRG; ++r) {
-      kr[r] = make_uint4(0, 0, 0, 0);
-      if (rr[r] >= 0)
-        kr[r] = *reinterpret_cast<const uint4*>(kp + static_cast<size_t>(rr[r]) * D + cl * VPL);
-    }
-#pragma unroll
-    for (int r = 0; r < NRG; ++r) {
-      vr[r] = make_uint4(0, 0, 0, 0);
-      if (rr[r] >= 0)
-        vr[r] = *reinterpret_cast<const uint4*>(vp + static_cast<size_t>(rr[r]) * D + cl * VPL);
-    }
-
-    float z[NRG][G];
-#pragma unroll
-    for (int r = 0; r < NRG; ++r) {
-      float x[VPL];
-      unpack16<E>(kr[r], x);
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float s = 0.f;
-#pragma unroll
-        for (int v = 0; v < VPL; ++v) s = fmaf(qf[h][v], x[v], s);
-        s = row_sum<LPR>(s);
-        z[r][h] = rr[r] >= 0 ? s : kNegInf;
-      }
-    }
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float mc = kNegInf;
-#pragma unroll
-      for (int r = 0; r < NRG; ++r) mc = fmaxf(mc, z[r][h]);
-      mc = slot_max<LPR>(mc);
-      const float mn = fmaxf(m_run[h], mc);
-      if (mn != kNegInf) {
-        const float alpha = exp2f(m_run[h] - mn);  // 0 when m_run is -inf
-        l_run[h] *= alpha;
-#pragma unroll
-        for (int v = 0; v < VPL; ++v) acc[h][v] *= alpha;
-        m_run[h] = mn;
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < NRG; ++r) {
-      float x[VPL];
-      unpack16<E>(vr[r], x);
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float p = z[r][h] != kNegInf ? exp2f(z[r][h] - m_run[h]) : 0.f;
-        l_run[h] += p;
-#pragma unroll
-        for (int v = 0; v < VPL; ++v) acc[h][v] = fmaf(p, x[v], acc[h][v]);
-      }
-    }
+  int total_s;
+  int run = wg_exclusive_scan(ms, scan_tmp, &total_s);
+  for (int p = p0; p < p1; ++p) {
+    const int n = L.cnt[p];
+    L.prefS[p] = run;
+    run += n > 0 ? max(1, (n + per / 2) / per) : 0;
   }
-
-  // ---- merge the row slots of the wave, then the waves of the workgroup ----
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    l_run[h] = slot_sum<LPR>(l_run[h]);
-#pragma unroll
-    for (int v = 0; v < VPL; ++v) acc[h][v] = slot_sum<LPR>(acc[h][v]);
+  if (t == 0) L.prefS[P] = total_s;
+  __syncthreads();
+  if (blockIdx.x == 0)
+    for (int p = t; p <= P; p += kThreads) a.ws_pref[p] = L.prefS[p];
+  const int w = blockIdx.x;
+  if (w >= total_s) return false;
+  int lo = 0, hi = P - 1;  // last pair with prefS[p] <= w
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (L.prefS[mid] <= w) lo = mid;
+    else hi = mid - 1;
   }
-  if (lane < LPR) {
+  const int p = lo;
+  const int S = L.prefS[p + 1] - L.prefS[p];
+  const int r = w - L.prefS[p];
+  const int64_t n = L.cnt[p];
+  as->p = p;
+  as->lo = static_cast<int>(r * n / S);
+  as->hi = static_cast<int>((r + 1) * n / S);
+  return true;
+}
+
+// Copy the block-table row of sequence b (its first ceil(T/16) entries) to LDS.
+__device__ __forceinline__ void fetch_row(const AttnArgs& a, const LdsLayout& L, int b, int T) {
+  const int n = (T + kBlock - 1) / kBlock;
+  const int32_t* src = a.block_table + static_cast<size_t>(b) * a.max_blocks;
+  for (int i = threadIdx.x; i < n; i += kThreads) L.row[i] = src[i];
+}
+
+// Span list of the pair in LDS, built by wave 0 (lanes over spans); the
+// caller synchronizes afterwards. Returns the number of spans through *nspans.
+template <bool DENSE>
+__device__ void build_pair_plan(const AttnArgs& a, const LdsLayout& L, int b, int g, int T,
+                                int tw, int* nspans) {
+  const int lane = threadIdx.x & 63;
+  if (threadIdx.x >= 64) return;
+  if (DENSE) {
+    if (lane == 0) {
+      L.plan_s[0] = 0;
+      L.plan_e[0] = T;
+      L.plan_pref[0] = 0;
+      L.plan_pref[1] = blocks_of(0, T);
+      *nspans = 1;
+    }
+    return;
+  }
+  const int n = a.k + 1;
+  int run = 0;
+  for (int base = 0; base < n; base += 64) {
+    const int i = base + lane;
+    int s = 0, e = 0;
+    if (i < n) pair_span(a, L.st, b, g, i, T, tw, &s, &e);
+    const int nb = blocks_of(s, e);
+    int incl = nb;
 #pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int v = 0; v < VPL; ++v) red_acc[wave][h][cl * VPL + v] = acc[h][v];
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o);
+      if (lane >= o) incl += v;
+    }
+    if (i < n) {
+      L.plan_s[i] = s;
+      L.plan_e[i] = e;
+      L.plan_pref[i] = run + incl - nb;
+    }
+    run += __shfl(incl, 63);
   }
   if (lane == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      red_m[wave][h] = m_run[h];
-      red_l[wave][h] = l_run[h];
-    }
+    L.plan_pref[n] = run;
+    *nspans = n;
   }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < G * D; idx += kAttnThreads) {
+}
+
+// Entry j of the pair's list -> physical block and slot mask (mask 0 when j
+// is past the list or its block id is out of range).
+__device__ __forceinline__ void resolve_entry(const AttnArgs& a, const LdsLayout& L, int nspans,
+                                              int total, int b, int j, int* pb, uint32_t* mask) {
+  *pb = 0;
+  *mask = 0;
+  if (j < 0 || j >= total) return;
+  int lo = 0, hi = nspans - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (L.plan_pref[mid] <= j) lo = mid;
+    else hi = mid - 1;
+  }
+  const int s = L.plan_s[lo], e = L.plan_e[lo];
+  const int lb = (s >> 4) + (j - L.plan_pref[lo]);
+  if (lb < 0 || lb >= a.max_blocks) return;
+  const int b0 = lb << 4;
+  const int from = (s > b0 ? s : b0) - b0;
+  const int to = (e < b0 + 16 ? e : b0 + 16) - b0;
+  const int blk = a.row_lds ? L.row[lb] : a.block_table[static_cast<size_t>(b) * a.max_blocks + lb];
+  if (blk < 0 || blk >= a.num_blocks || to <= from) return;
+  *pb = blk;
+  *mask = ((1u << to) - 1u) & ~((1u << from) - 1u);
+}
+
+// Entry of this wave for lane-indexed position e (chunks of NBW round-robin
+// over the waves): the list index j, or -1.
+template <int NBW>
+__device__ __forceinline__ int wave_entry(const Assign& as, int wave, int e) {
+  const int j = as.lo + ((e / NBW) * kWaves + wave) * NBW + e % NBW;
+  return j < as.hi ? j : -1;
+}
+
+// Number of this wave's chunks that hold at least one entry of the range.
+template <int NBW>
+__device__ __forceinline__ int wave_chunks(const Assign& as, int wave) {
+  const int nck = (as.hi - as.lo + NBW - 1) / NBW;  // chunks in the range
+  return nck > wave ? (nck - wave + kWaves - 1) / kWaves : 0;
+}
+
+// Merge the waves' (m, l, acc) and write this workgroup's partial.
+// red_m / red_l: [kWaves][G]; red_o: [kWaves][G][D].
+template <int G, int D>
+__device__ void write_partial(const AttnArgs& a, const float (*red_m)[G],
+                              const float (*red_l)[G], const float (*red_o)[G][D]) {
+  const size_t slot = blockIdx.x;
+  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
     const int h = idx / D, e = idx % D;
     float M = kNegInf;
 #pragma unroll
@@ -278,11 +391,11 @@ attn_partial_kernel(AttnArgs a) {
         if (red_m[w][h] != kNegInf) {
           const float f = exp2f(red_m[w][h] - M);
           L = fmaf(red_l[w][h], f, L);
-          A = fmaf(red_acc[w][h][e], f, A);
+          A = fmaf(red_o[w][h][e], f, A);
         }
       }
     }
-    const size_t o = ((static_cast<size_t>(b) * a.Hkv + g) * nsplit + split) * G + h;
+    const size_t o = slot * G + h;
     a.ws_acc[o * D + e] = A;
     if (e == 0) {
       a.ws_m[o] = M;
@@ -291,76 +404,596 @@ attn_partial_kernel(AttnArgs a) {
   }
 }
 
-// Merge the S partials of each (b, g): out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s.
-template <int D, int G>
-__global__ void __launch_bounds__(kAttnThreads)
-attn_combine_kernel(AttnArgs a, int nsplit) {
-  const int g = blockIdx.x, b = blockIdx.y;
-  const size_t base = (static_cast<size_t>(b) * a.Hkv + g) * nsplit;
-  for (int idx = threadIdx.x; idx < G * D; idx += kAttnThreads) {
-    const int h = idx / D, e = idx % D;
-    float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, a.ws_m[(base + s) * G + h]);
-    float L = 0.f, A = 0.f;
-    if (M != -INFINITY) {
-      for (int s = 0; s < nsplit; ++s) {
-        const float ms = a.ws_m[(base + s) * G + h];
-        if (ms != -INFINITY) {
-          const float f = exp2f(ms - M);
-          L = fmaf(a.ws_l[(base + s) * G + h], f, L);
-          A = fmaf(a.ws_acc[((base + s) * G + h) * D + e], f, A);
-        }
+// ---------------------------------------------------------------------------
+// bf16 matrix-core kernel. G query heads per KV head (G <= 16), head dim D,
+// NBW blocks per wave per chunk.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bf16x4 pack_bf16x4(float p0, float p1, float p2, float p3) {
+  const bf16x2v lo = __builtin_convertvector((f32x2v){p0, p1}, bf16x2v);
+  const bf16x2v hi = __builtin_convertvector((f32x2v){p2, p3}, bf16x2v);
+  const unsigned u0 = __builtin_bit_cast(unsigned, lo), u1 = __builtin_bit_cast(unsigned, hi);
+  bf16x4 r;
+  r[0] = static_cast<short>(u0 & 0xffffu);
+  r[1] = static_cast<short>(u0 >> 16);
+  r[2] = static_cast<short>(u1 & 0xffffu);
+  r[3] = static_cast<short>(u1 >> 16);
+  return r;
+}
+
+__device__ __forceinline__ float bf16_at(const bf16x4& v, int i) {
+  return __uint_as_float(static_cast<uint32_t>(static_cast<uint16_t>(v[i])) << 16);
+}
+
+template <int D, int NBW>
+struct Chunk {
+  bf16x8 k[NBW][D / 32];  // K rows: lane holds slot l16, dims 32 kk + 8 lg .. +7 (A operand)
+  bf16x4 v[NBW][D / 16];  // V: lane holds dim 16 nt + l16, slots 4 lg .. +3 (B operand)
+  uint32_t msk[NBW];
+};
+
+// Issue the loads of this wave's chunk `c` (entries held lane-wise in
+// pb_l/msk_l). Branch-free, so the compiler keeps the next chunk's loads in
+// flight while the current one is computed: a lane whose slot (or 4-slot
+// group) is outside the set re-reads a line that an attended slot's lane
+// fetches anyway, and its values are cleared (keys need no clearing: their
+// logits are replaced by -inf).
+template <int D, int NBW>
+__device__ __forceinline__ void load_chunk(const AttnArgs& a, int g, int c, int pb_l,
+                                           uint32_t msk_l, Chunk<D, NBW>& ch) {
+  constexpr int KS = D / 32, NT = D / 16;
+  const int lane = threadIdx.x & 63, l16 = lane & 15, lg = lane >> 4;
+  const uint16_t* kpool = static_cast<const uint16_t*>(a.k_pool);
+  const uint16_t* vpool = static_cast<const uint16_t*>(a.v_pool);
+#pragma unroll
+  for (int i = 0; i < NBW; ++i) {
+    const int pb = __builtin_amdgcn_readlane(pb_l, c * NBW + i);
+    const uint32_t msk = __builtin_amdgcn_readlane(static_cast<int>(msk_l), c * NBW + i);
+    ch.msk[i] = msk;
+    const int first = msk ? __builtin_ctz(msk) : 0;
+    const size_t tile = static_cast<size_t>(pb) * a.Hkv + g;
+    const int kslot = ((msk >> l16) & 1u) ? l16 : first;
+    const uint16_t* krow = kpool + (tile * kBlock + kslot) * D + 8 * lg;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) ch.k[i][kk] = *reinterpret_cast<const bf16x8*>(krow + 32 * kk);
+    const uint32_t m4 = (msk >> (4 * lg)) & 0xfu;
+    const int vgrp = m4 ? lg : (first >> 2);
+    const uint16_t* vcol = vpool + tile * (D * kBlock) + l16 * kBlock + 4 * vgrp;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      ch.v[i][nt] = *reinterpret_cast<const bf16x4*>(vcol + nt * 16 * kBlock);
+  }
+}
+
+struct MfmaState {
+  float m_run;  // running max of head l16 (log2 units)
+  float l_run;  // running sum of this lane's slots of head l16
+  bool first;
+};
+
+template <int D, int NBW>
+__device__ __forceinline__ void compute_chunk(const AttnArgs& a, Chunk<D, NBW>& ch,
+                                              const bf16x8 (&qop)[D / 32], f32x4 (&o)[D / 16],
+                                              MfmaState& stt) {
+  constexpr int KS = D / 32, NT = D / 16;
+  const int lane = threadIdx.x & 63, lg = lane >> 4;
+  // clear value slots outside the set (never trust their bits): one 16-bit
+  // lane mask per slot of this lane's 4-slot group
+#pragma unroll
+  for (int i = 0; i < NBW; ++i) {
+    const uint32_t m4 = (ch.msk[i] >> (4 * lg)) & 0xfu;
+    const uint32_t w0 = ((m4 & 1u) ? 0x0000ffffu : 0u) | ((m4 & 2u) ? 0xffff0000u : 0u);
+    const uint32_t w1 = ((m4 & 4u) ? 0x0000ffffu : 0u) | ((m4 & 8u) ? 0xffff0000u : 0u);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+      u32x2 bits = __builtin_bit_cast(u32x2, ch.v[i][nt]);
+      bits.x &= w0;
+      bits.y &= w1;
+      ch.v[i][nt] = __builtin_bit_cast(bf16x4, bits);
+    }
+  }
+  // S^T = K . Q^T: lane holds slots 4 lg + r of head l16
+  float z[NBW][4];
+  float mc = kNegInf;
+#pragma unroll
+  for (int i = 0; i < NBW; ++i) {
+    f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ch.k[i][kk], qop[kk], sacc, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const bool on = (ch.msk[i] >> (4 * lg + r)) & 1u;
+      z[i][r] = on ? sacc[r] * a.scale_log2 : kNegInf;
+      mc = fmaxf(mc, z[i][r]);
+    }
+  }
+  mc = fmaxf(mc, __shfl_xor(mc, 16));
+  mc = fmaxf(mc, __shfl_xor(mc, 32));
+  const float m_new = fmaxf(stt.m_run, mc);
+  if (!stt.first) {
+    // rescale what this wave accumulated under the old maximum
+    const float alpha = m_new == kNegInf ? 1.f : exp2f(stt.m_run - m_new);
+    stt.l_run *= alpha;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float ar = __shfl(alpha, lg * 16 + 4 * lg + r);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) o[nt][r] *= ar;
+    }
+  }
+  stt.m_run = m_new;
+  stt.first = false;
+#pragma unroll
+  for (int i = 0; i < NBW; ++i) {
+    float pr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      pr[r] = z[i][r] != kNegInf ? exp2f(z[i][r] - m_new) : 0.f;
+      stt.l_run += pr[r];
+    }
+    const bf16x4 phi = pack_bf16x4(pr[0], pr[1], pr[2], pr[3]);
+    const bf16x4 plo = pack_bf16x4(pr[0] - bf16_at(phi, 0), pr[1] - bf16_at(phi, 1),
+                                   pr[2] - bf16_at(phi, 2), pr[3] - bf16_at(phi, 3));
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      o[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, ch.v[i][nt], o[nt], 0, 0, 0);
+      o[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, ch.v[i][nt], o[nt], 0, 0, 0);
+    }
+  }
+}
+
+template <int G, int D, int NBW, bool DENSE, bool STAGED>
+__global__ void __launch_bounds__(kThreads, 2)
+attn_mfma_kernel(AttnArgs a) {
+  constexpr int KS = D / 32, NT = D / 16;
+  constexpr int EPB = 64;  // entries resolved per batch (one per lane)
+  extern __shared__ int32_t dyn[];
+  __shared__ float red_m[kWaves][G];
+  __shared__ float red_l[kWaves][G];
+  __shared__ float red_o[kWaves][G][D];
+  __shared__ int scan_tmp[kWaves];
+  __shared__ int sh_nspans;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const LdsLayout L = stage_inputs<DENSE, STAGED>(a, dyn);
+  __syncthreads();
+  Assign as;
+  if (!assign_work<DENSE>(a, L, scan_tmp, &as)) return;
+  const int b = as.p / a.Hkv, g = as.p % a.Hkv;
+  const int T = cached_len(a, L.st, b);
+  const int tw = T - a.window > 0 ? T - a.window : 0;
+  if (a.row_lds) fetch_row(a, L, b, T);
+  build_pair_plan<DENSE>(a, L, b, g, T, tw, &sh_nspans);
+  __syncthreads();
+  const int nspans = sh_nspans;
+  const int n_list = L.plan_pref[nspans];
+
+  // Q^T as the B operand: lane holds head l16, dims 32 kk + 8 lg .. +7
+  bf16x8 qop[KS];
+  {
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
+                           (static_cast<size_t>(b) * a.Hq + g * G + (l16 < G ? l16 : 0)) * D;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const bf16x8 qv = *reinterpret_cast<const bf16x8*>(qrow + 32 * kk + 8 * lg);
+      qop[kk] = l16 < G ? qv : bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+  }
+  f32x4 o[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  MfmaState stt{kNegInf, 0.f, true};
+
+  const int nck_all = wave_chunks<NBW>(as, wave);
+  constexpr int CPB = EPB / NBW;  // chunks per batch
+  for (int c0 = 0; c0 < nck_all; c0 += CPB) {
+    // one lane per entry: resolve this batch's block-table entries at once
+    int pb_l;
+    uint32_t msk_l;
+    resolve_entry(a, L, nspans, n_list, b, wave_entry<NBW>(as, wave, c0 * NBW + lane), &pb_l,
+                  &msk_l);
+    const int nck = nck_all - c0 < CPB ? nck_all - c0 : CPB;
+    Chunk<D, NBW> cA, cB;
+    load_chunk<D, NBW>(a, g, 0, pb_l, msk_l, cA);
+    for (int c = 0; c < nck; c += 2) {
+      if (c + 1 < nck) load_chunk<D, NBW>(a, g, c + 1, pb_l, msk_l, cB);
+      compute_chunk<D, NBW>(a, cA, qop, o, stt);
+      if (c + 1 < nck) {
+        if (c + 2 < nck) load_chunk<D, NBW>(a, g, c + 2, pb_l, msk_l, cA);
+        compute_chunk<D, NBW>(a, cB, qop, o, stt);
       }
     }
-    a.out[(static_cast<size_t>(b) * a.Hq + g * G + h) * D + e] = L > 0.f ? A / L : 0.f;
+  }
+
+  // per-wave results -> LDS: head h = l16 for m and l; O rows are heads 4 lg + r
+  float l_run = stt.l_run;
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  if (lg == 0 && l16 < G) {
+    red_m[wave][l16] = stt.m_run;
+    red_l[wave][l16] = l_run;
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int h = 4 * lg + r;
+    if (h < G) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) red_o[wave][h][16 * nt + l16] = o[nt][r];
+    }
+  }
+  __syncthreads();
+  write_partial<G, D>(a, red_m, red_l, red_o);
+}
+
+// ---------------------------------------------------------------------------
+// Vector-ALU kernel (fp32 inputs), G <= 8.
+// ---------------------------------------------------------------------------
+template <int LPR>
+__device__ __forceinline__ float row_sum(float v) {
+#pragma unroll
+  for (int o = LPR / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+template <typename E, int G, int D, bool DENSE, bool STAGED>
+__global__ void __launch_bounds__(kThreads)
+attn_valu_kernel(AttnArgs a) {
+  using St = typename E::storage;
+  constexpr int NBW = 2;
+  constexpr int VPL = 16 / E::kBytes;  // values per 16-byte load
+  constexpr int LPR = D / VPL;         // lanes per key row
+  constexpr int RPW = 64 / LPR;        // key rows per wave load
+  constexpr int NL = kBlock / RPW;     // key loads per block per lane
+  constexpr int DPL = D / 64;          // value dimensions per lane
+  constexpr int VCH = kBlock / VPL;    // 16-byte chunks per value column
+  constexpr int CPB = 64 / NBW;
+  extern __shared__ int32_t dyn[];
+  __shared__ float red_m[kWaves][G];
+  __shared__ float red_l[kWaves][G];
+  __shared__ float red_o[kWaves][G][D];
+  __shared__ float p_lds[kWaves][NBW * kBlock][G];
+  __shared__ int scan_tmp[kWaves];
+  __shared__ int sh_nspans;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const LdsLayout L = stage_inputs<DENSE, STAGED>(a, dyn);
+  __syncthreads();
+  Assign as;
+  if (!assign_work<DENSE>(a, L, scan_tmp, &as)) return;
+  const int b = as.p / a.Hkv, g = as.p % a.Hkv;
+  const int T = cached_len(a, L.st, b);
+  const int tw = T - a.window > 0 ? T - a.window : 0;
+  if (a.row_lds) fetch_row(a, L, b, T);
+  build_pair_plan<DENSE>(a, L, b, g, T, tw, &sh_nspans);
+  __syncthreads();
+  const int nspans = sh_nspans;
+  const int n_list = L.plan_pref[nspans];
+
+  const St* kpool = static_cast<const St*>(a.k_pool);
+  const St* vpool = static_cast<const St*>(a.v_pool);
+  const int cl = lane % LPR, rs = lane / LPR;
+  float qf[G][VPL];
+  {
+    const St* qb = static_cast<const St*>(a.q) + (static_cast<size_t>(b) * a.Hq + g * G) * D;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      unpack16<E>(*reinterpret_cast<const uint4*>(qb + h * D + cl * VPL), qf[h]);
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) qf[h][v] *= a.scale_log2;
+    }
+  }
+  float m_run[G], l_part[G], acc[G][DPL];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m_run[h] = kNegInf;
+    l_part[h] = 0.f;
+#pragma unroll
+    for (int dd = 0; dd < DPL; ++dd) acc[h][dd] = 0.f;
+  }
+
+  const int nck_all = wave_chunks<NBW>(as, wave);
+  for (int c0 = 0; c0 < nck_all; c0 += CPB) {
+    int pb_l;
+    uint32_t msk_l;
+    resolve_entry(a, L, nspans, n_list, b, wave_entry<NBW>(as, wave, c0 * NBW + lane), &pb_l,
+                  &msk_l);
+    const int nck = nck_all - c0 < CPB ? nck_all - c0 : CPB;
+    for (int c = 0; c < nck; ++c) {
+      int pb[NBW];
+      uint32_t msk[NBW];
+#pragma unroll
+      for (int i = 0; i < NBW; ++i) {
+        pb[i] = __shfl(pb_l, c * NBW + i);
+        msk[i] = __shfl(msk_l, c * NBW + i);
+      }
+      float z[NBW][NL][G];
+      float mc[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) mc[h] = kNegInf;
+#pragma unroll
+      for (int i = 0; i < NBW; ++i) {
+        const size_t tile = static_cast<size_t>(pb[i]) * a.Hkv + g;
+#pragma unroll
+        for (int t = 0; t < NL; ++t) {
+          const int slot = rs + RPW * t;
+          const bool on = (msk[i] >> slot) & 1u;
+          uint4 u = make_uint4(0, 0, 0, 0);
+          if (on)
+            u = *reinterpret_cast<const uint4*>(kpool + (tile * kBlock + slot) * D + cl * VPL);
+          float x[VPL];
+          unpack16<E>(u, x);
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            float s = 0.f;
+#pragma unroll
+            for (int v = 0; v < VPL; ++v) s = fmaf(qf[h][v], x[v], s);
+            s = row_sum<LPR>(s);
+            z[i][t][h] = on ? s : kNegInf;
+            mc[h] = fmaxf(mc[h], z[i][t][h]);
+          }
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+#pragma unroll
+        for (int o = LPR; o < 64; o <<= 1) mc[h] = fmaxf(mc[h], __shfl_xor(mc[h], o));
+        const float mn = fmaxf(m_run[h], mc[h]);
+        const float alpha = mn == kNegInf ? 1.f : exp2f(m_run[h] - mn);
+        l_part[h] *= alpha;
+#pragma unroll
+        for (int dd = 0; dd < DPL; ++dd) acc[h][dd] *= alpha;
+        m_run[h] = mn;
+      }
+      // probabilities of the wave's slots -> LDS (one writer lane per row)
+#pragma unroll
+      for (int i = 0; i < NBW; ++i)
+#pragma unroll
+        for (int t = 0; t < NL; ++t)
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            const float pv = z[i][t][h] != kNegInf ? exp2f(z[i][t][h] - m_run[h]) : 0.f;
+            if (cl == 0) {
+              p_lds[wave][i * kBlock + rs + RPW * t][h] = pv;
+              l_part[h] += pv;
+            }
+          }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      // values: lane owns dims lane + 64 dd; a value column holds 16 slots
+#pragma unroll
+      for (int i = 0; i < NBW; ++i) {
+        if (msk[i] == 0u) continue;
+        const size_t tile = static_cast<size_t>(pb[i]) * a.Hkv + g;
+#pragma unroll
+        for (int dd = 0; dd < DPL; ++dd) {
+          const St* col = vpool + (tile * D + lane + 64 * dd) * kBlock;
+#pragma unroll
+          for (int c2 = 0; c2 < VCH; ++c2) {
+            float x[VPL];
+            unpack16<E>(*reinterpret_cast<const uint4*>(col + c2 * VPL), x);
+#pragma unroll
+            for (int v = 0; v < VPL; ++v) {
+              const int slot = c2 * VPL + v;
+              if ((msk[i] >> slot) & 1u) {
+#pragma unroll
+                for (int h = 0; h < G; ++h)
+                  acc[h][dd] = fmaf(p_lds[wave][i * kBlock + slot][h], x[v], acc[h][dd]);
+              }
+            }
+          }
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    }
+  }
+
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float l = l_part[h];
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) l += __shfl_xor(l, o);
+    if (lane == 0) {
+      red_m[wave][h] = m_run[h];
+      red_l[wave][h] = l;
+    }
+#pragma unroll
+    for (int dd = 0; dd < DPL; ++dd) red_o[wave][h][lane + 64 * dd] = acc[h][dd];
+  }
+  __syncthreads();
+  write_partial<G, D>(a, red_m, red_l, red_o);
+}
+
+// ---------------------------------------------------------------------------
+// Combine: merge the partials of pair (b, g) (workgroups [ws_pref[p],
+// ws_pref[p+1])) by log-sum-exp,
+//   out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s,  M = max_s m_s.
+// Each thread owns (head, dim) outputs and reads a tile of partials with
+// independent loads, merging tiles online.
+// ---------------------------------------------------------------------------
+constexpr int kCombineTile = 16;
+
+template <int G, int D>
+__global__ void __launch_bounds__(kThreads)
+attn_combine_kernel(AttnArgs a) {
+  const int g = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
+  const int p = b * a.Hkv + g;
+  const int s0 = a.ws_pref[p], s1 = a.ws_pref[p + 1];
+  constexpr int PER = (G * D + kThreads - 1) / kThreads;
+  float* out = a.out + (static_cast<size_t>(b) * a.Hq + g * G) * D;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int idx = t + j * kThreads;
+    if (idx >= G * D) continue;
+    const int h = idx / D, e = idx % D;
+    float M = kNegInf, Lsum = 0.f, A = 0.f;
+    for (int c0 = s0; c0 < s1; c0 += kCombineTile) {
+      float ms[kCombineTile], ls[kCombineTile], vs[kCombineTile];
+#pragma unroll
+      for (int u = 0; u < kCombineTile; ++u) {
+        const int s = c0 + u;
+        ms[u] = kNegInf;
+        ls[u] = 0.f;
+        vs[u] = 0.f;
+        if (s < s1) {
+          ms[u] = a.ws_m[static_cast<size_t>(s) * G + h];
+          ls[u] = a.ws_l[static_cast<size_t>(s) * G + h];
+          vs[u] = a.ws_acc[(static_cast<size_t>(s) * G + h) * D + e];
+        }
+      }
+      float mt = M;
+#pragma unroll
+      for (int u = 0; u < kCombineTile; ++u) mt = fmaxf(mt, ms[u]);
+      if (mt == kNegInf) continue;
+      const float alpha = M == kNegInf ? 0.f : exp2f(M - mt);
+      Lsum *= alpha;
+      A *= alpha;
+#pragma unroll
+      for (int u = 0; u < kCombineTile; ++u) {
+        if (ms[u] != kNegInf) {
+          const float w = exp2f(ms[u] - mt);
+          Lsum = fmaf(ls[u], w, Lsum);
+          A = fmaf(vs[u], w, A);
+        }
+      }
+      M = mt;
+    }
+    out[idx] = Lsum > 0.f ? A / Lsum : 0.f;
   }
 }
 
-int attn_tokens_per_split(const zr_geom& gm) {
-  const int bytes = gm.dtype == ZR_BF16 ? 2 : 4;
-  const int lpr = gm.head_dim * bytes / 16;
-  return kWaves * (lpr <= 16 ? 64 : 32);
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+constexpr int kMfmaNBW = 2;
+
+int attn_workgroups(const zr_geom& gm, int32_t max_attended) {
+  const int64_t pairs = static_cast<int64_t>(gm.batch) * gm.n_kv_heads;
+  const int64_t blocks = pairs * ((static_cast<int64_t>(max_attended) + kBlock - 1) / kBlock + 2);
+  int64_t n = (blocks + kMinBlocksPerWg - 1) / kMinBlocksPerWg;
+  if (n < 1) n = 1;
+  if (n > kTargetWorkgroups) n = kTargetWorkgroups;
+  return static_cast<int>(n);
 }
 
-template <typename E, int D, int G>
-static hipError_t launch_typed(const zr_geom& gm, const AttnArgs& a, int splits, bool dense,
-                               hipStream_t s) {
-  dim3 grid(splits, gm.n_kv_heads, gm.batch);
-  if (dense) {
-    hipLaunchKernelGGL((attn_partial_kernel<E, D, G, true>), grid, dim3(kAttnThreads),
-                       4 * sizeof(int32_t), s, a);
-  } else {
-    const size_t lds = 2 * static_cast<size_t>(a.k + 2) * sizeof(int32_t);
-    hipLaunchKernelGGL((attn_partial_kernel<E, D, G, false>), grid, dim3(kAttnThreads), lds, s,
-                       a);
+size_t attn_workspace(const zr_geom& gm, int nwg, void* ws, AttnArgs* a) {
+  const size_t G = static_cast<size_t>(gm.n_q_heads / gm.n_kv_heads);
+  const size_t P = static_cast<size_t>(gm.batch) * gm.n_kv_heads;
+  const size_t slots = static_cast<size_t>(nwg) + P;
+  auto up16 = [](size_t x) { return (x + 15) & ~static_cast<size_t>(15); };
+  const size_t pref_b = up16((P + 1) * sizeof(int32_t));
+  const size_t ml_b = up16(slots * G * sizeof(float));
+  const size_t acc_b = slots * G * gm.head_dim * sizeof(float);
+  if (ws && a) {
+    char* c = static_cast<char*>(ws);
+    a->ws_pref = reinterpret_cast<int32_t*>(c);
+    a->ws_m = reinterpret_cast<float*>(c + pref_b);
+    a->ws_l = reinterpret_cast<float*>(c + pref_b + ml_b);
+    a->ws_acc = reinterpret_cast<float*>(c + pref_b + 2 * ml_b);
+    a->nwg = nwg;
   }
-  hipError_t err = hipGetLastError();
+  return pref_b + 2 * ml_b + acc_b;
+}
+
+static size_t dyn_lds_bytes(const zr_geom& gm, const AttnArgs& a, bool dense) {
+  return lds_ints(gm.batch, gm.n_kv_heads, a.k, a.n_total, dense, a.stage_sel != 0,
+                  a.row_lds ? gm.max_blocks_per_seq : 0) *
+         sizeof(int32_t);
+}
+
+template <int G, int D>
+static hipError_t launch_mfma(const zr_geom& gm, const AttnArgs& a, bool dense, hipStream_t s) {
+  const size_t lds = dyn_lds_bytes(gm, a, dense);
+  const dim3 grid(a.nwg + gm.batch * gm.n_kv_heads);
+  if (dense)
+    hipLaunchKernelGGL((attn_mfma_kernel<G, D, kMfmaNBW, true, false>), grid, dim3(kThreads), lds,
+                       s, a);
+  else if (a.stage_sel)
+    hipLaunchKernelGGL((attn_mfma_kernel<G, D, kMfmaNBW, false, true>), grid, dim3(kThreads), lds,
+                       s, a);
+  else
+    hipLaunchKernelGGL((attn_mfma_kernel<G, D, kMfmaNBW, false, false>), grid, dim3(kThreads),
+                       lds, s, a);
+  const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((attn_combine_kernel<D, G>), dim3(gm.n_kv_heads, gm.batch),
-                     dim3(kAttnThreads), 0, s, a, splits);
+  hipLaunchKernelGGL((attn_combine_kernel<G, D>), dim3(gm.n_kv_heads, gm.batch), dim3(kThreads),
+                     0, s, a);
   return hipGetLastError();
 }
 
-template <typename E, int D>
-static hipError_t launch_g(const zr_geom& gm, const AttnArgs& a, int splits, bool dense,
-                           hipStream_t s) {
-  switch (gm.n_q_heads / gm.n_kv_heads) {
-    case 1: return launch_typed<E, D, 1>(gm, a, splits, dense, s);
-    case 2: return launch_typed<E, D, 2>(gm, a, splits, dense, s);
-    case 4: return launch_typed<E, D, 4>(gm, a, splits, dense, s);
-    case 8: return launch_typed<E, D, 8>(gm, a, splits, dense, s);
+template <typename E, int G, int D>
+static hipError_t launch_valu(const zr_geom& gm, const AttnArgs& a, bool dense, hipStream_t s) {
+  const size_t lds = dyn_lds_bytes(gm, a, dense);
+  const dim3 grid(a.nwg + gm.batch * gm.n_kv_heads);
+  if (dense)
+    hipLaunchKernelGGL((attn_valu_kernel<E, G, D, true, false>), grid, dim3(kThreads), lds, s, a);
+  else if (a.stage_sel)
+    hipLaunchKernelGGL((attn_valu_kernel<E, G, D, false, true>), grid, dim3(kThreads), lds, s, a);
+  else
+    hipLaunchKernelGGL((attn_valu_kernel<E, G, D, false, false>), grid, dim3(kThreads), lds, s, a);
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((attn_combine_kernel<G, D>), dim3(gm.n_kv_heads, gm.batch), dim3(kThreads),
+                     0, s, a);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_d(const zr_geom& gm, const AttnArgs& a, bool dense, hipStream_t s) {
+  const int G = gm.n_q_heads / gm.n_kv_heads;
+  if (gm.dtype == ZR_BF16) {
+    switch (G) {
+      case 1: return launch_mfma<1, D>(gm, a, dense, s);
+      case 2: return launch_mfma<2, D>(gm, a, dense, s);
+      case 4: return launch_mfma<4, D>(gm, a, dense, s);
+      case 8: return launch_mfma<8, D>(gm, a, dense, s);
+      case 16: return launch_mfma<16, D>(gm, a, dense, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  switch (G) {
+    case 1: return launch_valu<F32, 1, D>(gm, a, dense, s);
+    case 2: return launch_valu<F32, 2, D>(gm, a, dense, s);
+    case 4: return launch_valu<F32, 4, D>(gm, a, dense, s);
+    case 8: return launch_valu<F32, 8, D>(gm, a, dense, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_attention(const zr_geom& gm, const AttnArgs& a, int splits, bool dense,
-                            hipStream_t s) {
+// LDS of one workgroup: the static arrays (bounded for every G, D) plus the
+// dynamic plan region; kept within 64 KiB.
+constexpr size_t kLdsLimit = 64 * 1024;
+
+static size_t static_lds_bound(const zr_geom& gm) {
+  const size_t G = static_cast<size_t>(gm.n_q_heads / gm.n_kv_heads);
+  return (kWaves * G * gm.head_dim + 2 * kWaves * G + kWaves * 2 * kBlock * G) * sizeof(float) +
+         256;
+}
+
+bool attn_lds_ok(const zr_geom& gm, int k, bool dense) {
+  return static_lds_bound(gm) +
+             lds_ints(gm.batch, gm.n_kv_heads, k, 0, dense, false, 0) * sizeof(int32_t) <=
+         kLdsLimit;
+}
+
+hipError_t launch_attention(const zr_geom& gm, const AttnArgs& a0, bool dense, hipStream_t s) {
   if (gm.batch == 0) return hipSuccess;
-  if (gm.dtype == ZR_BF16)
-    return gm.head_dim == 128 ? launch_g<BF16, 128>(gm, a, splits, dense, s)
-                              : launch_g<BF16, 64>(gm, a, splits, dense, s);
-  return gm.head_dim == 128 ? launch_g<F32, 128>(gm, a, splits, dense, s)
-                            : launch_g<F32, 64>(gm, a, splits, dense, s);
+  AttnArgs a = a0;
+  const int64_t P = static_cast<int64_t>(gm.batch) * gm.n_kv_heads;
+  // stage the selections and thought spans in LDS when they fit
+  a.stage_sel = !dense && P * a.k + 2 * static_cast<int64_t>(a.n_total) <= kStageCap;
+  if (a.stage_sel && static_lds_bound(gm) + dyn_lds_bytes(gm, a, dense) > kLdsLimit)
+    a.stage_sel = 0;
+  a.stage_th = a.stage_sel;
+  // the block-table row of the workgroup's sequence in LDS when it fits
+  a.row_lds = gm.max_blocks_per_seq <= 4096;
+  if (a.row_lds && static_lds_bound(gm) + dyn_lds_bytes(gm, a, dense) > kLdsLimit) a.row_lds = 0;
+  if (static_lds_bound(gm) + dyn_lds_bytes(gm, a, dense) > kLdsLimit) return hipErrorInvalidValue;
+  return gm.head_dim == 128 ? launch_d<128>(gm, a, dense, s) : launch_d<64>(gm, a, dense, s);
 }
 
 }  // namespace zr

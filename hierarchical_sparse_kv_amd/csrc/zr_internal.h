@@ -57,6 +57,8 @@ __device__ __forceinline__ float load_elem<BF16>(const uint16_t* p, size_t i) {
 }
 
 // Attention launch parameters (device pointers + sizes), passed by value.
+// Partial results are indexed by workgroup; workgroups [ws_pref[p],
+// ws_pref[p + 1]) hold the partials of pair p = b * Hkv + g (see zr_attn.hip).
 struct AttnArgs {
   const void* q;
   const void* k_pool;
@@ -67,12 +69,17 @@ struct AttnArgs {
   const int32_t* th_start;
   const int32_t* th_len;
   const int32_t* sel;        // [B][Hkv][k] (sparse only, may be null when k == 0)
-  float* ws_m;               // [B][Hkv][S][G]
-  float* ws_l;               // [B][Hkv][S][G]
-  float* ws_acc;             // [B][Hkv][S][G][D]
+  int32_t* ws_pref;          // [P + 1]: first workgroup of each pair
+  float* ws_m;               // [nwg + P][G]
+  float* ws_l;               // [nwg + P][G]
+  float* ws_acc;             // [nwg + P][G][D]
   float* out;                // [B][Hq][D]
-  int32_t Hq, Hkv, max_blocks, num_blocks, n_total;
+  int32_t B, Hq, Hkv, max_blocks, num_blocks, n_total;
   int32_t k, window;
+  int32_t nwg;               // target workgroups; the grid has nwg + P
+  int32_t stage_sel;         // 1: stage sel in LDS (else read it from global memory)
+  int32_t stage_th;          // 1: stage the thought spans in LDS
+  int32_t row_lds;           // 1: copy the workgroup's block-table row to LDS
   float scale_log2;          // scale * log2(e)
 };
 
@@ -81,9 +88,14 @@ hipError_t launch_coarse_score(const zr_geom& g, const void* q, const zr_thought
                                float* scores, hipStream_t s);
 hipError_t launch_select_topk(const zr_geom& g, const zr_thoughts& th, const float* scores,
                               int k, int32_t* sel, hipStream_t s);
-// Tokens per split-K partition for this geometry.
-int attn_tokens_per_split(const zr_geom& g);
-hipError_t launch_attention(const zr_geom& g, const AttnArgs& a, int splits, bool dense,
-                            hipStream_t s);
+// Workgroups of the attention kernel for a bound of `max_attended` tokens per
+// (sequence, KV head); the workspace layout depends on it.
+int attn_workgroups(const zr_geom& g, int32_t max_attended);
+// Bytes of workspace for `nwg` workgroups; fills the AttnArgs pointers when
+// `ws` is not null.
+size_t attn_workspace(const zr_geom& g, int nwg, void* ws, AttnArgs* a);
+// Whether the attention kernel's LDS fits for this shape (with nothing staged).
+bool attn_lds_ok(const zr_geom& g, int k, bool dense);
+hipError_t launch_attention(const zr_geom& g, const AttnArgs& a, bool dense, hipStream_t s);
 
 }  // namespace zr

@@ -93,23 +93,31 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Exclusive prefix sum of one value per thread across the workgroup.
-// `tmp` holds kSelThreads entries. Returns the exclusive prefix; *total gets
-// the workgroup sum. Contains barriers: every thread must call it.
+// Exclusive prefix sum of one value per thread across the workgroup: a
+// shuffle scan inside each wave, then the wave totals. `tmp` holds
+// kSelThreads / 64 entries. *total gets the workgroup sum. Contains
+// barriers: every thread must call it.
 __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* tmp, uint32_t* total) {
-  const int t = threadIdx.x;
-  tmp[t] = v;
-  __syncthreads();
-  for (int off = 1; off < kSelThreads; off <<= 1) {
-    uint32_t add = t >= off ? tmp[t - off] : 0u;
-    __syncthreads();
-    tmp[t] += add;
-    __syncthreads();
+  constexpr int kW = kSelThreads / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t x = __shfl_up(incl, o);
+    if (lane >= o) incl += x;
   }
-  uint32_t incl = tmp[t];
-  *total = tmp[kSelThreads - 1];
+  if (lane == 63) tmp[wave] = incl;
   __syncthreads();
-  return incl - v;
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kW; ++w) {
+    const uint32_t t = tmp[w];
+    before += w < wave ? t : 0u;
+    all += t;
+  }
+  __syncthreads();
+  *total = all;
+  return before + incl - v;
 }
 
 __global__ void __launch_bounds__(kSelThreads)
@@ -117,10 +125,11 @@ select_topk_kernel(const float* __restrict__ scores, const int32_t* __restrict__
                    int Hkv, int k, int n_total, int max_per_seq, int32_t* __restrict__ sel) {
   extern __shared__ uint32_t keys[];  // max_per_seq entries
   __shared__ uint32_t hist[256];
-  __shared__ uint32_t scan_tmp[kSelThreads];
+  __shared__ uint32_t scan_tmp[kSelThreads / 64];
   __shared__ uint32_t sh_prefix, sh_remaining;
 
   const int g = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
+  const int lane = t & 63;
   int lo = seq_ptr[b], hi = seq_ptr[b + 1];
   hi = hi < n_total ? hi : n_total;
   int n = hi - lo;
@@ -142,19 +151,38 @@ select_topk_kernel(const float* __restrict__ scores, const int32_t* __restrict__
     hist[t] = 0;  // kSelThreads == 256 bins
     __syncthreads();
     for (int i = t; i < n; i += kSelThreads) {
-      uint32_t key = keys[i];
+      const uint32_t key = keys[i];
       if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 0xffu], 1u);
     }
     __syncthreads();
-    if (t == 0) {
-      uint32_t above = 0;
-      int digit = 255;
-      for (; digit > 0; --digit) {
-        if (above + hist[digit] >= remaining) break;
-        above += hist[digit];
+    if (t < 64) {
+      // lane L owns digits 4L .. 4L+3; find the digit d where the count of
+      // keys with a larger digit is < remaining <= that count + hist[d]
+      const uint32_t c0 = hist[4 * lane], c1 = hist[4 * lane + 1], c2 = hist[4 * lane + 2],
+                     c3 = hist[4 * lane + 3];
+      const uint32_t mine = c0 + c1 + c2 + c3;
+      uint32_t suffix = mine;  // keys in digits >= 4 * lane
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t x = __shfl_down(suffix, o);
+        if (lane + o < 64) suffix += x;
       }
-      sh_prefix = prefix | (static_cast<uint32_t>(digit) << shift);
-      sh_remaining = remaining - above;
+      const unsigned long long hit = __ballot(suffix >= remaining);
+      const int L = 63 - __clzll(hit);  // last lane whose suffix still covers k
+      if (lane == L) {
+        uint32_t above = suffix - mine;
+        const uint32_t c[4] = {c0, c1, c2, c3};
+        int digit = 4 * lane;
+        for (int dd = 3; dd >= 0; --dd) {
+          if (above + c[dd] >= remaining || dd == 0) {
+            digit = 4 * lane + dd;
+            break;
+          }
+          above += c[dd];
+        }
+        sh_prefix = prefix | (static_cast<uint32_t>(digit) << shift);
+        sh_remaining = remaining - above;
+      }
     }
     __syncthreads();
     prefix = sh_prefix;
@@ -170,12 +198,12 @@ select_topk_kernel(const float* __restrict__ scores, const int32_t* __restrict__
   uint32_t n_eq = 0;
   for (int i = i0; i < i1; ++i) n_eq += keys[i] == kth;
   uint32_t tot;
-  uint32_t eq_before = block_exclusive_scan(n_eq, scan_tmp, &tot);
+  const uint32_t eq_before = block_exclusive_scan(n_eq, scan_tmp, &tot);
   uint32_t n_sel = 0;
   {
     uint32_t r = eq_before;
     for (int i = i0; i < i1; ++i) {
-      uint32_t key = keys[i];
+      const uint32_t key = keys[i];
       if (key > kth) {
         ++n_sel;
       } else if (key == kth) {
@@ -188,7 +216,7 @@ select_topk_kernel(const float* __restrict__ scores, const int32_t* __restrict__
   {
     uint32_t r = eq_before;
     for (int i = i0; i < i1; ++i) {
-      uint32_t key = keys[i];
+      const uint32_t key = keys[i];
       bool take = false;
       if (key > kth) {
         take = true;

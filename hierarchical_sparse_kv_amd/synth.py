@@ -8,9 +8,10 @@ Workload recipes (shapes follow the pages' setting: Llama-3.1-8B-shaped GQA
 heads, 16K+ token reasoning outputs at batch 8, paragraph "thoughts" of a few
 hundred tokens as in ZoomR Sec. 3.5's worked example):
 
-* K, V ~ N(0, 1), rounded to the workload dtype, written straight into a paged
-  pool [num_blocks][Hkv][16][d] (the values are i.i.d., so drawing them in
-  physical order is the same distribution as drawing them in logical order).
+* K, V ~ N(0, 1), rounded to the workload dtype, written straight into the
+  paged pools, keys [num_blocks][Hkv][16][d] and values [num_blocks][Hkv][d][16]
+  (the values are i.i.d., so drawing them in physical order is the same
+  distribution as drawing them in logical order).
 * Thought lengths are integers drawn until they cover the sequence; the last
   thought is cut to end at the last cached token.
 * Summary key of a thought (per KV head) = mean of that thought's cached keys
@@ -83,7 +84,7 @@ class Workload:
     th_len: np.ndarray            # int32 [n_total]
     planted: np.ndarray           # int32 [B][Hkv][n_planted] (local thought index)
     k_pool: torch.Tensor          # [num_blocks][Hkv][16][d]
-    v_pool: torch.Tensor
+    v_pool: torch.Tensor          # [num_blocks][Hkv][d][16]
     summary_keys: torch.Tensor    # [n_total][Hkv][d]
     q: torch.Tensor               # [B][Hq][d]
     extra: dict = field(default_factory=dict)
@@ -227,9 +228,10 @@ def make_workload(cfg_id, seed=None, device="cpu", overrides=None, seq_lens=None
     gen = torch.Generator(device=device)
     gen.manual_seed(int(seed if value_seed is None else value_seed) * 7919 + 17)
     dt = TORCH_DTYPE[cfg["dtype"]]
-    shape = (st["num_blocks"], cfg["Hkv"], BLOCK_SIZE, cfg["d"])
-    k_pool = torch.randn(shape, generator=gen, device=device, dtype=torch.float32).to(dt)
-    v_pool = torch.randn(shape, generator=gen, device=device, dtype=torch.float32).to(dt)
+    k_shape = (st["num_blocks"], cfg["Hkv"], BLOCK_SIZE, cfg["d"])   # one row per slot
+    v_shape = (st["num_blocks"], cfg["Hkv"], cfg["d"], BLOCK_SIZE)   # dimension-major
+    k_pool = torch.randn(k_shape, generator=gen, device=device, dtype=torch.float32).to(dt)
+    v_pool = torch.randn(v_shape, generator=gen, device=device, dtype=torch.float32).to(dt)
     kbar = _summary_keys(k_pool, st, cfg, gen, device)
     B, Hq, Hkv, d = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["d"]
     G = Hq // Hkv

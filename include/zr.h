@@ -37,9 +37,14 @@
  *
  * Data layouts (row-major, innermost last; dtype = zr_geom.dtype)
  *   q            [batch][n_q_heads][head_dim]                    dtype
- *   k_pool/v_pool[num_blocks][n_kv_heads][block_size=16][head_dim] dtype
- *                token j of sequence b, KV head g is row
- *                pool[block_table[b][j/16]][g][j%16][:]
+ *   k_pool       [num_blocks][n_kv_heads][16][head_dim]          dtype
+ *                token j of sequence b, KV head g is the key row
+ *                k_pool[block_table[b][j/16]][g][j%16][:]
+ *   v_pool       [num_blocks][n_kv_heads][head_dim][16]          dtype
+ *                values are stored dimension-major inside a block: the
+ *                value of token j is v_pool[block_table[b][j/16]][g][:][j%16]
+ *                (each dimension's 16 slots are contiguous, so a block's
+ *                values load directly as matrix-core operands)
  *   block_table  [batch][max_blocks_per_seq]                     int32
  *   seq_lens     [batch]  cached tokens T_b                      int32
  *   thoughts     CSR by sequence: thoughts of sequence b are rows
@@ -76,14 +81,14 @@ typedef enum { ZR_F32 = 0, ZR_BF16 = 1 } zr_dtype;
 
 /* Built limits. */
 #define ZR_BLOCK_SIZE 16
-#define ZR_MAX_K 4096                 /* k of zr_select_topk / zr_sparse_decode_attn */
+#define ZR_MAX_K 1024                 /* k of zr_select_topk / zr_sparse_decode_attn */
 #define ZR_MAX_THOUGHTS_PER_SEQ 8192  /* zr_thoughts.max_per_seq */
-#define ZR_MAX_SPLITS 1024            /* split-K partitions per (sequence, KV head) */
+#define ZR_MAX_PAIRS 4096             /* batch * n_kv_heads of the attention calls */
 
 typedef struct {
   int32_t batch;              /* B >= 0 (B = 0: every call is a no-op) */
   int32_t n_q_heads;          /* Hq > 0, multiple of n_kv_heads */
-  int32_t n_kv_heads;         /* Hkv > 0; Hq / Hkv in {1, 2, 4, 8} */
+  int32_t n_kv_heads;         /* Hkv > 0; Hq / Hkv in {1, 2, 4, 8, 16} (16: bf16 only) */
   int32_t head_dim;           /* 64 or 128 */
   int32_t block_size;         /* must be ZR_BLOCK_SIZE (16) */
   int32_t max_blocks_per_seq; /* columns of block_table, >= 1 */
@@ -139,8 +144,10 @@ zr_status zr_select_topk(const zr_geom* geom, const zr_thoughts* th, const float
  * Split-K: each (b, g) is cut into partitions of the attended token list;
  * `max_attended` is the caller's bound on tokens per (b, g) used to size the
  * grid (a larger count is still handled correctly, just with fewer
- * partitions). `workspace` holds per-partition partial results and must be at
- * least zr_workspace_bytes(geom, max_attended) bytes (16-byte aligned).
+ * partitions). `workspace` holds per-partition partial results (no state
+ * is kept between calls); it must be at least zr_workspace_bytes(geom,
+ * max_attended) bytes and 16-byte aligned, and calls that share a workspace
+ * must not run concurrently.
  * Errors: ZR_E_NULL, ZR_E_SHAPE (k, window, max_attended < 0; k > ZR_MAX_K),
  * ZR_E_UNSUPPORTED, ZR_E_WORKSPACE, ZR_E_ALIGN, ZR_E_LAUNCH.
  */

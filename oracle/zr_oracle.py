@@ -8,10 +8,12 @@ imports nothing from the product package; callers hand it plain numpy arrays.
 What it computes, step by step, in float64 (inputs are fp32 or bf16 values,
 which convert to float64 exactly):
 
-1. ``gather_logical``  - the paged cache read: logical token j of a sequence
-   lives in physical block ``block_table[j // 16]`` at slot ``j % 16``
-   (KV-cache management page, "Paged KV cache (PagedAttention)": block table
-   per sequence, attention as a sum over blocks fetched through the table).
+1. ``gather_keys`` / ``gather_values`` - the paged cache read: logical token
+   j of a sequence lives in physical block ``block_table[j // 16]`` at slot
+   ``j % 16`` (KV-cache management page, "Paged KV cache (PagedAttention)":
+   block table per sequence, attention as a sum over blocks fetched through
+   the table). Key blocks hold one row per slot; value blocks are stored
+   dimension-major (each dimension's 16 slots contiguous).
 2. ``coarse_scores``   - approximate attention score of the decode query
    against every mean summary key (ZoomR, Sec. 3.3 "Per-Head Importance
    Scoring and Voting", eq. for alpha_i). With grouped-query attention one
@@ -50,19 +52,37 @@ BLOCK_SIZE = 16
 # --------------------------------------------------------------------------
 # 1. Paged cache read
 # --------------------------------------------------------------------------
-def gather_logical(pool: np.ndarray, table_row: np.ndarray, n_tokens: int) -> np.ndarray:
-    """Logical view of one sequence's K (or V): float64 [n_tokens][Hkv][d].
+def gather_logical(pool: np.ndarray, table_row: np.ndarray, n_tokens: int,
+                   slot_axis: int = 2) -> np.ndarray:
+    """Logical view of one sequence's keys or values: float64 [n_tokens][Hkv][d].
 
-    ``pool`` is [num_blocks][Hkv][BLOCK_SIZE][d]; ``table_row`` maps logical
-    block index to physical block id. Token j is read from block
-    ``table_row[j // BLOCK_SIZE]``, slot ``j % BLOCK_SIZE`` (paged KV cache,
-    KV-cache management page, "Paged KV cache (PagedAttention)").
+    Token j is in physical block ``table_row[j // BLOCK_SIZE]`` at slot
+    ``j % BLOCK_SIZE`` (paged KV cache, KV-cache management page, "Paged KV
+    cache (PagedAttention)"). The page leaves the layout inside a block open;
+    keys are [num_blocks][Hkv][16][d] (``slot_axis=2``, one row per slot) and
+    values are [num_blocks][Hkv][d][16] (``slot_axis=3``, dimension-major).
     """
     j = np.arange(n_tokens)
     blocks = np.asarray(table_row)[j // BLOCK_SIZE]
     slots = j % BLOCK_SIZE
-    # pool[blocks[t], :, slots[t], :] for every t -> [n_tokens][Hkv][d]
-    return np.asarray(pool)[blocks, :, slots, :].astype(np.float64)
+    pool = np.asarray(pool)
+    if slot_axis == 2:
+        # pool[blocks[t], :, slots[t], :] for every t -> [n_tokens][Hkv][d]
+        return pool[blocks, :, slots, :].astype(np.float64)
+    if slot_axis == 3:
+        # pool[blocks[t], :, :, slots[t]] for every t -> [n_tokens][Hkv][d]
+        return pool[blocks, :, :, slots].astype(np.float64)
+    raise ValueError(slot_axis)
+
+
+def gather_keys(k_pool, table_row, n_tokens):
+    """Keys of one sequence in logical order (block layout [Hkv][16][d])."""
+    return gather_logical(k_pool, table_row, n_tokens, slot_axis=2)
+
+
+def gather_values(v_pool, table_row, n_tokens):
+    """Values of one sequence in logical order (block layout [Hkv][d][16])."""
+    return gather_logical(v_pool, table_row, n_tokens, slot_axis=3)
 
 
 # --------------------------------------------------------------------------
@@ -203,8 +223,8 @@ def sparse_decode_step(q, k_pool, v_pool, block_table, seq_lens, seq_ptr, starts
     for b, g in todo:
         T = int(seq_lens[b])
         if b not in cache:
-            cache = {b: (gather_logical(k_pool, block_table[b], T),
-                         gather_logical(v_pool, block_table[b], T))}
+            cache = {b: (gather_keys(k_pool, block_table[b], T),
+                         gather_values(v_pool, block_table[b], T))}
         K, V = cache[b]
         lo, hi = int(seq_ptr[b]), int(seq_ptr[b + 1])
         toks = attended_tokens(use_sel[b, g], starts[lo:hi], lens[lo:hi], T, window)
@@ -226,8 +246,8 @@ def dense_decode_step(q, k_pool, v_pool, block_table, seq_lens, scale, pairs=Non
     for b, g in todo:
         T = int(seq_lens[b])
         if b not in cache:
-            cache = {b: (gather_logical(k_pool, block_table[b], T),
-                         gather_logical(v_pool, block_table[b], T))}
+            cache = {b: (gather_keys(k_pool, block_table[b], T),
+                         gather_values(v_pool, block_table[b], T))}
         K, V = cache[b]
         out[b, g * G:(g + 1) * G] = attend(q[b, g * G:(g + 1) * G], K[:, g], V[:, g], scale)
     return out

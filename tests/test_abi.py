@@ -55,16 +55,26 @@ def _th(**kw):
 def test_workspace_bytes(L):
     g = _geom()
     n = zr.zr_workspace_bytes(g, 1000)
-    # 1000 tokens at 256 per partition -> 4 partitions; rows = B*Hkv*S*G
-    rows = 2 * 2 * 4 * 4
-    assert n == ((2 * rows * 4 + 15) // 16) * 16 + rows * 128 * 4
+    # 4 (sequence, KV head) pairs of at most ceil(1000/16) + 2 blocks, 8 blocks
+    # per workgroup -> 33 workgroups; partial slots = workgroups + pairs; the
+    # pair prefix (pairs + 2 ints) first, then m, l [slots][G] and
+    # acc [slots][G][128], each region 16-byte aligned
+    up16 = lambda x: (x + 15) // 16 * 16
+    nwg = -(-4 * (-(-1000 // 16) + 2) // 8)
+    slots = nwg + 4
+    assert n == up16(6 * 4) + 2 * up16(slots * 4 * 4) + slots * 4 * 128 * 4
+    # the grid is capped at 512 workgroups
+    big = zr.zr_workspace_bytes(g, 10 ** 6)
+    assert big == up16(6 * 4) + 2 * up16(516 * 16) + 516 * 4 * 128 * 4
     assert zr.zr_workspace_bytes(_geom(head_dim=96), 10) == 0
     assert zr.zr_workspace_bytes(g, -1) == 0
+    assert zr.zr_workspace_bytes(_geom(batch=1024, n_q_heads=32, n_kv_heads=8), 10) == 0
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(n_q_heads=6, n_kv_heads=4), zr.ZR_E_SHAPE),
     (dict(n_q_heads=48, n_kv_heads=2), zr.ZR_E_UNSUPPORTED),
+    (dict(n_q_heads=32, n_kv_heads=2, dtype=zr.ZR_F32), zr.ZR_E_UNSUPPORTED),
     (dict(head_dim=96), zr.ZR_E_UNSUPPORTED),
     (dict(block_size=32), zr.ZR_E_UNSUPPORTED),
     (dict(dtype=7), zr.ZR_E_UNSUPPORTED),
@@ -88,7 +98,7 @@ def test_null_and_range_errors(L):
     assert zr.zr_coarse_score(g, FAKE + 4, _th(), FAKE) == zr.ZR_E_ALIGN
     assert zr.zr_coarse_score(g, FAKE, _th(max_per_seq=100000), FAKE) == zr.ZR_E_UNSUPPORTED
     assert zr.zr_select_topk(g, _th(), FAKE, -1, FAKE) == zr.ZR_E_SHAPE
-    assert zr.zr_select_topk(g, _th(), FAKE, 5000, FAKE) == zr.ZR_E_SHAPE
+    assert zr.zr_select_topk(g, _th(), FAKE, 1025, FAKE) == zr.ZR_E_SHAPE
     assert zr.zr_select_topk(g, _th(), FAKE, 3, None) == zr.ZR_E_NULL
     assert zr.zr_select_topk(g, _th(seq_ptr=None), FAKE, 3, FAKE) == zr.ZR_E_NULL
     args = lambda **kw: dict(dict(geom=g, q=FAKE, k_pool=FAKE, v_pool=FAKE, block_table=FAKE,

@@ -215,15 +215,20 @@ def test_attend_closed_forms():
 
 
 # ---------------------------------------------------------------- paging
-def _scatter_to_pool(K, perm_seed, extra_blocks=3):
-    """Write a contiguous [T][Hkv][d] cache into a pool at random physical blocks."""
+def _scatter_to_pool(K, perm_seed, extra_blocks=3, slot_axis=2):
+    """Write a contiguous [T][Hkv][d] cache into a pool at random physical
+    blocks, one row per slot (slot_axis 2) or dimension-major (slot_axis 3)."""
     T, Hkv, d = K.shape
     nb = (T + 15) // 16
     rng = np.random.default_rng(perm_seed)
     ids = rng.permutation(nb + extra_blocks)[:nb]
-    pool = rng.standard_normal((nb + extra_blocks, Hkv, 16, d))
+    shape = (nb + extra_blocks, Hkv, 16, d) if slot_axis == 2 else (nb + extra_blocks, Hkv, d, 16)
+    pool = rng.standard_normal(shape)
     for j in range(T):
-        pool[ids[j // 16], :, j % 16, :] = K[j]
+        if slot_axis == 2:
+            pool[ids[j // 16], :, j % 16, :] = K[j]
+        else:
+            pool[ids[j // 16], :, :, j % 16] = K[j]
     return pool, ids.astype(np.int32)
 
 
@@ -231,7 +236,11 @@ def test_paged_equals_contiguous():
     rng = np.random.default_rng(3)
     K = rng.standard_normal((53, 2, 4))
     pool, table = _scatter_to_pool(K, 11)
-    assert np.array_equal(O.gather_logical(pool, table, 53), K)
+    assert np.array_equal(O.gather_keys(pool, table, 53), K)
+    vpool, vtable = _scatter_to_pool(K, 12, slot_axis=3)
+    assert np.array_equal(O.gather_values(vpool, vtable, 53), K)
+    # one element placed by hand: token 37, head 1, dim 2
+    assert O.gather_values(vpool, vtable, 53)[37, 1, 2] == vpool[vtable[2], 1, 2, 5]
 
 
 def _tiny_case(seed, T=77, Hq=4, Hkv=2, d=8, W=9):
@@ -255,7 +264,7 @@ def test_sparse_step_invariant_under_block_permutation(seed):
     outs = []
     for perm_seed in (1, 2, 3):
         kp, table = _scatter_to_pool(K, perm_seed)
-        vp, _ = _scatter_to_pool(V, perm_seed)  # same seed -> same block ids
+        vp, _ = _scatter_to_pool(V, perm_seed, slot_axis=3)  # same seed -> same block ids
         r = O.sparse_decode_step(q, kp, vp, table[None], np.array([T]), ptr, starts, lens,
                                  kbar, 3, W, 0.35)
         outs.append(r["out"])
@@ -269,7 +278,7 @@ def test_sparse_all_thoughts_equals_dense_sdpa(seed):
     T, Hkv, d = K.shape
     G = q.shape[1] // Hkv
     kp, table = _scatter_to_pool(K, 5)
-    vp, _ = _scatter_to_pool(V, 5)
+    vp, _ = _scatter_to_pool(V, 5, slot_axis=3)
     ptr = np.array([0, len(starts)], np.int32)
     r = O.sparse_decode_step(q, kp, vp, table[None], np.array([T]), ptr, starts, lens, kbar,
                              len(starts), W, 0.35)
@@ -290,7 +299,7 @@ def test_sparse_step_equals_masked_sdpa(seed):
     T, Hkv, d = K.shape
     G = q.shape[1] // Hkv
     kp, table = _scatter_to_pool(K, 9)
-    vp, _ = _scatter_to_pool(V, 9)
+    vp, _ = _scatter_to_pool(V, 9, slot_axis=3)
     ptr = np.array([0, len(starts)], np.int32)
     k = 2
     r = O.sparse_decode_step(q, kp, vp, table[None], np.array([T]), ptr, starts, lens, kbar,

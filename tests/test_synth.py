@@ -33,6 +33,7 @@ def test_structure_tiles_and_pages(cfg):
         used.extend(w.block_table[b, :nb].tolist())
     assert sorted(used) == list(range(w.num_blocks))
     assert tuple(w.k_pool.shape) == (w.num_blocks, w.Hkv, 16, w.d)
+    assert tuple(w.v_pool.shape) == (w.num_blocks, w.Hkv, w.d, 16)
     assert w.k_pool.dtype == synth.TORCH_DTYPE[w.dtype]
 
 
