@@ -1,0 +1,45 @@
+"""The decode step captured in a HIP graph gives, on every replay, exactly the
+eager result (the benchmark times graph replays)."""
+import pytest
+import torch
+
+from hierarchical_sparse_kv_amd import synth, zr
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    zr.lib()
+
+
+def test_graph_replays_match_eager():
+    w = synth.make_workload(1, device="cuda", overrides=dict(B=4, seq_len=("fixed", 4096)))
+    other = synth.make_workload(3, device="cuda",
+                                overrides=dict(B=3, seq_len=("uniform", 500, 3000)))
+    st, st2 = zr.step_from_workload(w), zr.step_from_workload(other)
+    st.step()
+    torch.cuda.synchronize()
+    ref = (st.scores.clone(), st.sel.clone(), st.out.clone())
+    st.dense_attn(out=torch.empty_like(st.out))
+
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            st.step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        st.out.fill_(float("nan"))
+        st.sel.fill_(-7)
+        st2.step()              # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(st.scores, ref[0]), rep
+        assert torch.equal(st.sel, ref[1]), rep
+        assert torch.equal(st.out, ref[2]), rep
