@@ -3,8 +3,8 @@
 Workload: Llama-3.1-8B-shaped single-layer decode step, batch 8, 32 query /
 8 KV heads, head_dim 128, 16384 cached tokens per sequence, bf16, thoughts of
 64-512 tokens, top-8 thoughts + 128-token window, paged (16-token blocks,
-random block table). A step = zr_coarse_score + zr_select_topk +
-zr_sparse_decode_attn for the whole batch, on layer (step mod L) of L
+random block table). A step = one zr_sparse_decode_step call (scores, top-k,
+block lists, attention, combine) for the whole batch, on layer (step mod L) of L
 independent layer caches (L = 32 by default: the 17.2 GB cache of a 32-layer
 model), so the bytes come from HBM, not from the 256 MB Infinity Cache.
 
@@ -14,6 +14,7 @@ the timed region starts.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -25,6 +26,22 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+
+# HBM bytes per zr_sparse_decode_attn call on this workload, from hardware
+# counters (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE, summed over the
+# call's kernels, each scaled by the counter's reading for a known-size copy).
+# Valid only for the kernel sources they were taken with: reported as null as
+# soon as any of these files changes.
+TRAFFIC_SOURCES = ("zr_internal.h", "zr_pair.hip", "zr_attn.hip")
+TRAFFIC = None  # {"sources_sha256": ..., "bytes_per_call": ...}
+
+
+def sources_sha256():
+    h = hashlib.sha256()
+    for name in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, "hierarchical_sparse_kv_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 METRIC = "decode steps/s and effective KV GB/s (% of HBM peak), 16K tokens, batch 8"
 
 
@@ -65,6 +82,10 @@ def main():
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibrate", action="store_true",
+                    help="first run an elementwise copy (negation) of 1 GiB into 1 GiB twice, "
+                         "untimed: the known-size kernel that scales hardware byte counters "
+                         "(FETCH_SIZE, WRITE_SIZE)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the decode step is built and timed on a "
@@ -78,6 +99,13 @@ def main():
     torch.cuda.set_device(0)
     dev = "cuda:0"
     L = args.layers
+    if args.copy_calibrate:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     log(f"[bench] generating {L} layer caches (config: llama8b-16k-b8)")
     layers, steps = [], []
     for l in range(L):
@@ -124,6 +152,7 @@ def main():
     log(f"[bench] capturing {args.warmup} warmup and {args.steps} timed steps")
     g_warm = capture(lambda i: steps[i % L].step(), max(args.warmup, 1))
     g_step = capture(lambda i: steps[i % L].step(), args.steps)
+    g_calls = capture(lambda i: steps[i % L].step_calls(), args.steps)
     g_attn = capture(lambda i: steps[i % L].sparse_attn(), args.steps)
     g_dense = capture(lambda i: steps[i % L].dense_attn(), L)
     if args.warmup > 0:
@@ -132,9 +161,11 @@ def main():
     log(f"[bench] timing {args.steps} steps")
     us_per_step = timed(g_step, args.steps)
     ms_per_step = us_per_step / 1e3
+    calls_us = timed(g_calls, args.steps)
 
-    # dominant kernel: the sparse attention call (attention + combine kernels),
-    # timed with HIP events around a graph of back-to-back calls on its stream
+    # dominant kernel: the sparse attention call (block lists, attention and
+    # combine kernels), timed with HIP events around a graph of back-to-back
+    # calls on the stream they run on
     attn_us = timed(g_attn, args.steps)
     bytes_per_launch = float(np.mean([kv_bytes[i % L] for i in range(args.steps)]))
     achieved = bytes_per_launch / (attn_us * 1e-6) / 1e9
@@ -168,10 +199,15 @@ def main():
                    "global_batch": w0.B, "seq_len": int(w0.seq_lens[0]),
                    "layers_rotated": L, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "zr_sparse_decode_attn (attn_mfma_kernel + attn_combine_kernel)",
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": (TRAFFIC["bytes_per_call"]
+                                 if TRAFFIC and TRAFFIC["sources_sha256"] == sources_sha256()
+                                 else None),
+                     "kernel": "zr_sparse_decode_attn call: pair_kernel (block lists) + "
+                               "attn_mfma_kernel + attn_combine_kernel",
                      "avg_launch_us": round(attn_us, 3),
                      "algorithmic_bytes_per_launch": int(bytes_per_launch)},
+        "step_as_three_calls_us": round(calls_us, 3),
         "effective_kv_gbs": round(achieved, 1),
         "kv_tokens_per_step": int(np.mean([a.sum() for a in att])),
         "q_out_bytes_per_step": q_out_bytes,

@@ -74,6 +74,30 @@ zr_status attention_common(const zr_geom* geom, const void* q, const void* k_poo
   return ZR_OK;
 }
 
+void fill_pair_sizes(const zr_geom& g, const zr_thoughts& th, int k, int window,
+                     zr::PairArgs* pa) {
+  pa->n_total = th.n_total;
+  pa->max_per_seq = th.max_per_seq;
+  pa->Hq = g.n_q_heads;
+  pa->Hkv = g.n_kv_heads;
+  pa->k = k;
+  pa->window = window;
+  pa->max_blocks = g.max_blocks_per_seq;
+  pa->num_blocks = g.num_blocks;
+}
+
+// Plan-mode arguments: the pair kernel writes its block lists into the
+// workspace regions the attention kernel reads.
+void fill_plan(const zr_geom& g, const zr_thoughts& th, int k, int window,
+               const int32_t* block_table, const int32_t* seq_lens, const zr::AttnArgs& a,
+               zr::PairArgs* pa) {
+  fill_pair_sizes(g, th, k, window, pa);
+  pa->seq_lens = seq_lens;
+  pa->block_table = block_table;
+  pa->counts = const_cast<int32_t*>(a.counts);
+  pa->entries = const_cast<int2*>(a.entries);
+}
+
 }  // namespace
 
 ZR_API const char* zr_status_string(zr_status s) {
@@ -103,8 +127,13 @@ ZR_API zr_status zr_coarse_score(const zr_geom* geom, const void* q, const zr_th
   if (st != ZR_OK) return st;
   if (!q || !scores) return ZR_E_NULL;
   if (!aligned16(q)) return ZR_E_ALIGN;
-  if (zr::launch_coarse_score(*geom, q, *th, scores, static_cast<hipStream_t>(stream)) !=
-      hipSuccess)
+  zr::PairArgs a{};
+  a.q = q;
+  a.kbar = th->summary_keys;
+  a.seq_ptr = th->seq_ptr;
+  a.scores = scores;
+  fill_pair_sizes(*geom, *th, 0, 0, &a);
+  if (zr::launch_pair(*geom, a, zr::kModeScore, static_cast<hipStream_t>(stream)) != hipSuccess)
     return ZR_E_LAUNCH;
   return ZR_OK;
 }
@@ -116,8 +145,15 @@ ZR_API zr_status zr_select_topk(const zr_geom* geom, const zr_thoughts* th, cons
   st = check_thoughts(th, false);
   if (st != ZR_OK) return st;
   if (k < 0 || k > ZR_MAX_K) return ZR_E_SHAPE;
-  if (k > 0 && (!scores || !sel)) return ZR_E_NULL;
-  if (zr::launch_select_topk(*geom, *th, scores, k, sel, static_cast<hipStream_t>(stream)) !=
+  if (k == 0) return ZR_OK;
+  if (!scores || !sel) return ZR_E_NULL;
+  if (!zr::pair_lds_ok(*geom, th->max_per_seq, k, true, false)) return ZR_E_UNSUPPORTED;
+  zr::PairArgs a{};
+  a.seq_ptr = th->seq_ptr;
+  a.scores = const_cast<float*>(scores);  // read only in this mode
+  a.sel = sel;
+  fill_pair_sizes(*geom, *th, k, 0, &a);
+  if (zr::launch_pair(*geom, a, zr::kModeSelect, static_cast<hipStream_t>(stream)) !=
       hipSuccess)
     return ZR_E_LAUNCH;
   return ZR_OK;
@@ -135,21 +171,52 @@ ZR_API zr_status zr_sparse_decode_attn(const zr_geom* geom, const void* q, const
   if (st != ZR_OK) return st;
   if (k < 0 || k > ZR_MAX_K || window < 0) return ZR_E_SHAPE;
   if (k > 0 && !sel) return ZR_E_NULL;
-  if (!zr::attn_lds_ok(*geom, k, false)) return ZR_E_UNSUPPORTED;
   zr::AttnArgs a{};
   st = attention_common(geom, q, k_pool, v_pool, block_table, seq_lens, scale, out, workspace,
                         ws_bytes, max_attended, &a);
   if (st != ZR_OK) return st;
-  a.seq_ptr = th->seq_ptr;
-  a.th_start = th->start;
-  a.th_len = th->len;
-  a.sel = sel;
-  a.n_total = th->n_total;
-  a.k = k;
-  a.window = window;
-  if (zr::launch_attention(*geom, a, false, static_cast<hipStream_t>(stream)) !=
-      hipSuccess)
-    return ZR_E_LAUNCH;
+  if (!zr::pair_lds_ok(*geom, th->max_per_seq, k, false, true)) return ZR_E_UNSUPPORTED;
+  zr::PairArgs pa{};
+  pa.seq_ptr = th->seq_ptr;
+  pa.th_start = th->start;
+  pa.th_len = th->len;
+  pa.sel = const_cast<int32_t*>(sel);  // read only in this mode
+  fill_plan(*geom, *th, k, window, block_table, seq_lens, a, &pa);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (zr::launch_pair(*geom, pa, zr::kModePlan, s) != hipSuccess) return ZR_E_LAUNCH;
+  if (zr::launch_attention(*geom, a, false, s) != hipSuccess) return ZR_E_LAUNCH;
+  return ZR_OK;
+}
+
+ZR_API zr_status zr_sparse_decode_step(const zr_geom* geom, const void* q, const void* k_pool,
+                                       const void* v_pool, const int32_t* block_table,
+                                       const int32_t* seq_lens, const zr_thoughts* th, int32_t k,
+                                       int32_t window, float scale, int32_t max_attended,
+                                       float* scores, int32_t* sel, float* out,
+                                       void* workspace, size_t ws_bytes, void* stream) {
+  zr_status st = check_geom(geom);
+  if (st != ZR_OK) return st;
+  st = check_thoughts(th, true);
+  if (st != ZR_OK) return st;
+  if (k < 0 || k > ZR_MAX_K || window < 0) return ZR_E_SHAPE;
+  if (!scores || (k > 0 && !sel)) return ZR_E_NULL;
+  zr::AttnArgs a{};
+  st = attention_common(geom, q, k_pool, v_pool, block_table, seq_lens, scale, out, workspace,
+                        ws_bytes, max_attended, &a);
+  if (st != ZR_OK) return st;
+  if (!zr::pair_lds_ok(*geom, th->max_per_seq, k, true, true)) return ZR_E_UNSUPPORTED;
+  zr::PairArgs pa{};
+  pa.q = q;
+  pa.kbar = th->summary_keys;
+  pa.seq_ptr = th->seq_ptr;
+  pa.th_start = th->start;
+  pa.th_len = th->len;
+  pa.scores = scores;
+  pa.sel = sel;
+  fill_plan(*geom, *th, k, window, block_table, seq_lens, a, &pa);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (zr::launch_pair(*geom, pa, zr::kModeStep, s) != hipSuccess) return ZR_E_LAUNCH;
+  if (zr::launch_attention(*geom, a, false, s) != hipSuccess) return ZR_E_LAUNCH;
   return ZR_OK;
 }
 
@@ -160,13 +227,11 @@ ZR_API zr_status zr_dense_paged_decode_attn(const zr_geom* geom, const void* q,
                                             size_t ws_bytes, void* stream) {
   zr_status st = check_geom(geom);
   if (st != ZR_OK) return st;
-  if (!zr::attn_lds_ok(*geom, 0, true)) return ZR_E_UNSUPPORTED;
   zr::AttnArgs a{};
   st = attention_common(geom, q, k_pool, v_pool, block_table, seq_lens, scale, out, workspace,
                         ws_bytes, geom->max_blocks_per_seq * ZR_BLOCK_SIZE, &a);
   if (st != ZR_OK) return st;
-  if (zr::launch_attention(*geom, a, true, static_cast<hipStream_t>(stream)) !=
-      hipSuccess)
+  if (zr::launch_attention(*geom, a, true, static_cast<hipStream_t>(stream)) != hipSuccess)
     return ZR_E_LAUNCH;
   return ZR_OK;
 }

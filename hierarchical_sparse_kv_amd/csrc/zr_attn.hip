@@ -1,32 +1,26 @@
 // Split-K decode attention over a paged KV pool, sparse ("zoomed-in") and dense.
 //
-// Attended tokens of one (sequence b, KV head g), a "pair":
-//   sparse: each selected thought's span [start, start+len) clipped below
-//           T - window, then the window [T - window, T)  (ZoomR Sec. 3.3,
-//           eq. I_f restricted to the window and the full-resolution spans;
-//           the clip makes the union count each token once);
-//   dense:  [0, T).
-// The spans are cut at the 16-token block boundaries of the paged cache
-// (KV-cache management page, paged KV cache, eq. 4: attention as a sum over
-// blocks fetched through the block table). A pair's work list is the sequence
-// of (logical block, 16-bit slot mask) entries over its spans; only attended
-// slots are fetched (the gather reads kept entries, it does not mask a full
-// read).
+// The tokens of one (sequence b, KV head g), a "pair", arrive as a list of
+// (physical block, 16-bit slot mask) entries (KV-cache management page, paged
+// KV cache, eq. 4: attention as a sum over blocks fetched through the block
+// table). Sparse: the pair kernel lists the blocks of the window and the
+// selected thoughts' spans (ZoomR Sec. 3.3, eq. I_f restricted to those
+// spans); dense: every block of [0, T), read from the block table here. Only
+// attended slots enter the softmax; the gather reads the listed blocks, it
+// does not mask a full read.
 //
 // Work split. The grid is sized once for the whole GPU (about `nwg`
-// workgroups). Every workgroup stages the plan inputs (sequence lengths,
-// selections, thought spans) in LDS with one round of independent loads,
-// counts every pair's blocks (one item per (pair, span), LDS atomics), and
-// gives pair p a number of workgroups proportional to its block count,
-// S_p = max(1, round(n_p / per)), per = ceil(total / nwg). Each workgroup
-// thus serves exactly one pair with about `per` blocks, however ragged the
-// pairs are. Its 4 waves take chunks of NBW blocks in turn: a wave resolves
-// all its block-table entries at once (one lane per entry), then streams its
-// chunks with the next chunk's K/V loads in flight while the current one is
-// computed, keeping a running (max, sum, weighted V) per query head (online
-// softmax across chunks, two-pass inside one). The waves merge in LDS into
-// one partial per workgroup; a combine kernel merges each pair's partials by
-// log-sum-exp. (Merging inside the attention kernel would need a device-scope
+// workgroups). Every workgroup reads all pairs' list lengths n_p and gives
+// pair p a number of workgroups proportional to its length,
+// S_p = max(1, round(n_p / per)), per = ceil(total / nwg), so each workgroup
+// serves one pair with about `per` blocks however ragged the pairs are. Its
+// 4 waves take chunks of NBW blocks in turn: a wave loads all its entries at
+// once (one lane per entry), then streams its chunks with the next chunk's
+// K/V loads in flight while the current one is computed, keeping a running
+// (max, sum, weighted V) per query head (online softmax across chunks,
+// two-pass inside one). The waves merge in LDS into one partial per
+// workgroup; a combine kernel merges each pair's partials by log-sum-exp.
+// (Merging inside the attention kernel would need a device-scope
 // release/acquire per workgroup, which on this GPU writes back and
 // invalidates the whole L2; the kernel boundary is far cheaper.)
 //
@@ -57,7 +51,7 @@ constexpr int kWaves = kThreads / 64;
 constexpr float kNegInf = -INFINITY;
 constexpr int kTargetWorkgroups = 512;  // two per CU on MI355X: one resident round
 constexpr int kMinBlocksPerWg = 8;
-constexpr int kStageCap = 8192;         // ints of selections / spans staged in LDS
+constexpr int kPairsPerThread = (ZR_MAX_PAIRS + kThreads - 1) / kThreads;
 
 typedef short bf16x8 __attribute__((vector_size(16)));
 typedef short bf16x4 __attribute__((vector_size(8)));
@@ -66,296 +60,121 @@ typedef float f32x2v __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------------------
-// Plan inputs (LDS copies when they fit, else global memory)
+// Work assignment
 // ---------------------------------------------------------------------------
-struct Stage {
-  const int32_t* seq_ptr;
-  const int32_t* seq_lens;
-  const int32_t* sel;
-  const int32_t* th_s;
-  const int32_t* th_l;
-};
-
-// Dynamic LDS layout (int32): cnt[P+1] prefS[P+1] seq_ptr[B+1] seq_lens[B]
-// [sel[P*k] th_s[n] th_l[n] when staged] plan s/e/pref[3*(k+2)]
-// [block-table row[max_blocks] when row_lds].
-__host__ __device__ inline size_t lds_ints(int B, int Hkv, int k, int n_total, bool dense,
-                                           bool staged, int row_ints) {
-  const size_t P = static_cast<size_t>(B) * Hkv;
-  size_t n = 2 * (P + 1) + 2 * static_cast<size_t>(B) + 1;
-  if (!dense && staged) n += P * k + 2 * static_cast<size_t>(n_total);
-  n += 3 * static_cast<size_t>((dense ? 0 : k) + 2);
-  n += static_cast<size_t>(row_ints);
-  return n;
-}
-
-struct LdsLayout {
-  int32_t* cnt;    // [P]; cnt[P] accumulates the total
-  int32_t* prefS;
-  Stage st;
-  int32_t* plan_s;
-  int32_t* plan_e;
-  int32_t* plan_pref;
-  int32_t* row;    // this workgroup's block-table row (when a.row_lds)
-};
-
-template <bool DENSE, bool STAGED>
-__device__ LdsLayout stage_inputs(const AttnArgs& a, int32_t* dyn) {
-  const int P = a.B * a.Hkv;
-  const int t = threadIdx.x;
-  LdsLayout L;
-  int32_t* c = dyn;
-  L.cnt = c;
-  c += P + 1;
-  L.prefS = c;
-  c += P + 1;
-  int32_t* sp = c;
-  c += a.B + 1;
-  int32_t* sl = c;
-  c += a.B;
-  for (int i = t; i <= a.B; i += kThreads) sp[i] = DENSE ? 0 : a.seq_ptr[i];
-  for (int i = t; i < a.B; i += kThreads) sl[i] = a.seq_lens[i];
-  for (int p = t; p <= P; p += kThreads) L.cnt[p] = 0;
-  L.st.seq_ptr = sp;
-  L.st.seq_lens = sl;
-  L.st.sel = a.sel;
-  L.st.th_s = a.th_start;
-  L.st.th_l = a.th_len;
-  if (!DENSE && STAGED) {
-    const int n = P * a.k;
-    for (int i = t; i < n; i += kThreads) c[i] = a.sel[i];
-    L.st.sel = c;
-    c += n;
-    for (int i = t; i < a.n_total; i += kThreads) {
-      c[i] = a.th_start[i];
-      c[a.n_total + i] = a.th_len[i];
-    }
-    L.st.th_s = c;
-    L.st.th_l = c + a.n_total;
-    c += 2 * a.n_total;
-  }
-  const int cap = (DENSE ? 0 : a.k) + 2;
-  L.plan_s = c;
-  L.plan_e = c + cap;
-  L.plan_pref = c + 2 * cap;
-  L.row = c + 3 * cap;
-  return L;
-}
-
-// ---------------------------------------------------------------------------
-// Spans of a pair
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ int blocks_of(int s, int e) {
-  return e > s ? ((e - 1) >> 4) - (s >> 4) + 1 : 0;
-}
-
-__device__ __forceinline__ int cached_len(const AttnArgs& a, const Stage& st, int b) {
-  const int T = st.seq_lens[b];
+__device__ __forceinline__ int cached_len(const AttnArgs& a, int b) {
+  const int T = a.seq_lens[b];
   const int cap = a.max_blocks * kBlock;
   return T < 0 ? 0 : (T > cap ? cap : T);
 }
 
-// Span i (< k: selected thought i, == k: the window) of pair (b, g), clipped.
-__device__ __forceinline__ void pair_span(const AttnArgs& a, const Stage& st, int b, int g,
-                                          int i, int T, int tw, int* s, int* e) {
-  if (i == a.k) {
-    *s = tw;
-    *e = T;
-    return;
-  }
-  *s = 0;
-  *e = 0;
-  const int lo = st.seq_ptr[b];
-  int hi = st.seq_ptr[b + 1];
-  hi = hi < a.n_total ? hi : a.n_total;
-  const int t = st.sel[(static_cast<size_t>(b) * a.Hkv + g) * a.k + i];
-  if (t < 0 || t >= hi - lo) return;
-  int ss = st.th_s[lo + t];
-  int ee = ss + st.th_l[lo + t];
-  ss = ss > 0 ? ss : 0;
-  ee = ee < tw ? ee : tw;
-  *s = ss;
-  *e = ee > ss ? ee : ss;
-}
-
-// Exclusive prefix sum across the workgroup (one value per thread).
-__device__ int wg_exclusive_scan(int v, int* tmp, int* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int x = __shfl_up(incl, o);
-    if (lane >= o) incl += x;
-  }
-  if (lane == 63) tmp[wave] = incl;
-  __syncthreads();
-  int before = 0, all = 0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    before += w < wave ? tmp[w] : 0;
-    all += tmp[w];
-  }
-  __syncthreads();
-  *total = all;
-  return before + incl - v;
-}
-
 struct Assign {
   int p;       // pair
-  int lo, hi;  // blocks [lo, hi) of the pair's list
+  int T;       // cached tokens of the pair's sequence (dense)
+  int lo, hi;  // entries [lo, hi) of the pair's list
 };
 
-// Block counts of every pair, workgroups per pair, and this workgroup's share.
-// Returns false when this workgroup has no work. Workgroup 0 publishes the
-// first workgroup of every pair for the combine kernel. Expects L.cnt zeroed.
+// Workgroups per pair and this workgroup's share. Pair p has n_p list
+// entries (sparse: counted by the pair kernel; dense: ceil(T_b / 16)); with
+// per = ceil(total / nwg) it gets S_p = max(1, round(n_p / per)) workgroups
+// (0 when n_p = 0), each an equal slice of its list. Workgroup 0 publishes
+// the first workgroup of every pair for the combine kernel. Returns false
+// when this workgroup has no work (uniform over the workgroup).
 template <bool DENSE>
-__device__ bool assign_work(const AttnArgs& a, const LdsLayout& L, int* scan_tmp, Assign* as) {
+__device__ bool assign_work(const AttnArgs& a, int* tmp_n, int* tmp_s, int* sh, Assign* as) {
   const int P = a.B * a.Hkv;
-  const int t = threadIdx.x;
-  int mine_blocks = 0;
-  if (DENSE) {
-    for (int p = t; p < P; p += kThreads) {
-      const int n = blocks_of(0, cached_len(a, L.st, p / a.Hkv));
-      L.cnt[p] = n;
-      mine_blocks += n;
-    }
-  } else {
-    // one item per (pair, span); spans of a pair on a power-of-two stride.
-    // A rolled loop: this runs once per launch from a cold instruction
-    // cache, where compact code is faster than unrolled code.
-    const int sh = 32 - __clz(a.k);  // 2^sh > k, so spans 0..k fit
-    const int items = P << sh;
-#pragma unroll 1
-    for (int it = t; it < items; it += kThreads) {
-      const int p = it >> sh, i = it & ((1 << sh) - 1);
-      if (i > a.k) continue;
-      const int b = p / a.Hkv, g = p - b * a.Hkv;
-      const int T = cached_len(a, L.st, b);
-      const int tw = T - a.window > 0 ? T - a.window : 0;
-      int s0, e0;
-      pair_span(a, L.st, b, g, i, T, tw, &s0, &e0);
-      const int n = blocks_of(s0, e0);
-      if (n > 0) atomicAdd(&L.cnt[p], n);
-      mine_blocks += n;
-    }
-  }
-  // total blocks: wave sums, one atomic per wave
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, w = blockIdx.x;
+  const int per_t = (P + kThreads - 1) / kThreads;  // <= kPairsPerThread
+  const int p0 = t * per_t;
+  int nreg[kPairsPerThread];
+  int mine = 0;
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) mine_blocks += __shfl_xor(mine_blocks, o);
-  if ((t & 63) == 0) atomicAdd(&L.cnt[P], mine_blocks);
+  for (int j = 0; j < kPairsPerThread; ++j) {
+    const int p = p0 + j;
+    int n = 0;
+    if (j < per_t && p < P) {
+      if (DENSE) {
+        n = (cached_len(a, p / a.Hkv) + kBlock - 1) / kBlock;
+      } else {
+        n = a.counts[p];
+        n = n < 0 ? 0 : (n > a.max_blocks ? a.max_blocks : n);
+      }
+    }
+    nreg[j] = n;
+    mine += n;
+  }
+  // total list length
+  const int wsum = wave_sum(mine);
+  if (lane == 0) tmp_n[wave] = wsum;
   __syncthreads();
-  const int total = L.cnt[P];
+  int total = 0;
+#pragma unroll
+  for (int v = 0; v < kWaves; ++v) total += tmp_n[v];
   const int per = total > 0 ? (total + a.nwg - 1) / a.nwg : 1;
-  // workgroups per pair and their prefix (thread t owns a contiguous run)
-  const int per_t = (P + kThreads - 1) / kThreads;
-  const int p0 = t * per_t, p1 = p0 + per_t < P ? p0 + per_t : P;
+  // workgroups per pair, prefix over pairs (thread t owns a contiguous run)
   int ms = 0;
-  for (int p = p0; p < p1; ++p) {
-    const int n = L.cnt[p];
-    ms += n > 0 ? max(1, (n + per / 2) / per) : 0;
-  }
-  int total_s;
-  int run = wg_exclusive_scan(ms, scan_tmp, &total_s);
-  for (int p = p0; p < p1; ++p) {
-    const int n = L.cnt[p];
-    L.prefS[p] = run;
-    run += n > 0 ? max(1, (n + per / 2) / per) : 0;
-  }
-  if (t == 0) L.prefS[P] = total_s;
+#pragma unroll
+  for (int j = 0; j < kPairsPerThread; ++j)
+    ms += nreg[j] > 0 ? max(1, (nreg[j] + per / 2) / per) : 0;
+  const int incl = wave_incl_sum(ms);
+  if (lane == 63) tmp_s[wave] = incl;
   __syncthreads();
-  if (blockIdx.x == 0)
-    for (int p = t; p <= P; p += kThreads) a.ws_pref[p] = L.prefS[p];
-  const int w = blockIdx.x;
-  if (w >= total_s) return false;
-  int lo = 0, hi = P - 1;  // last pair with prefS[p] <= w
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (L.prefS[mid] <= w) lo = mid;
-    else hi = mid - 1;
+  int run = incl - ms, total_s = 0;
+#pragma unroll
+  for (int v = 0; v < kWaves; ++v) {
+    run += v < wave ? tmp_s[v] : 0;
+    total_s += tmp_s[v];
   }
-  const int p = lo;
-  const int S = L.prefS[p + 1] - L.prefS[p];
-  const int r = w - L.prefS[p];
-  const int64_t n = L.cnt[p];
+#pragma unroll
+  for (int j = 0; j < kPairsPerThread; ++j) {
+    const int p = p0 + j;
+    if (j < per_t && p < P) {
+      const int n = nreg[j];
+      const int S = n > 0 ? max(1, (n + per / 2) / per) : 0;
+      if (w >= run && w < run + S) {
+        sh[0] = p;
+        sh[1] = w - run;
+        sh[2] = S;
+        sh[3] = n;
+      }
+      if (w == 0) a.ws_pref[p] = run;
+      run += S;
+    }
+  }
+  if (w == 0 && t == 0) a.ws_pref[P] = total_s;
+  if (w >= total_s) return false;  // uniform: total_s is the same in every thread
+  __syncthreads();
+  const int p = sh[0], r = sh[1], S = sh[2];
+  const int64_t n = sh[3];
   as->p = p;
+  as->T = DENSE ? cached_len(a, p / a.Hkv) : 0;
   as->lo = static_cast<int>(r * n / S);
   as->hi = static_cast<int>((r + 1) * n / S);
   return true;
 }
 
-// Copy the block-table row of sequence b (its first ceil(T/16) entries) to LDS.
-__device__ __forceinline__ void fetch_row(const AttnArgs& a, const LdsLayout& L, int b, int T) {
-  const int n = (T + kBlock - 1) / kBlock;
-  const int32_t* src = a.block_table + static_cast<size_t>(b) * a.max_blocks;
-  for (int i = threadIdx.x; i < n; i += kThreads) L.row[i] = src[i];
-}
-
-// Span list of the pair in LDS, built by wave 0 (lanes over spans); the
-// caller synchronizes afterwards. Returns the number of spans through *nspans.
+// Entry j of the pair's list -> physical block and slot mask ((0, 0) when j
+// is -1 or the block id is out of range).
 template <bool DENSE>
-__device__ void build_pair_plan(const AttnArgs& a, const LdsLayout& L, int b, int g, int T,
-                                int tw, int* nspans) {
-  const int lane = threadIdx.x & 63;
-  if (threadIdx.x >= 64) return;
-  if (DENSE) {
-    if (lane == 0) {
-      L.plan_s[0] = 0;
-      L.plan_e[0] = T;
-      L.plan_pref[0] = 0;
-      L.plan_pref[1] = blocks_of(0, T);
-      *nspans = 1;
-    }
-    return;
-  }
-  const int n = a.k + 1;
-  int run = 0;
-  for (int base = 0; base < n; base += 64) {
-    const int i = base + lane;
-    int s = 0, e = 0;
-    if (i < n) pair_span(a, L.st, b, g, i, T, tw, &s, &e);
-    const int nb = blocks_of(s, e);
-    int incl = nb;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int v = __shfl_up(incl, o);
-      if (lane >= o) incl += v;
-    }
-    if (i < n) {
-      L.plan_s[i] = s;
-      L.plan_e[i] = e;
-      L.plan_pref[i] = run + incl - nb;
-    }
-    run += __shfl(incl, 63);
-  }
-  if (lane == 0) {
-    L.plan_pref[n] = run;
-    *nspans = n;
-  }
-}
-
-// Entry j of the pair's list -> physical block and slot mask (mask 0 when j
-// is past the list or its block id is out of range).
-__device__ __forceinline__ void resolve_entry(const AttnArgs& a, const LdsLayout& L, int nspans,
-                                              int total, int b, int j, int* pb, uint32_t* mask) {
+__device__ __forceinline__ void resolve_entry(const AttnArgs& a, const Assign& as, int b, int j,
+                                              int* pb, uint32_t* mask) {
   *pb = 0;
   *mask = 0;
-  if (j < 0 || j >= total) return;
-  int lo = 0, hi = nspans - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (L.plan_pref[mid] <= j) lo = mid;
-    else hi = mid - 1;
+  if (j < 0) return;
+  int blk;
+  uint32_t m;
+  if (DENSE) {
+    blk = a.block_table[static_cast<size_t>(b) * a.max_blocks + j];
+    const int rest = as.T - j * kBlock;
+    m = rest >= kBlock ? 0xffffu : ((1u << rest) - 1u);
+  } else {
+    const int2 e = a.entries[static_cast<size_t>(as.p) * a.max_blocks + j];
+    blk = e.x;
+    m = static_cast<uint32_t>(e.y) & 0xffffu;
   }
-  const int s = L.plan_s[lo], e = L.plan_e[lo];
-  const int lb = (s >> 4) + (j - L.plan_pref[lo]);
-  if (lb < 0 || lb >= a.max_blocks) return;
-  const int b0 = lb << 4;
-  const int from = (s > b0 ? s : b0) - b0;
-  const int to = (e < b0 + 16 ? e : b0 + 16) - b0;
-  const int blk = a.row_lds ? L.row[lb] : a.block_table[static_cast<size_t>(b) * a.max_blocks + lb];
-  if (blk < 0 || blk >= a.num_blocks || to <= from) return;
+  if (blk < 0 || blk >= a.num_blocks) return;
   *pb = blk;
-  *mask = ((1u << to) - 1u) & ~((1u << from) - 1u);
+  *mask = m;
 }
 
 // Entry of this wave for lane-indexed position e (chunks of NBW round-robin
@@ -543,32 +362,22 @@ __device__ __forceinline__ void compute_chunk(const AttnArgs& a, Chunk<D, NBW>& 
   }
 }
 
-template <int G, int D, int NBW, bool DENSE, bool STAGED>
+template <int G, int D, int NBW, bool DENSE>
 __global__ void __launch_bounds__(kThreads, 2)
 attn_mfma_kernel(AttnArgs a) {
   constexpr int KS = D / 32, NT = D / 16;
   constexpr int EPB = 64;  // entries resolved per batch (one per lane)
-  extern __shared__ int32_t dyn[];
   __shared__ float red_m[kWaves][G];
   __shared__ float red_l[kWaves][G];
   __shared__ float red_o[kWaves][G][D];
-  __shared__ int scan_tmp[kWaves];
-  __shared__ int sh_nspans;
+  __shared__ int tmp_n[kWaves], tmp_s[kWaves];
+  __shared__ int sh_as[4];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
-  const LdsLayout L = stage_inputs<DENSE, STAGED>(a, dyn);
-  __syncthreads();
   Assign as;
-  if (!assign_work<DENSE>(a, L, scan_tmp, &as)) return;
+  if (!assign_work<DENSE>(a, tmp_n, tmp_s, sh_as, &as)) return;
   const int b = as.p / a.Hkv, g = as.p % a.Hkv;
-  const int T = cached_len(a, L.st, b);
-  const int tw = T - a.window > 0 ? T - a.window : 0;
-  if (a.row_lds) fetch_row(a, L, b, T);
-  build_pair_plan<DENSE>(a, L, b, g, T, tw, &sh_nspans);
-  __syncthreads();
-  const int nspans = sh_nspans;
-  const int n_list = L.plan_pref[nspans];
 
   // Q^T as the B operand: lane holds head l16, dims 32 kk + 8 lg .. +7
   bf16x8 qop[KS];
@@ -592,8 +401,7 @@ attn_mfma_kernel(AttnArgs a) {
     // one lane per entry: resolve this batch's block-table entries at once
     int pb_l;
     uint32_t msk_l;
-    resolve_entry(a, L, nspans, n_list, b, wave_entry<NBW>(as, wave, c0 * NBW + lane), &pb_l,
-                  &msk_l);
+    resolve_entry<DENSE>(a, as, b, wave_entry<NBW>(as, wave, c0 * NBW + lane), &pb_l, &msk_l);
     const int nck = nck_all - c0 < CPB ? nck_all - c0 : CPB;
     Chunk<D, NBW> cA, cB;
     load_chunk<D, NBW>(a, g, 0, pb_l, msk_l, cA);
@@ -637,7 +445,7 @@ __device__ __forceinline__ float row_sum(float v) {
   return v;
 }
 
-template <typename E, int G, int D, bool DENSE, bool STAGED>
+template <typename E, int G, int D, bool DENSE>
 __global__ void __launch_bounds__(kThreads)
 attn_valu_kernel(AttnArgs a) {
   using St = typename E::storage;
@@ -649,27 +457,17 @@ attn_valu_kernel(AttnArgs a) {
   constexpr int DPL = D / 64;          // value dimensions per lane
   constexpr int VCH = kBlock / VPL;    // 16-byte chunks per value column
   constexpr int CPB = 64 / NBW;
-  extern __shared__ int32_t dyn[];
   __shared__ float red_m[kWaves][G];
   __shared__ float red_l[kWaves][G];
   __shared__ float red_o[kWaves][G][D];
   __shared__ float p_lds[kWaves][NBW * kBlock][G];
-  __shared__ int scan_tmp[kWaves];
-  __shared__ int sh_nspans;
+  __shared__ int tmp_n[kWaves], tmp_s[kWaves];
+  __shared__ int sh_as[4];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const LdsLayout L = stage_inputs<DENSE, STAGED>(a, dyn);
-  __syncthreads();
   Assign as;
-  if (!assign_work<DENSE>(a, L, scan_tmp, &as)) return;
+  if (!assign_work<DENSE>(a, tmp_n, tmp_s, sh_as, &as)) return;
   const int b = as.p / a.Hkv, g = as.p % a.Hkv;
-  const int T = cached_len(a, L.st, b);
-  const int tw = T - a.window > 0 ? T - a.window : 0;
-  if (a.row_lds) fetch_row(a, L, b, T);
-  build_pair_plan<DENSE>(a, L, b, g, T, tw, &sh_nspans);
-  __syncthreads();
-  const int nspans = sh_nspans;
-  const int n_list = L.plan_pref[nspans];
 
   const St* kpool = static_cast<const St*>(a.k_pool);
   const St* vpool = static_cast<const St*>(a.v_pool);
@@ -697,8 +495,7 @@ attn_valu_kernel(AttnArgs a) {
   for (int c0 = 0; c0 < nck_all; c0 += CPB) {
     int pb_l;
     uint32_t msk_l;
-    resolve_entry(a, L, nspans, n_list, b, wave_entry<NBW>(as, wave, c0 * NBW + lane), &pb_l,
-                  &msk_l);
+    resolve_entry<DENSE>(a, as, b, wave_entry<NBW>(as, wave, c0 * NBW + lane), &pb_l, &msk_l);
     const int nck = nck_all - c0 < CPB ? nck_all - c0 : CPB;
     for (int c = 0; c < nck; ++c) {
       int pb[NBW];
@@ -886,38 +683,35 @@ size_t attn_workspace(const zr_geom& gm, int nwg, void* ws, AttnArgs* a) {
   const size_t slots = static_cast<size_t>(nwg) + P;
   auto up16 = [](size_t x) { return (x + 15) & ~static_cast<size_t>(15); };
   const size_t pref_b = up16((P + 1) * sizeof(int32_t));
+  const size_t cnt_b = up16(P * sizeof(int32_t));
+  const size_t ent_b = P * static_cast<size_t>(gm.max_blocks_per_seq) * sizeof(int2);
   const size_t ml_b = up16(slots * G * sizeof(float));
   const size_t acc_b = slots * G * gm.head_dim * sizeof(float);
   if (ws && a) {
     char* c = static_cast<char*>(ws);
     a->ws_pref = reinterpret_cast<int32_t*>(c);
-    a->ws_m = reinterpret_cast<float*>(c + pref_b);
-    a->ws_l = reinterpret_cast<float*>(c + pref_b + ml_b);
-    a->ws_acc = reinterpret_cast<float*>(c + pref_b + 2 * ml_b);
+    c += pref_b;
+    a->counts = reinterpret_cast<int32_t*>(c);
+    c += cnt_b;
+    a->entries = reinterpret_cast<int2*>(c);
+    c += ent_b;
+    a->ws_m = reinterpret_cast<float*>(c);
+    c += ml_b;
+    a->ws_l = reinterpret_cast<float*>(c);
+    c += ml_b;
+    a->ws_acc = reinterpret_cast<float*>(c);
     a->nwg = nwg;
   }
-  return pref_b + 2 * ml_b + acc_b;
-}
-
-static size_t dyn_lds_bytes(const zr_geom& gm, const AttnArgs& a, bool dense) {
-  return lds_ints(gm.batch, gm.n_kv_heads, a.k, a.n_total, dense, a.stage_sel != 0,
-                  a.row_lds ? gm.max_blocks_per_seq : 0) *
-         sizeof(int32_t);
+  return pref_b + cnt_b + ent_b + 2 * ml_b + acc_b;
 }
 
 template <int G, int D>
 static hipError_t launch_mfma(const zr_geom& gm, const AttnArgs& a, bool dense, hipStream_t s) {
-  const size_t lds = dyn_lds_bytes(gm, a, dense);
   const dim3 grid(a.nwg + gm.batch * gm.n_kv_heads);
   if (dense)
-    hipLaunchKernelGGL((attn_mfma_kernel<G, D, kMfmaNBW, true, false>), grid, dim3(kThreads), lds,
-                       s, a);
-  else if (a.stage_sel)
-    hipLaunchKernelGGL((attn_mfma_kernel<G, D, kMfmaNBW, false, true>), grid, dim3(kThreads), lds,
-                       s, a);
+    hipLaunchKernelGGL((attn_mfma_kernel<G, D, kMfmaNBW, true>), grid, dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((attn_mfma_kernel<G, D, kMfmaNBW, false, false>), grid, dim3(kThreads),
-                       lds, s, a);
+    hipLaunchKernelGGL((attn_mfma_kernel<G, D, kMfmaNBW, false>), grid, dim3(kThreads), 0, s, a);
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL((attn_combine_kernel<G, D>), dim3(gm.n_kv_heads, gm.batch), dim3(kThreads),
@@ -927,14 +721,11 @@ static hipError_t launch_mfma(const zr_geom& gm, const AttnArgs& a, bool dense, 
 
 template <typename E, int G, int D>
 static hipError_t launch_valu(const zr_geom& gm, const AttnArgs& a, bool dense, hipStream_t s) {
-  const size_t lds = dyn_lds_bytes(gm, a, dense);
   const dim3 grid(a.nwg + gm.batch * gm.n_kv_heads);
   if (dense)
-    hipLaunchKernelGGL((attn_valu_kernel<E, G, D, true, false>), grid, dim3(kThreads), lds, s, a);
-  else if (a.stage_sel)
-    hipLaunchKernelGGL((attn_valu_kernel<E, G, D, false, true>), grid, dim3(kThreads), lds, s, a);
+    hipLaunchKernelGGL((attn_valu_kernel<E, G, D, true>), grid, dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((attn_valu_kernel<E, G, D, false, false>), grid, dim3(kThreads), lds, s, a);
+    hipLaunchKernelGGL((attn_valu_kernel<E, G, D, false>), grid, dim3(kThreads), 0, s, a);
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL((attn_combine_kernel<G, D>), dim3(gm.n_kv_heads, gm.batch), dim3(kThreads),
@@ -964,35 +755,8 @@ static hipError_t launch_d(const zr_geom& gm, const AttnArgs& a, bool dense, hip
   }
 }
 
-// LDS of one workgroup: the static arrays (bounded for every G, D) plus the
-// dynamic plan region; kept within 64 KiB.
-constexpr size_t kLdsLimit = 64 * 1024;
-
-static size_t static_lds_bound(const zr_geom& gm) {
-  const size_t G = static_cast<size_t>(gm.n_q_heads / gm.n_kv_heads);
-  return (kWaves * G * gm.head_dim + 2 * kWaves * G + kWaves * 2 * kBlock * G) * sizeof(float) +
-         256;
-}
-
-bool attn_lds_ok(const zr_geom& gm, int k, bool dense) {
-  return static_lds_bound(gm) +
-             lds_ints(gm.batch, gm.n_kv_heads, k, 0, dense, false, 0) * sizeof(int32_t) <=
-         kLdsLimit;
-}
-
-hipError_t launch_attention(const zr_geom& gm, const AttnArgs& a0, bool dense, hipStream_t s) {
+hipError_t launch_attention(const zr_geom& gm, const AttnArgs& a, bool dense, hipStream_t s) {
   if (gm.batch == 0) return hipSuccess;
-  AttnArgs a = a0;
-  const int64_t P = static_cast<int64_t>(gm.batch) * gm.n_kv_heads;
-  // stage the selections and thought spans in LDS when they fit
-  a.stage_sel = !dense && P * a.k + 2 * static_cast<int64_t>(a.n_total) <= kStageCap;
-  if (a.stage_sel && static_lds_bound(gm) + dyn_lds_bytes(gm, a, dense) > kLdsLimit)
-    a.stage_sel = 0;
-  a.stage_th = a.stage_sel;
-  // the block-table row of the workgroup's sequence in LDS when it fits
-  a.row_lds = gm.max_blocks_per_seq <= 4096;
-  if (a.row_lds && static_lds_bound(gm) + dyn_lds_bytes(gm, a, dense) > kLdsLimit) a.row_lds = 0;
-  if (static_lds_bound(gm) + dyn_lds_bytes(gm, a, dense) > kLdsLimit) return hipErrorInvalidValue;
   return gm.head_dim == 128 ? launch_d<128>(gm, a, dense, s) : launch_d<64>(gm, a, dense, s);
 }
 

@@ -43,6 +43,64 @@ __device__ __forceinline__ void unpack16<BF16>(const uint4& u, float* out) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Cross-lane helpers built on DPP (data-parallel primitives inside the VALU,
+// no LDS round trip). DPP controls: quad_perm 0x00-0xff, row_shr:n 0x110+n,
+// row_mirror 0x140, row_half_mirror 0x141, row_bcast:15 0x142,
+// row_bcast:31 0x143 (a row is 16 lanes).
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ int dpp_move(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, false);
+}
+
+// Inclusive prefix sum of v over the 64 lanes of the wave. Every lane must
+// be active.
+__device__ __forceinline__ int wave_incl_sum(int v) {
+  const int lane = threadIdx.x & 63, r = lane & 15;
+  int t;
+  t = dpp_move<0x111>(v);
+  v += r >= 1 ? t : 0;
+  t = dpp_move<0x112>(v);
+  v += r >= 2 ? t : 0;
+  t = dpp_move<0x114>(v);
+  v += r >= 4 ? t : 0;
+  t = dpp_move<0x118>(v);
+  v += r >= 8 ? t : 0;
+  t = dpp_move<0x142>(v);  // lane 15 of the previous row into rows 1 and 3
+  v += (lane & 16) ? t : 0;
+  t = dpp_move<0x143>(v);  // lane 31 into rows 2 and 3
+  v += (lane & 32) ? t : 0;
+  return v;
+}
+
+// Sum of v over the wave, in every lane.
+__device__ __forceinline__ int wave_sum(int v) {
+  return __builtin_amdgcn_readlane(wave_incl_sum(v), 63);
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_move_f64(double x) {
+  const int2 w = __builtin_bit_cast(int2, x);
+  int2 r;
+  r.x = __builtin_amdgcn_update_dpp(0, w.x, CTRL, 0xf, 0xf, false);
+  r.y = __builtin_amdgcn_update_dpp(0, w.y, CTRL, 0xf, 0xf, false);
+  return __builtin_bit_cast(double, r);
+}
+
+// Sum of x over aligned groups of N lanes (N = 4, 8, 16 or 32), in every lane
+// of the group: pairs in a quad, then quads mirrored inside a half row, then
+// half rows mirrored inside a row, then rows 16 apart.
+template <int N>
+__device__ __forceinline__ double group_sum_f64(double x) {
+  x += dpp_move_f64<0xb1>(x);  // quad_perm [1,0,3,2]
+  x += dpp_move_f64<0x4e>(x);  // quad_perm [2,3,0,1]
+  if (N >= 8) x += dpp_move_f64<0x141>(x);
+  if (N >= 16) x += dpp_move_f64<0x140>(x);
+  if (N >= 32) x += __shfl_xor(x, 16);
+  return x;
+}
+
 template <typename E>
 __device__ __forceinline__ float load_elem(const typename E::storage* p, size_t i);
 
@@ -56,46 +114,61 @@ __device__ __forceinline__ float load_elem<BF16>(const uint16_t* p, size_t i) {
   return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
 }
 
+// Pre-attention work of one (sequence, KV head) pair (zr_pair.hip): scores,
+// top-k and the attended-block list, by mode.
+enum PairMode { kModeScore = 0, kModeSelect = 1, kModePlan = 2, kModeStep = 3 };
+
+struct PairArgs {
+  const void* q;              // [B][Hq][D]                      (score)
+  const void* kbar;           // [n_total][Hkv][D]               (score)
+  const int32_t* seq_ptr;     // [B + 1] thoughts CSR
+  const int32_t* th_start;    // [n_total]                       (plan)
+  const int32_t* th_len;      // [n_total]                       (plan)
+  float* scores;              // [n_total][Hkv] written (score) or read (select)
+  int32_t* sel;               // [B][Hkv][k] written (select) or read (plan)
+  const int32_t* seq_lens;    // [B]                             (plan)
+  const int32_t* block_table; // [B][max_blocks]                 (plan)
+  int32_t* counts;            // [B * Hkv] list length per pair  (plan)
+  int2* entries;              // [B * Hkv][max_blocks] (physical block, slot mask) (plan)
+  int32_t n_total, max_per_seq, Hq, Hkv, k, window, max_blocks, num_blocks;
+  int32_t bt_per;             // block-table entries per thread: ceil(max_blocks / 256)
+  int32_t stage_th;           // 1: thought spans staged in LDS
+};
+
 // Attention launch parameters (device pointers + sizes), passed by value.
-// Partial results are indexed by workgroup; workgroups [ws_pref[p],
-// ws_pref[p + 1]) hold the partials of pair p = b * Hkv + g (see zr_attn.hip).
+// Pair p = b * Hkv + g has counts[p] entries entries[p][0..) (sparse; the
+// dense kernel reads the block table directly). Partial results are indexed
+// by workgroup; workgroups [ws_pref[p], ws_pref[p + 1]) hold pair p's.
 struct AttnArgs {
   const void* q;
   const void* k_pool;
   const void* v_pool;
   const int32_t* block_table;
   const int32_t* seq_lens;
-  const int32_t* seq_ptr;    // thoughts CSR (sparse only)
-  const int32_t* th_start;
-  const int32_t* th_len;
-  const int32_t* sel;        // [B][Hkv][k] (sparse only, may be null when k == 0)
+  const int32_t* counts;     // [P] (sparse)
+  const int2* entries;       // [P][max_blocks] (sparse)
   int32_t* ws_pref;          // [P + 1]: first workgroup of each pair
   float* ws_m;               // [nwg + P][G]
   float* ws_l;               // [nwg + P][G]
   float* ws_acc;             // [nwg + P][G][D]
   float* out;                // [B][Hq][D]
-  int32_t B, Hq, Hkv, max_blocks, num_blocks, n_total;
-  int32_t k, window;
+  int32_t B, Hq, Hkv, max_blocks, num_blocks;
   int32_t nwg;               // target workgroups; the grid has nwg + P
-  int32_t stage_sel;         // 1: stage sel in LDS (else read it from global memory)
-  int32_t stage_th;          // 1: stage the thought spans in LDS
-  int32_t row_lds;           // 1: copy the workgroup's block-table row to LDS
   float scale_log2;          // scale * log2(e)
 };
 
 // Host-side launchers (defined next to their kernels).
-hipError_t launch_coarse_score(const zr_geom& g, const void* q, const zr_thoughts& th,
-                               float* scores, hipStream_t s);
-hipError_t launch_select_topk(const zr_geom& g, const zr_thoughts& th, const float* scores,
-                              int k, int32_t* sel, hipStream_t s);
+hipError_t launch_pair(const zr_geom& g, const PairArgs& a, int mode, hipStream_t s);
+// Whether the pair kernel's LDS fits (with nothing optional staged).
+bool pair_lds_ok(const zr_geom& g, int max_per_seq, int k, bool select, bool plan);
 // Workgroups of the attention kernel for a bound of `max_attended` tokens per
 // (sequence, KV head); the workspace layout depends on it.
 int attn_workgroups(const zr_geom& g, int32_t max_attended);
 // Bytes of workspace for `nwg` workgroups; fills the AttnArgs pointers when
-// `ws` is not null.
+// `ws` is not null. Layout (each region 16-byte aligned): ws_pref [P + 1],
+// counts [P], entries [P][max_blocks] (int2), m and l [nwg + P][G],
+// acc [nwg + P][G][D].
 size_t attn_workspace(const zr_geom& g, int nwg, void* ws, AttnArgs* a);
-// Whether the attention kernel's LDS fits for this shape (with nothing staged).
-bool attn_lds_ok(const zr_geom& g, int k, bool dense);
 hipError_t launch_attention(const zr_geom& g, const AttnArgs& a, bool dense, hipStream_t s);
 
 }  // namespace zr

@@ -1,0 +1,582 @@
+// Per-(sequence, KV head) work before attention: coarse scores, top-k
+// selection and the attended-block list, in one workgroup per pair.
+//
+// Scoring follows ZoomR Sec. 3.3 (eq. alpha): the inner product of the decode
+// query with each thought's mean summary key. With grouped-query attention
+// one score is kept per KV head: the query heads of the group are summed
+// first (their sum dotted with the key equals the sum of the per-head
+// scores). Products and sums run in float64 so the float32 result does not
+// depend on the summation order for bf16 inputs (products and partial sums
+// are exact there for inputs of ordinary range); the float32 scores are what
+// the selector compares.
+//
+// Selection follows ZoomR Sec. 3.3 (eq. I_top-k) under the total order
+// (score descending, thought index ascending) on order-preserving 32-bit
+// keys: up to 256 thoughts each thread ranks its own thought by counting the
+// thoughts ahead of it; beyond that a radix select finds the k-th key and
+// the ties at it are taken lowest index first. Winners are emitted in
+// ascending thought index.
+//
+// The attended set is the union of the window [T - W, T) and the selected
+// thoughts' spans clipped below T - W (ZoomR Sec. 3.3 eq. I_f restricted to
+// the window and full-resolution spans). It is built as a bitmap of slot
+// masks, one 16-bit mask per logical block of the paged cache, so tokens
+// shared by several spans count once whatever the order of `sel`. The
+// non-empty blocks, resolved through the block table (KV-cache management
+// page, paged KV cache, eq. 4), form the pair's list of (physical block,
+// slot mask) entries for the attention kernel.
+//
+// The four modes (template flags) share this code:
+//   SCORE            scores only                       (zr_coarse_score)
+//   SELECT           top-k from given scores           (zr_select_topk)
+//   PLAN             block list from a given sel       (zr_sparse_decode_attn)
+//   SCORE+SELECT+PLAN the whole pre-attention step      (zr_sparse_decode_step)
+#include "zr_internal.h"
+
+namespace zr {
+
+constexpr int kPairThreads = 256;
+constexpr int kPairWaves = kPairThreads / 64;
+constexpr int kRankMax = kPairThreads;  // up to this many thoughts: ranking by counting
+constexpr int kBtRegs = 16;             // block-table entries prefetched per thread
+constexpr int kSelRegs = (ZR_MAX_K + kPairThreads - 1) / kPairThreads;  // given sel per thread
+constexpr int kMaxGroup = 16;           // query heads per KV head
+
+// Larger key = better score. NaN maps below every number; -0 maps like +0.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0u;  // NaN
+  if (u == 0x80000000u) u = 0u;                     // -0 -> +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Exclusive prefix sum of one value per thread across the workgroup; *total
+// gets the sum. `tmp` holds kPairWaves ints. Contains barriers: every thread
+// must call it.
+__device__ int pair_exclusive_scan(int v, int* tmp, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int incl = wave_incl_sum(v);
+  if (lane == 63) tmp[wave] = incl;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kPairWaves; ++w) {
+    const int x = tmp[w];
+    before += w < wave ? x : 0;
+    all += x;
+  }
+  __syncthreads();
+  *total = all;
+  return before + incl - v;
+}
+
+__device__ __forceinline__ int blocks_of_span(int s, int e) {
+  return e > s ? ((e - 1) >> 4) - (s >> 4) + 1 : 0;
+}
+
+// Dynamic LDS (int32 units), each region 4-int aligned:
+//   keys[max_per_seq]                 SELECT (order keys, zero padded)
+//   th_s[max_per_seq] th_l[...]       PLAN with staged thought spans
+//   sel_l[k]                          PLAN
+//   sp_s[k+1] sp_e[k+1] sp_pref[k+2]  PLAN
+//   bmask[ceil(max_blocks / 2)]       PLAN (two 16-bit slot masks per int)
+__host__ __device__ inline int up4(int x) { return (x + 3) & ~3; }
+
+struct PairLds {
+  uint32_t* keys;
+  int32_t* th_s;
+  int32_t* th_l;
+  int32_t* sel_l;
+  int32_t* sp_s;
+  int32_t* sp_e;
+  int32_t* sp_pref;
+  uint32_t* bmask;
+};
+
+__host__ __device__ inline size_t pair_lds_ints(int max_per_seq, int k, int max_blocks,
+                                                bool select, bool plan, bool stage_th) {
+  size_t n = 0;
+  if (select) n += up4(max_per_seq);
+  if (plan) {
+    if (stage_th) n += 2 * static_cast<size_t>(up4(max_per_seq));
+    n += up4(k) + 2 * static_cast<size_t>(up4(k + 1)) + up4(k + 2);
+    n += up4((max_blocks + 1) / 2);
+  }
+  return n;
+}
+
+__device__ inline PairLds pair_lds(int32_t* dyn, int max_per_seq, int k, int max_blocks,
+                                   bool select, bool plan, bool stage_th) {
+  PairLds L{};
+  int32_t* c = dyn;
+  if (select) {
+    L.keys = reinterpret_cast<uint32_t*>(c);
+    c += up4(max_per_seq);
+  }
+  if (plan) {
+    if (stage_th) {
+      L.th_s = c;
+      c += up4(max_per_seq);
+      L.th_l = c;
+      c += up4(max_per_seq);
+    }
+    L.sel_l = c;
+    c += up4(k);
+    L.sp_s = c;
+    c += up4(k + 1);
+    L.sp_e = c;
+    c += up4(k + 1);
+    L.sp_pref = c;
+    c += up4(k + 2);
+    L.bmask = reinterpret_cast<uint32_t*>(c);
+  }
+  return L;
+}
+
+// ---------------------------------------------------------------------------
+// Selection of the k best of n keys (n > k), written in ascending index to
+// L.sel_l (when PLAN) and to `out` (k ints).
+// ---------------------------------------------------------------------------
+
+// n <= kPairThreads: thread t ranks thought t by counting the thoughts
+// ahead of it. The order (larger key, then lower index) is the order of the
+// 64-bit composite key << 32 | ~index, so one unsigned compare per thought.
+template <bool PLAN>
+__device__ void select_by_rank(const PairLds& L, int n, int k, int32_t* out, int* wtmp,
+                               uint64_t* comp) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const uint64_t mine =
+      t < n ? (static_cast<uint64_t>(L.keys[t]) << 32) | static_cast<uint32_t>(~t) : 0ull;
+  comp[t] = mine;  // entries past n are 0: never ahead of a real thought
+  __syncthreads();
+  bool take = false;
+  if (t < n) {
+    int rank = 0;
+    const ulonglong2* c2 = reinterpret_cast<const ulonglong2*>(comp);
+#pragma unroll 4
+    for (int j2 = 0; j2 < (n + 1) / 2; ++j2) {
+      const ulonglong2 v = c2[j2];
+      rank += v.x > mine ? 1 : 0;
+      rank += v.y > mine ? 1 : 0;
+    }
+    take = rank < k;
+  }
+  const uint64_t bal = __ballot(take);
+  if (lane == 0) wtmp[wave] = __popcll(bal);
+  __syncthreads();
+  int before = 0;
+#pragma unroll
+  for (int w = 0; w < kPairWaves; ++w) before += w < wave ? wtmp[w] : 0;
+  if (take) {
+    const int pos = before + __popcll(bal & ((1ull << lane) - 1ull));
+    out[pos] = t;
+    if (PLAN) L.sel_l[pos] = t;
+  }
+}
+
+// General n: radix select (most significant byte first) finds the k-th key
+// and how many keys equal to it still belong to the top k; two scans then
+// compact the winners in index order. Each thread owns a contiguous run of
+// indices so that the scans follow index order.
+template <bool PLAN>
+__device__ void select_by_radix(const PairLds& L, int n, int k, int32_t* out, uint32_t* hist,
+                                int* wtmp, uint32_t* sh) {
+  const int t = threadIdx.x, lane = t & 63;
+  uint32_t prefix = 0, mask = 0, remaining = static_cast<uint32_t>(k);
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    hist[t] = 0;  // kPairThreads == 256 bins
+    __syncthreads();
+    for (int i = t; i < n; i += kPairThreads) {
+      const uint32_t key = L.keys[i];
+      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 0xffu], 1u);
+    }
+    __syncthreads();
+    if (t < 64) {
+      // lane owns digits 4 lane .. 4 lane + 3; find the digit d where the
+      // count of keys with a larger digit is < remaining <= that + hist[d]
+      const uint32_t c0 = hist[4 * lane], c1 = hist[4 * lane + 1], c2 = hist[4 * lane + 2],
+                     c3 = hist[4 * lane + 3];
+      const uint32_t mine = c0 + c1 + c2 + c3;
+      uint32_t suffix = mine;  // keys in digits >= 4 lane
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t x = __shfl_down(suffix, o);
+        if (lane + o < 64) suffix += x;
+      }
+      const unsigned long long hit = __ballot(suffix >= remaining);
+      const int last = 63 - __clzll(hit);  // last lane whose suffix still covers k
+      if (lane == last) {
+        uint32_t above = suffix - mine;
+        const uint32_t c[4] = {c0, c1, c2, c3};
+        int digit = 4 * lane;
+        for (int dd = 3; dd >= 0; --dd) {
+          if (above + c[dd] >= remaining || dd == 0) {
+            digit = 4 * lane + dd;
+            break;
+          }
+          above += c[dd];
+        }
+        sh[0] = prefix | (static_cast<uint32_t>(digit) << shift);
+        sh[1] = remaining - above;
+      }
+    }
+    __syncthreads();
+    prefix = sh[0];
+    remaining = sh[1];
+    mask |= 0xffu << shift;
+  }
+  const uint32_t kth = prefix;
+  const int per = (n + kPairThreads - 1) / kPairThreads;
+  const int i0 = t * per;
+  const int i1 = i0 + per < n ? i0 + per : n;
+  int n_eq = 0;
+  for (int i = i0; i < i1; ++i) n_eq += L.keys[i] == kth;
+  int tot;
+  const int eq_before = pair_exclusive_scan(n_eq, wtmp, &tot);
+  int n_sel = 0;
+  {
+    int r = eq_before;
+    for (int i = i0; i < i1; ++i) {
+      const uint32_t key = L.keys[i];
+      if (key > kth) {
+        ++n_sel;
+      } else if (key == kth) {
+        n_sel += r < static_cast<int>(remaining);
+        ++r;
+      }
+    }
+  }
+  int pos = pair_exclusive_scan(n_sel, wtmp, &tot);
+  {
+    int r = eq_before;
+    for (int i = i0; i < i1; ++i) {
+      const uint32_t key = L.keys[i];
+      bool take = false;
+      if (key > kth) {
+        take = true;
+      } else if (key == kth) {
+        take = r < static_cast<int>(remaining);
+        ++r;
+      }
+      if (take && pos < k) {
+        out[pos] = i;
+        if (PLAN) L.sel_l[pos] = i;
+        ++pos;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The pair kernel: one 256-thread workgroup per pair p = b * Hkv + g.
+// ---------------------------------------------------------------------------
+template <typename E, int D, bool SCORE, bool SELECT, bool PLAN>
+__global__ void __launch_bounds__(kPairThreads)
+pair_kernel(PairArgs a) {
+  constexpr int VPL = 16 / E::kBytes;  // elements per 16-byte load
+  constexpr int LPT = D / VPL;         // lanes per thought row
+  constexpr int TPP = kPairThreads / LPT;
+  constexpr int R = 4;                 // rows in flight per lane
+  extern __shared__ __align__(16) int32_t dyn[];
+  __shared__ int wtmp[kPairWaves];
+  __shared__ uint32_t hist[kPairThreads];
+  __shared__ uint32_t sh[2];
+  __shared__ uint64_t comp[kPairThreads];
+
+  const int p = blockIdx.x, t = threadIdx.x;
+  const int b = p / a.Hkv, g = p - b * a.Hkv;
+  const PairLds L = pair_lds(dyn, a.max_per_seq, a.k, a.max_blocks, SELECT, PLAN, a.stage_th);
+
+  using St = typename E::storage;
+  const int c = t % LPT, r0 = t / LPT;
+  const int G = a.Hq / a.Hkv;
+
+  // --- loads that need nothing but the pair index, all issued up front:
+  // thought range, sequence length, query rows, block-table row, given sel
+  int lo = a.seq_ptr[b], hi = a.seq_ptr[b + 1];
+  int T = 0;
+  if (PLAN) T = a.seq_lens[b];
+  uint4 qv[kMaxGroup];
+  if (SCORE) {
+    const St* qg = static_cast<const St*>(a.q) + (static_cast<size_t>(b) * a.Hq + g * G) * D;
+#pragma unroll
+    for (int h = 0; h < kMaxGroup; ++h)
+      if (h < G) qv[h] = *reinterpret_cast<const uint4*>(qg + h * D + c * VPL);
+  }
+  int btr[kBtRegs];
+  const bool bt_pref = a.bt_per <= kBtRegs;
+  if (PLAN && bt_pref) {
+    const int32_t* row = a.block_table + static_cast<size_t>(b) * a.max_blocks;
+#pragma unroll
+    for (int j = 0; j < kBtRegs; ++j) {
+      const int lb = t * a.bt_per + j;
+      btr[j] = (j < a.bt_per && lb < a.max_blocks) ? row[lb] : 0;
+    }
+  }
+  int selr[kSelRegs];
+  if (PLAN && !SELECT) {
+#pragma unroll
+    for (int j = 0; j < kSelRegs; ++j) {
+      const int i = t + j * kPairThreads;
+      selr[j] = i < a.k ? a.sel[static_cast<size_t>(p) * a.k + i] : -1;
+    }
+  }
+
+  // --- loads that need the thought range: the first thought spans and the
+  // first batch of summary-key rows
+  lo = lo < 0 ? 0 : (lo > a.n_total ? a.n_total : lo);
+  hi = hi < lo ? lo : (hi > a.n_total ? a.n_total : hi);
+  const int n = hi - lo < a.max_per_seq ? hi - lo : a.max_per_seq;
+  int ths0 = 0, thl0 = 0;
+  if (PLAN && a.stage_th && t < n) {
+    ths0 = a.th_start[lo + t];
+    thl0 = a.th_len[lo + t];
+  }
+  const St* kb = static_cast<const St*>(a.kbar);
+  uint4 u[R];
+  auto load_rows = [&](int i0) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      int i = i0 + r0 + r * TPP;
+      i = i < n ? i : n - 1;  // a valid row; the result is dropped
+      u[r] = *reinterpret_cast<const uint4*>(kb + (static_cast<size_t>(lo + i) * a.Hkv + g) * D +
+                                             c * VPL);
+    }
+  };
+  if (SCORE && n > 0) load_rows(0);
+
+  int tw = 0, nb = 0;
+  if (PLAN) {
+    const int cap = a.max_blocks * kBlock;
+    T = T < 0 ? 0 : (T > cap ? cap : T);
+    tw = T - a.window > 0 ? T - a.window : 0;
+    nb = (T + kBlock - 1) / kBlock;
+    for (int i = t; i < (nb + 1) / 2; i += kPairThreads) L.bmask[i] = 0u;
+    if (!SELECT) {
+#pragma unroll
+      for (int j = 0; j < kSelRegs; ++j) {
+        const int i = t + j * kPairThreads;
+        if (i < a.k) L.sel_l[i] = selr[j];
+      }
+    }
+    if (a.stage_th) {
+      if (t < n) {
+        L.th_s[t] = ths0;
+        L.th_l[t] = thl0;
+      }
+      for (int i = t + kPairThreads; i < n; i += kPairThreads) {
+        L.th_s[i] = a.th_start[lo + i];
+        L.th_l[i] = a.th_len[lo + i];
+      }
+    }
+  }
+
+  if (SCORE) {
+    // this lane's VPL dimensions of the group's query sum, in float64
+    double qs[VPL];
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) qs[v] = 0.0;
+#pragma unroll
+    for (int h = 0; h < kMaxGroup; ++h) {
+      if (h < G) {
+        float x[VPL];
+        unpack16<E>(qv[h], x);
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) qs[v] += static_cast<double>(x[v]);
+      }
+    }
+    for (int i0 = 0; i0 < n; i0 += TPP * R) {
+      uint4 cur[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) cur[r] = u[r];
+      if (i0 + TPP * R < n) load_rows(i0 + TPP * R);  // next batch in flight
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        float x[VPL];
+        unpack16<E>(cur[r], x);
+        double acc = 0.0;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) acc = fma(qs[v], static_cast<double>(x[v]), acc);
+        acc = group_sum_f64<LPT>(acc);
+        const int i = i0 + r0 + r * TPP;
+        if (c == 0 && i < n) {
+          const float f = static_cast<float>(acc);
+          a.scores[static_cast<size_t>(lo + i) * a.Hkv + g] = f;
+          if (SELECT) L.keys[i] = order_key(f);
+        }
+      }
+    }
+  } else if (SELECT) {
+    for (int i = t; i < n; i += kPairThreads)
+      L.keys[i] = order_key(a.scores[static_cast<size_t>(lo + i) * a.Hkv + g]);
+  }
+  if (SELECT)
+    for (int i = n + t; i < up4(n); i += kPairThreads) L.keys[i] = 0u;
+  __syncthreads();
+
+  if (SELECT && a.k > 0) {
+    int32_t* out = a.sel + static_cast<size_t>(p) * a.k;
+    if (n <= a.k) {
+      for (int j = t; j < a.k; j += kPairThreads) {
+        const int v = j < n ? j : -1;
+        out[j] = v;
+        if (PLAN) L.sel_l[j] = v;
+      }
+    } else if (n <= kRankMax) {
+      select_by_rank<PLAN>(L, n, a.k, out, wtmp, comp);
+    } else {
+      select_by_radix<PLAN>(L, n, a.k, out, hist, wtmp, sh);
+    }
+    if (PLAN) __syncthreads();
+  }
+
+  if (PLAN) {
+    // spans: 0..k-1 the selected thoughts, k the window; thread t owns a
+    // contiguous run of spans so the block-count scan follows span order
+    const int nsp = a.k + 1;
+    const int per_s = (nsp + kPairThreads - 1) / kPairThreads;
+    const int s0 = t * per_s, s1 = s0 + per_s < nsp ? s0 + per_s : nsp;
+    int cnt = 0;
+    for (int i = s0; i < s1; ++i) {
+      int s = tw, e = T;
+      if (i < a.k) {
+        s = 0;
+        e = 0;
+        const int th = L.sel_l[i];
+        if (th >= 0 && th < n) {
+          const int ts = a.stage_th ? L.th_s[th] : a.th_start[lo + th];
+          const int tl = a.stage_th ? L.th_l[th] : a.th_len[lo + th];
+          s = ts > 0 ? ts : 0;
+          e = tl > 0 ? ts + tl : s;
+          e = e < tw ? e : tw;
+          e = e > s ? e : s;
+        }
+      }
+      L.sp_s[i] = s;
+      L.sp_e[i] = e;
+      cnt += blocks_of_span(s, e);
+    }
+    int total;
+    int run = pair_exclusive_scan(cnt, wtmp, &total);
+    for (int i = s0; i < s1; ++i) {
+      L.sp_pref[i] = run;
+      run += blocks_of_span(L.sp_s[i], L.sp_e[i]);
+    }
+    if (t == 0) L.sp_pref[nsp] = total;
+    __syncthreads();
+    // every (span, block) item ORs its slots into the block's mask
+    for (int f = t; f < total; f += kPairThreads) {
+      int l = 0, h = nsp - 1;  // last span with sp_pref <= f (it holds item f)
+      while (l < h) {
+        const int mid = (l + h + 1) >> 1;
+        if (L.sp_pref[mid] <= f) l = mid;
+        else h = mid - 1;
+      }
+      const int s = L.sp_s[l], e = L.sp_e[l];
+      const int lb = (s >> 4) + (f - L.sp_pref[l]);
+      const int b0 = lb << 4;
+      const int from = (s > b0 ? s : b0) - b0;
+      const int to = (e < b0 + kBlock ? e : b0 + kBlock) - b0;
+      const uint32_t m = ((1u << to) - 1u) & ~((1u << from) - 1u);
+      atomicOr(&L.bmask[lb >> 1], m << (16 * (lb & 1)));
+    }
+    __syncthreads();
+    // non-empty blocks in logical order -> (physical block, slot mask)
+    const int bl0 = t * a.bt_per;
+    int nz = 0;
+    for (int j = 0; j < a.bt_per; ++j) {
+      const int lb = bl0 + j;
+      if (lb < nb) nz += ((L.bmask[lb >> 1] >> (16 * (lb & 1))) & 0xffffu) != 0u;
+    }
+    int n_list;
+    int pos = pair_exclusive_scan(nz, wtmp, &n_list);
+    int2* ent = a.entries + static_cast<size_t>(p) * a.max_blocks;
+    const int32_t* row = a.block_table + static_cast<size_t>(b) * a.max_blocks;
+    if (bt_pref) {
+#pragma unroll
+      for (int j = 0; j < kBtRegs; ++j) {
+        const int lb = bl0 + j;
+        if (j < a.bt_per && lb < nb) {
+          const uint32_t m = (L.bmask[lb >> 1] >> (16 * (lb & 1))) & 0xffffu;
+          if (m) {
+            const int pb = btr[j];
+            const bool ok = pb >= 0 && pb < a.num_blocks;
+            ent[pos++] = ok ? make_int2(pb, static_cast<int>(m)) : make_int2(0, 0);
+          }
+        }
+      }
+    } else {
+      for (int j = 0; j < a.bt_per; ++j) {
+        const int lb = bl0 + j;
+        if (lb < nb) {
+          const uint32_t m = (L.bmask[lb >> 1] >> (16 * (lb & 1))) & 0xffffu;
+          if (m) {
+            const int pb = row[lb];
+            const bool ok = pb >= 0 && pb < a.num_blocks;
+            ent[pos++] = ok ? make_int2(pb, static_cast<int>(m)) : make_int2(0, 0);
+          }
+        }
+      }
+    }
+    if (t == 0) a.counts[p] = n_list;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+constexpr size_t kPairLdsLimit = 64 * 1024;
+constexpr size_t kPairStaticLds = (kPairWaves + kPairThreads + 2) * sizeof(int32_t) + kPairThreads * sizeof(uint64_t);
+
+static size_t pair_dyn_lds(const PairArgs& a, bool select, bool plan) {
+  return pair_lds_ints(a.max_per_seq, a.k, a.max_blocks, select, plan, a.stage_th != 0) *
+         sizeof(int32_t);
+}
+
+bool pair_lds_ok(const zr_geom& gm, int max_per_seq, int k, bool select, bool plan) {
+  return kPairStaticLds + pair_lds_ints(max_per_seq, k, gm.max_blocks_per_seq, select, plan,
+                                        false) * sizeof(int32_t) <=
+         kPairLdsLimit;
+}
+
+template <typename E, int D, bool SCORE, bool SELECT, bool PLAN>
+static hipError_t launch_pair_t(const zr_geom& gm, PairArgs a, hipStream_t s) {
+  a.bt_per = (gm.max_blocks_per_seq + kPairThreads - 1) / kPairThreads;
+  a.stage_th = 0;
+  if (PLAN) {
+    PairArgs b2 = a;
+    b2.stage_th = 1;
+    if (kPairStaticLds + pair_dyn_lds(b2, SELECT, PLAN) <= kPairLdsLimit) a.stage_th = 1;
+  }
+  const size_t lds = pair_dyn_lds(a, SELECT, PLAN);
+  if (kPairStaticLds + lds > kPairLdsLimit) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((pair_kernel<E, D, SCORE, SELECT, PLAN>),
+                     dim3(gm.batch * gm.n_kv_heads), dim3(kPairThreads), lds, s, a);
+  return hipGetLastError();
+}
+
+template <bool SCORE, bool SELECT, bool PLAN>
+static hipError_t launch_pair_mode(const zr_geom& gm, const PairArgs& a, hipStream_t s) {
+  if constexpr (!SCORE) {
+    return launch_pair_t<BF16, 128, SCORE, SELECT, PLAN>(gm, a, s);
+  } else {
+    if (gm.dtype == ZR_BF16)
+      return gm.head_dim == 128 ? launch_pair_t<BF16, 128, SCORE, SELECT, PLAN>(gm, a, s)
+                                : launch_pair_t<BF16, 64, SCORE, SELECT, PLAN>(gm, a, s);
+    return gm.head_dim == 128 ? launch_pair_t<F32, 128, SCORE, SELECT, PLAN>(gm, a, s)
+                              : launch_pair_t<F32, 64, SCORE, SELECT, PLAN>(gm, a, s);
+  }
+}
+
+hipError_t launch_pair(const zr_geom& gm, const PairArgs& a, int mode, hipStream_t s) {
+  if (gm.batch == 0) return hipSuccess;
+  switch (mode) {
+    case kModeScore: return launch_pair_mode<true, false, false>(gm, a, s);
+    case kModeSelect: return launch_pair_mode<false, true, false>(gm, a, s);
+    case kModePlan: return launch_pair_mode<false, false, true>(gm, a, s);
+    case kModeStep: return launch_pair_mode<true, true, true>(gm, a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace zr

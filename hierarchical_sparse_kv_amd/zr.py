@@ -52,6 +52,9 @@ _SIGS = {
     "zr_sparse_decode_attn": (ctypes.c_int, [_G, _P, _P, _P, _P, _P, _T, _P, ctypes.c_int32,
                                              ctypes.c_int32, ctypes.c_float, ctypes.c_int32,
                                              _P, _P, ctypes.c_size_t, _P]),
+    "zr_sparse_decode_step": (ctypes.c_int, [_G, _P, _P, _P, _P, _P, _T, ctypes.c_int32,
+                                             ctypes.c_int32, ctypes.c_float, ctypes.c_int32,
+                                             _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "zr_dense_paged_decode_attn": (ctypes.c_int, [_G, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P,
                                                   ctypes.c_size_t, _P]),
     "zr_workspace_bytes": (ctypes.c_size_t, [_G, ctypes.c_int32]),
@@ -107,6 +110,14 @@ def zr_sparse_decode_attn(geom, q, k_pool, v_pool, block_table, seq_lens, th, se
                                        seq_lens, ctypes.byref(th), sel, int(k), int(window),
                                        float(scale), int(max_attended), out, workspace,
                                        int(ws_bytes), stream)
+
+
+def zr_sparse_decode_step(geom, q, k_pool, v_pool, block_table, seq_lens, th, k, window, scale,
+                          max_attended, scores, sel, out, workspace, ws_bytes, stream=None) -> int:
+    return lib().zr_sparse_decode_step(ctypes.byref(geom), q, k_pool, v_pool, block_table,
+                                       seq_lens, ctypes.byref(th), int(k), int(window),
+                                       float(scale), int(max_attended), scores, sel, out,
+                                       workspace, int(ws_bytes), stream)
 
 
 def zr_dense_paged_decode_attn(geom, q, k_pool, v_pool, block_table, seq_lens, scale, out,
@@ -197,8 +208,19 @@ class DeviceStep:
             _ptr(self.block_table), _ptr(self.seq_lens), self.scale, _ptr(out),
             _ptr(self.workspace), self.workspace.numel(), _stream()))
 
-    def step(self):
-        """One sparse decode step: score, select, attend (+ combine)."""
+    def step(self, scores=None, sel=None, out=None):
+        """One sparse decode step as one call (zr_sparse_decode_step)."""
+        scores = self.scores if scores is None else scores
+        sel = self.sel if sel is None else sel
+        out = self.out if out is None else out
+        check("zr_sparse_decode_step", zr_sparse_decode_step(
+            self.geom, _ptr(self.q), _ptr(self.k_pool), _ptr(self.v_pool),
+            _ptr(self.block_table), _ptr(self.seq_lens), self.th, self.k, self.window,
+            self.scale, self.max_attended, _ptr(scores), _ptr(sel) if self.k else None,
+            _ptr(out), _ptr(self.workspace), self.workspace.numel(), _stream()))
+
+    def step_calls(self):
+        """The same step as three calls: score, select, attend."""
         self.coarse_score()
         self.select_topk()
         self.sparse_attn()
@@ -225,8 +247,9 @@ def step_from_workload(w, k=None):
 def attended_counts(sel, seq_lens, seq_ptr, th_start, th_len, window):
     """Tokens the sparse kernel gathers per (sequence, KV head), from a
     selection read back to the host: the window [T - W, T) plus each selected
-    thought's span clipped below T - W (every token once). Used for byte
-    accounting; int64 [B][Hkv]."""
+    thought's span clipped below T - W (every token once; thoughts do not
+    overlap, repeated indices count once). Used for byte accounting; int64
+    [B][Hkv]."""
     sel = np.asarray(sel)
     B, Hkv = sel.shape[0], sel.shape[1]
     n = np.zeros((B, Hkv), dtype=np.int64)
@@ -237,6 +260,6 @@ def attended_counts(sel, seq_lens, seq_ptr, th_start, th_len, window):
         st = np.asarray(th_start[lo:hi], np.int64)
         en = st + np.asarray(th_len[lo:hi], np.int64)
         for g in range(Hkv):
-            idx = sel[b, g][(sel[b, g] >= 0) & (sel[b, g] < hi - lo)]
+            idx = np.unique(sel[b, g][(sel[b, g] >= 0) & (sel[b, g] < hi - lo)])
             n[b, g] = (T - tw) + int(np.maximum(0, np.minimum(en[idx], tw) - np.maximum(st[idx], 0)).sum())
     return n

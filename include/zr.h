@@ -14,6 +14,8 @@
  *                        Sec. 2 eq. A), read from a paged block pool through a
  *                        per-sequence block table (KV-cache management page,
  *                        "Paged KV cache (PagedAttention)").
+ *   zr_sparse_decode_step runs steps 1-3 as one call (fewer launches and
+ *   dependent memory round trips; same results as the three calls).
  *   zr_dense_paged_decode_attn is the dense baseline: attention over every
  *   cached token through the same block table (same page, eq. 4).
  *
@@ -83,7 +85,7 @@ typedef enum { ZR_F32 = 0, ZR_BF16 = 1 } zr_dtype;
 #define ZR_BLOCK_SIZE 16
 #define ZR_MAX_K 1024                 /* k of zr_select_topk / zr_sparse_decode_attn */
 #define ZR_MAX_THOUGHTS_PER_SEQ 8192  /* zr_thoughts.max_per_seq */
-#define ZR_MAX_PAIRS 4096             /* batch * n_kv_heads of the attention calls */
+#define ZR_MAX_PAIRS 4096             /* batch * n_kv_heads of the attention and step calls */
 
 typedef struct {
   int32_t batch;              /* B >= 0 (B = 0: every call is a no-op) */
@@ -139,17 +141,22 @@ zr_status zr_select_topk(const zr_geom* geom, const zr_thoughts* th, const float
  * each token once (window clipped at 0). Every query head h of group g gets
  *   out[b][h] = softmax(scale * q[b][h] . K_j) weighted sum of V_j
  * over those tokens, with float32 accumulation; an empty token set gives 0.
- * `sel` rows are read as written by zr_select_topk (k columns, -1 = none);
- * k = 0 means window only (sel may be NULL).
- * Split-K: each (b, g) is cut into partitions of the attended token list;
- * `max_attended` is the caller's bound on tokens per (b, g) used to size the
- * grid (a larger count is still handled correctly, just with fewer
- * partitions). `workspace` holds per-partition partial results (no state
- * is kept between calls); it must be at least zr_workspace_bytes(geom,
- * max_attended) bytes and 16-byte aligned, and calls that share a workspace
- * must not run concurrently.
+ * `sel` rows are read as written by zr_select_topk (k columns, -1 = none;
+ * any order, repeats count once); k = 0 means window only (sel may then be
+ * NULL).
+ * Work split: one pair kernel lists each (b, g)'s attended 16-token blocks
+ * with slot masks; the attention kernel gives each (b, g) a number of
+ * workgroups proportional to its block count (the grid is sized from
+ * `max_attended`, the caller's bound on tokens per (b, g); a larger count is
+ * still handled correctly, only with a coarser split); a combine kernel
+ * merges the partial softmax states by log-sum-exp. `workspace` holds the
+ * block lists and partial results (no state is kept between calls); it must
+ * be at least zr_workspace_bytes(geom, max_attended) bytes and 16-byte
+ * aligned, and calls that share a workspace must not run concurrently.
  * Errors: ZR_E_NULL, ZR_E_SHAPE (k, window, max_attended < 0; k > ZR_MAX_K),
- * ZR_E_UNSUPPORTED, ZR_E_WORKSPACE, ZR_E_ALIGN, ZR_E_LAUNCH.
+ * ZR_E_UNSUPPORTED (also: the per-(b, g) lists do not fit the kernel's
+ * on-chip memory, roughly max_blocks_per_seq > 20000), ZR_E_WORKSPACE,
+ * ZR_E_ALIGN, ZR_E_LAUNCH.
  */
 zr_status zr_sparse_decode_attn(const zr_geom* geom, const void* q, const void* k_pool,
                                 const void* v_pool, const int32_t* block_table,
@@ -159,12 +166,29 @@ zr_status zr_sparse_decode_attn(const zr_geom* geom, const void* q, const void* 
                                 size_t ws_bytes, void* stream);
 
 /*
+ * One whole sparse decode step: zr_coarse_score, zr_select_topk and
+ * zr_sparse_decode_attn with the same arguments, fused so that the scores,
+ * the selection and the block lists of each (b, g) come from one kernel.
+ * Writes `scores` ([n_total][n_kv_heads]), `sel` ([batch][n_kv_heads][k];
+ * may be NULL when k = 0) and `out`, bit-identical to the three calls.
+ * Needs summary keys (16-byte aligned) and the workspace of
+ * zr_sparse_decode_attn.
+ * Errors: as the three calls.
+ */
+zr_status zr_sparse_decode_step(const zr_geom* geom, const void* q, const void* k_pool,
+                                const void* v_pool, const int32_t* block_table,
+                                const int32_t* seq_lens, const zr_thoughts* th, int32_t k,
+                                int32_t window, float scale, int32_t max_attended,
+                                float* scores, int32_t* sel, float* out, void* workspace,
+                                size_t ws_bytes, void* stream);
+
+/*
  * Dense paged decode attention (the baseline): softmax attention of every
  * query head over all T_b cached tokens of its sequence, read block by block
  * through the block table (KV-cache management page, eq. 4; ZoomR Sec. 2
- * eq. A). Same split-K scheme as the sparse call with max_attended =
- * 16 * max_blocks_per_seq; workspace >= zr_workspace_bytes(geom,
- * 16 * max_blocks_per_seq).
+ * eq. A). Same split and combine as the sparse call (every block of the
+ * sequence, no pair kernel) with max_attended = 16 * max_blocks_per_seq;
+ * workspace >= zr_workspace_bytes(geom, 16 * max_blocks_per_seq).
  * Errors: as zr_sparse_decode_attn.
  */
 zr_status zr_dense_paged_decode_attn(const zr_geom* geom, const void* q, const void* k_pool,
@@ -173,7 +197,9 @@ zr_status zr_dense_paged_decode_attn(const zr_geom* geom, const void* q, const v
                                      void* workspace, size_t ws_bytes, void* stream);
 
 /* Workspace bytes the attention calls need for a grid sized for
- * `max_attended` tokens per (sequence, KV head). 0 if geom is invalid. */
+ * `max_attended` tokens per (sequence, KV head): per-(b, g) block lists
+ * (8 bytes per block-table column) and per-workgroup partial softmax
+ * states. 0 if geom is invalid or batch * n_kv_heads > ZR_MAX_PAIRS. */
 size_t zr_workspace_bytes(const zr_geom* geom, int32_t max_attended);
 
 /* Static, NUL-terminated description of a status code. */

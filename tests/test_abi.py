@@ -23,8 +23,8 @@ def L():
 def test_exports_every_declared_symbol(L):
     declared = zr.header_symbols()
     assert declared == sorted(["zr_coarse_score", "zr_select_topk", "zr_sparse_decode_attn",
-                               "zr_dense_paged_decode_attn", "zr_workspace_bytes",
-                               "zr_status_string"])
+                               "zr_sparse_decode_step", "zr_dense_paged_decode_attn",
+                               "zr_workspace_bytes", "zr_status_string"])
     out = subprocess.run(["nm", "-D", "--defined-only", zr.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = sorted(l.split()[-1] for l in out.splitlines() if l.split()[-2] == "T")
@@ -56,16 +56,18 @@ def test_workspace_bytes(L):
     g = _geom()
     n = zr.zr_workspace_bytes(g, 1000)
     # 4 (sequence, KV head) pairs of at most ceil(1000/16) + 2 blocks, 8 blocks
-    # per workgroup -> 33 workgroups; partial slots = workgroups + pairs; the
-    # pair prefix (pairs + 2 ints) first, then m, l [slots][G] and
-    # acc [slots][G][128], each region 16-byte aligned
+    # per workgroup -> 33 workgroups; partial slots = workgroups + pairs.
+    # Regions, each 16-byte aligned: first workgroup per pair [pairs + 1],
+    # list length per pair [pairs], block lists [pairs][max_blocks] (8 bytes
+    # each), m and l [slots][G], acc [slots][G][128]
     up16 = lambda x: (x + 15) // 16 * 16
     nwg = -(-4 * (-(-1000 // 16) + 2) // 8)
     slots = nwg + 4
-    assert n == up16(6 * 4) + 2 * up16(slots * 4 * 4) + slots * 4 * 128 * 4
+    lists = up16(5 * 4) + up16(4 * 4) + 4 * 4 * 8
+    assert n == lists + 2 * up16(slots * 4 * 4) + slots * 4 * 128 * 4
     # the grid is capped at 512 workgroups
     big = zr.zr_workspace_bytes(g, 10 ** 6)
-    assert big == up16(6 * 4) + 2 * up16(516 * 16) + 516 * 4 * 128 * 4
+    assert big == lists + 2 * up16(516 * 16) + 516 * 4 * 128 * 4
     assert zr.zr_workspace_bytes(_geom(head_dim=96), 10) == 0
     assert zr.zr_workspace_bytes(g, -1) == 0
     assert zr.zr_workspace_bytes(_geom(batch=1024, n_q_heads=32, n_kv_heads=8), 10) == 0
@@ -88,6 +90,8 @@ def test_geometry_rejected(L, kw, code):
                                     100, FAKE, FAKE, 1 << 20) == code
     assert zr.zr_dense_paged_decode_attn(g, FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, FAKE,
                                          1 << 20) == code
+    assert zr.zr_sparse_decode_step(g, FAKE, FAKE, FAKE, FAKE, FAKE, _th(), 2, 16, 0.1, 100,
+                                    FAKE, FAKE, FAKE, FAKE, 1 << 20) == code
 
 
 def test_null_and_range_errors(L):
@@ -119,3 +123,22 @@ def test_null_and_range_errors(L):
     assert sp(ws_bytes=need - 1) == zr.ZR_E_WORKSPACE
     assert zr.zr_dense_paged_decode_attn(g, FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, FAKE, 64) \
         == zr.ZR_E_WORKSPACE
+
+
+def test_step_errors(L):
+    g = _geom()
+    args = lambda **kw: dict(dict(geom=g, q=FAKE, k_pool=FAKE, v_pool=FAKE, block_table=FAKE,
+                                  seq_lens=FAKE, th=_th(), k=2, window=16, scale=0.1,
+                                  max_attended=100, scores=FAKE, sel=FAKE, out=FAKE,
+                                  workspace=FAKE, ws_bytes=1 << 20), **kw)
+    st = lambda **kw: zr.zr_sparse_decode_step(**args(**kw))
+    assert st(k=-1) == zr.ZR_E_SHAPE
+    assert st(k=2000) == zr.ZR_E_SHAPE
+    assert st(window=-3) == zr.ZR_E_SHAPE
+    assert st(scores=None) == zr.ZR_E_NULL
+    assert st(sel=None) == zr.ZR_E_NULL
+    assert st(th=_th(summary_keys=None)) == zr.ZR_E_NULL
+    assert st(th=_th(summary_keys=FAKE + 2)) == zr.ZR_E_ALIGN
+    assert st(ws_bytes=zr.zr_workspace_bytes(g, 100) - 1) == zr.ZR_E_WORKSPACE
+    # block lists too large for the pair kernel's on-chip memory
+    assert st(geom=_geom(max_blocks_per_seq=60000, batch=1), ws_bytes=1 << 30) == zr.ZR_E_UNSUPPORTED

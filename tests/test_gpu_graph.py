@@ -15,12 +15,14 @@ def _gpu():
     zr.lib()
 
 
-def test_graph_replays_match_eager():
+@pytest.mark.parametrize("fused", [True, False])
+def test_graph_replays_match_eager(fused):
     w = synth.make_workload(1, device="cuda", overrides=dict(B=4, seq_len=("fixed", 4096)))
     other = synth.make_workload(3, device="cuda",
                                 overrides=dict(B=3, seq_len=("uniform", 500, 3000)))
     st, st2 = zr.step_from_workload(w), zr.step_from_workload(other)
-    st.step()
+    run = st.step if fused else st.step_calls
+    run()
     torch.cuda.synchronize()
     ref = (st.scores.clone(), st.sel.clone(), st.out.clone())
     st.dense_attn(out=torch.empty_like(st.out))
@@ -30,7 +32,7 @@ def test_graph_replays_match_eager():
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
         with torch.cuda.graph(g, stream=s):
-            st.step()
+            run()
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     for rep in range(3):

@@ -1,9 +1,10 @@
 """GPU parity of the HIP path (through the C ABI) against the CPU oracle.
 
 Every workload is generated on the GPU from its seed, copied to the host for
-the oracle, and run through zr_coarse_score -> zr_select_topk ->
-zr_sparse_decode_attn (and zr_dense_paged_decode_attn) with the same launch
-configuration the benchmark uses. Bars: scores within one float32 ulp (bit
+the oracle, and run through zr_sparse_decode_step (the benchmark's call, same
+launch configuration) and through zr_coarse_score -> zr_select_topk ->
+zr_sparse_decode_attn, which must agree bit for bit; zr_dense_paged_decode_attn
+where noted. Bars: scores within one float32 ulp (bit
 exact for bf16 inputs, where the float64 sums are exact), selection bit-exact
 apart from logged near-ties, outputs within max-abs 1e-5 (fp32 inputs) or
 2e-3 (bf16 inputs).
@@ -57,6 +58,12 @@ def run_and_check(w, name, k=None, check_dense=False):
         f"n_total={w.n_total} max_attended={st.max_attended}")
     st.step()
     torch.cuda.synchronize()
+    fused = (st.scores.clone(), st.sel.clone(), st.out.clone())
+    st.step_calls()
+    torch.cuda.synchronize()
+    assert torch.equal(fused[0][:w.n_total], st.scores[:w.n_total]), name
+    assert torch.equal(fused[1], st.sel), name
+    assert torch.equal(fused[2], st.out), name
     scores = st.scores.cpu().numpy()[:w.n_total]
     sel = st.sel.cpu().numpy()
     out = st.out.cpu().numpy()
@@ -195,3 +202,54 @@ def test_small_grid_loops_over_chunks():
     st.sparse_attn()
     torch.cuda.synchronize()
     assert torch.max(torch.abs(full - st.out)).item() <= 1e-5
+
+
+def test_unordered_and_repeated_selection():
+    """zr_sparse_decode_attn reads sel as a set: reversed order, repeats and
+    -1 holes give the oracle's union of spans (each token once)."""
+    w = _small(1, k=6)
+    st = zr.step_from_workload(w)
+    st.step()
+    torch.cuda.synchronize()
+    sel = st.sel.cpu().numpy()
+    messy = sel[:, :, ::-1].copy()
+    messy[:, :, 1] = messy[:, :, 0]          # a repeat
+    messy[:, :, 3] = -1                      # a hole
+    st.sparse_attn(sel=torch.as_tensor(messy, device="cuda"))
+    torch.cuda.synchronize()
+    h = P.host(w)
+    ref = P.oracle_step(w, h, sel=messy)
+    err = np.max(np.abs(st.out.cpu().numpy() - ref["out"]))
+    say(f"[gpu] messy-sel: max|out-oracle| = {err:.3e}")
+    assert err <= P.TOL[w.dtype]
+
+
+def test_wide_block_table_and_unstaged_spans():
+    """A block table far wider than the sequences (5000 columns: the pair
+    kernel reads it without register prefetch) and a declared max_per_seq of
+    8192 (the thought spans are then read from global memory, not LDS)."""
+    w = _small(1, k=5)
+    wide = np.full((w.B, 5000), -1, np.int32)
+    wide[:, :w.block_table.shape[1]] = w.block_table
+    st = zr.DeviceStep(w.q, w.k_pool, w.v_pool, wide, w.seq_lens, w.seq_ptr, w.th_start,
+                       w.th_len, w.summary_keys, 8192, w.k, w.window, w.scale,
+                       zr.max_attended_bound(w.seq_lens, w.seq_ptr, w.th_len, w.k, w.window))
+    st.step()
+    torch.cuda.synchronize()
+    fused = (st.sel.clone(), st.out.clone())
+    st.step_calls()
+    torch.cuda.synchronize()
+    assert torch.equal(fused[0], st.sel) and torch.equal(fused[1], st.out)
+    h = P.host(w)
+    ref = P.oracle_step(w, h)
+    events = P.compare_selection(st.sel.cpu().numpy(), ref["scores"], w.seq_ptr, w.k, w.Hkv)
+    if events:
+        ref = P.oracle_step(w, h, sel=st.sel.cpu().numpy())
+    err = np.max(np.abs(st.out.cpu().numpy() - ref["out"]))
+    say(f"[gpu] wide-table: max|out-oracle| = {err:.3e}")
+    assert err <= P.TOL[w.dtype]
+    st.dense_attn()
+    torch.cuda.synchronize()
+    ref_d = O.dense_decode_step(h["q"], h["k_pool"], h["v_pool"], w.block_table, w.seq_lens,
+                                w.scale)
+    assert np.max(np.abs(st.out.cpu().numpy() - ref_d)) <= P.TOL[w.dtype]
