@@ -80,9 +80,48 @@ struct Assign {
 // (0 when n_p = 0), each an equal slice of its list. Workgroup 0 publishes
 // the first workgroup of every pair for the combine kernel. Returns false
 // when this workgroup has no work (uniform over the workgroup).
+// List length of pair p (dense: blocks of its sequence).
+template <bool DENSE>
+__device__ __forceinline__ int pair_len(const AttnArgs& a, int p) {
+  if (DENSE) return (cached_len(a, p / a.Hkv) + kBlock - 1) / kBlock;
+  const int n = a.counts[p];
+  return n < 0 ? 0 : (n > a.max_blocks ? a.max_blocks : n);
+}
+
+// Up to 64 pairs: every wave computes the whole assignment by itself (one
+// pair per lane, DPP scans), with no LDS and no workgroup barrier.
+template <bool DENSE>
+__device__ bool assign_work_wave(const AttnArgs& a, Assign* as) {
+  const int P = a.B * a.Hkv;
+  const int lane = threadIdx.x & 63, w = blockIdx.x;
+  const int n = lane < P ? pair_len<DENSE>(a, lane) : 0;
+  const int total = wave_sum(n);
+  const int per = total > 0 ? (total + a.nwg - 1) / a.nwg : 1;
+  const int S = n > 0 ? max(1, (n + per / 2) / per) : 0;
+  const int incl = wave_incl_sum(S);
+  const int total_s = __builtin_amdgcn_readlane(incl, 63);
+  const int run = incl - S;
+  if (w == 0 && threadIdx.x < 64) {
+    if (lane < P) a.ws_pref[lane] = run;
+    if (lane == 0) a.ws_pref[P] = total_s;
+  }
+  if (w >= total_s) return false;  // uniform over the workgroup
+  const uint64_t own = __ballot(lane < P && w >= run && w < run + S);
+  const int p = __ffsll(static_cast<unsigned long long>(own)) - 1;
+  const int r = w - __builtin_amdgcn_readlane(run, p);
+  const int Sp = __builtin_amdgcn_readlane(S, p);
+  const int64_t np = __builtin_amdgcn_readlane(n, p);
+  as->p = p;
+  as->T = DENSE ? cached_len(a, p / a.Hkv) : 0;
+  as->lo = static_cast<int>(r * np / Sp);
+  as->hi = static_cast<int>((r + 1) * np / Sp);
+  return true;
+}
+
 template <bool DENSE>
 __device__ bool assign_work(const AttnArgs& a, int* tmp_n, int* tmp_s, int* sh, Assign* as) {
   const int P = a.B * a.Hkv;
+  if (P <= 64) return assign_work_wave<DENSE>(a, as);
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6, w = blockIdx.x;
   const int per_t = (P + kThreads - 1) / kThreads;  // <= kPairsPerThread
   const int p0 = t * per_t;
@@ -92,14 +131,7 @@ __device__ bool assign_work(const AttnArgs& a, int* tmp_n, int* tmp_s, int* sh, 
   for (int j = 0; j < kPairsPerThread; ++j) {
     const int p = p0 + j;
     int n = 0;
-    if (j < per_t && p < P) {
-      if (DENSE) {
-        n = (cached_len(a, p / a.Hkv) + kBlock - 1) / kBlock;
-      } else {
-        n = a.counts[p];
-        n = n < 0 ? 0 : (n > a.max_blocks ? a.max_blocks : n);
-      }
-    }
+    if (j < per_t && p < P) n = pair_len<DENSE>(a, p);
     nreg[j] = n;
     mine += n;
   }
