@@ -85,6 +85,8 @@ def main():
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--period", type=int, default=35,
+                    help="decode steps per semantic boundary for the selection-reuse figure")
     ap.add_argument("--copy-calibrate", action="store_true",
                     help="first run an elementwise copy (negation) of 1 GiB into 1 GiB twice, "
                          "untimed: the known-size kernel that scales hardware byte counters "
@@ -173,6 +175,28 @@ def main():
     bytes_per_launch = float(np.mean([kv_bytes[i % L] for i in range(args.steps)]))
     achieved = bytes_per_launch / (attn_us * 1e-6) / 1e9
 
+    # selection reuse (ZoomR Sec. 3.4, Appendix A.3): the attended set is
+    # rebuilt at semantic boundaries, about every 35 tokens. Each layer runs
+    # its own period: a full step at T0 = T - period + 1, then cached-selection
+    # attention at T0 + i with the window grown by i. Layers rotate call by
+    # call, as in the timed steps above.
+    R = max(args.period, 1)
+    T_full = int(w0.seq_lens[0])
+    lens_i = [torch.full((w0.B,), T_full - R + 1 + i, dtype=torch.int32, device=dev)
+              for i in range(R)]
+
+    def period_call(c):
+        l, i = c % L, (c // L) % R
+        if i == 0:
+            steps[l].step(seq_lens=lens_i[0])
+        else:
+            steps[l].cached_attn(w0.window + i, seq_lens=lens_i[i])
+
+    g_period = capture(period_call, L * R)
+    g_period.replay()
+    torch.cuda.synchronize()
+    period_us = timed(g_period, L * R)
+
     # dense baseline (same caches, every token) for context
     dense_us = timed(g_dense, L)
     dense_bytes = int(w0.seq_lens.sum()) * w0.Hkv * 2 * d * s_bytes
@@ -183,6 +207,7 @@ def main():
         cpu = cpu_baseline(w0, args.cpu_seconds)
 
     steps_per_s = 1000.0 / ms_per_step
+    dense_gbs = dense_bytes / (dense_us * 1e-6) / 1e9
     res = {
         "metric": METRIC,
         "value": round(steps_per_s, 2),
@@ -211,11 +236,15 @@ def main():
                      "avg_launch_us": round(attn_us, 3),
                      "algorithmic_bytes_per_launch": int(bytes_per_launch)},
         "step_as_three_calls_us": round(calls_us, 3),
+        "tokens_per_s": round(steps_per_s * w0.B, 1),
+        "selection_reuse": {"period_steps": R, "us_per_step": round(period_us, 3),
+                            "steps_per_s": round(1e6 / period_us, 1)},
+        "speedup_vs_dense_attention": round(dense_us / attn_us, 3),
         "effective_kv_gbs": round(achieved, 1),
         "kv_tokens_per_step": int(np.mean([a.sum() for a in att])),
         "q_out_bytes_per_step": q_out_bytes,
         "dense_baseline": {"avg_launch_us": round(dense_us, 3), "kv_bytes": dense_bytes,
-                           "gbs": round(dense_bytes / (dense_us * 1e-6) / 1e9, 1)},
+                           "gbs": round(dense_gbs, 1)},
         "kv_reduction": round(dense_bytes / float(np.mean(kv_bytes)), 3),
         "cpu_baseline": cpu,
     }

@@ -49,7 +49,8 @@ zr_status attention_common(const zr_geom* geom, const void* q, const void* k_poo
   zr_status st = check_geom(geom);
   if (st != ZR_OK) return st;
   if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !out) return ZR_E_NULL;
-  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool)) return ZR_E_ALIGN;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out))
+    return ZR_E_ALIGN;
   if (max_attended < 0) return ZR_E_SHAPE;
   if (!isfinite(scale)) return ZR_E_SHAPE;
   if (static_cast<int64_t>(geom->batch) * geom->n_kv_heads > ZR_MAX_PAIRS)
@@ -108,7 +109,7 @@ ZR_API const char* zr_status_string(zr_status s) {
     case ZR_E_UNSUPPORTED: return "this build has no kernel for the requested shape or dtype";
     case ZR_E_WORKSPACE: return "workspace missing, misaligned or smaller than zr_workspace_bytes()";
     case ZR_E_LAUNCH: return "the HIP runtime reported a launch error";
-    case ZR_E_ALIGN: return "q, pools or summary keys are not 16-byte aligned";
+    case ZR_E_ALIGN: return "q, pools, out or summary keys are not 16-byte aligned";
   }
   return "unknown zr_status";
 }
@@ -182,6 +183,7 @@ ZR_API zr_status zr_sparse_decode_attn(const zr_geom* geom, const void* q, const
   pa.th_len = th->len;
   pa.sel = const_cast<int32_t*>(sel);  // read only in this mode
   fill_plan(*geom, *th, k, window, block_table, seq_lens, a, &pa);
+  a.window = window;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (zr::launch_pair(*geom, pa, zr::kModePlan, s) != hipSuccess) return ZR_E_LAUNCH;
   if (zr::launch_attention(*geom, a, false, s) != hipSuccess) return ZR_E_LAUNCH;
@@ -214,9 +216,29 @@ ZR_API zr_status zr_sparse_decode_step(const zr_geom* geom, const void* q, const
   pa.scores = scores;
   pa.sel = sel;
   fill_plan(*geom, *th, k, window, block_table, seq_lens, a, &pa);
+  a.window = window;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (zr::launch_pair(*geom, pa, zr::kModeStep, s) != hipSuccess) return ZR_E_LAUNCH;
   if (zr::launch_attention(*geom, a, false, s) != hipSuccess) return ZR_E_LAUNCH;
+  return ZR_OK;
+}
+
+ZR_API zr_status zr_sparse_decode_attn_cached(const zr_geom* geom, const void* q,
+                                              const void* k_pool, const void* v_pool,
+                                              const int32_t* block_table,
+                                              const int32_t* seq_lens, int32_t window,
+                                              float scale, int32_t max_attended, float* out,
+                                              void* workspace, size_t ws_bytes, void* stream) {
+  zr_status st = check_geom(geom);
+  if (st != ZR_OK) return st;
+  if (window < 0) return ZR_E_SHAPE;
+  zr::AttnArgs a{};
+  st = attention_common(geom, q, k_pool, v_pool, block_table, seq_lens, scale, out, workspace,
+                        ws_bytes, max_attended, &a);
+  if (st != ZR_OK) return st;
+  a.window = window;
+  if (zr::launch_attention(*geom, a, false, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return ZR_E_LAUNCH;
   return ZR_OK;
 }
 

@@ -70,31 +70,48 @@ __device__ __forceinline__ int cached_len(const AttnArgs& a, int b) {
 
 struct Assign {
   int p;       // pair
-  int T;       // cached tokens of the pair's sequence (dense)
+  int T;       // cached tokens of the pair's sequence
+  int tw;      // first window token (dense: 0)
+  int ncache;  // leading list entries read from the block lists (dense: 0)
   int lo, hi;  // entries [lo, hi) of the pair's list
 };
 
-// Workgroups per pair and this workgroup's share. Pair p has n_p list
-// entries (sparse: counted by the pair kernel; dense: ceil(T_b / 16)); with
-// per = ceil(total / nwg) it gets S_p = max(1, round(n_p / per)) workgroups
-// (0 when n_p = 0), each an equal slice of its list. Workgroup 0 publishes
-// the first workgroup of every pair for the combine kernel. Returns false
-// when this workgroup has no work (uniform over the workgroup).
-// List length of pair p (dense: blocks of its sequence).
+// A pair's list: its ncache span entries (sparse), then the blocks of the
+// window [tw, T) (dense: [0, T)).
+struct PairList {
+  int T, tw, ncache, n;
+};
+
 template <bool DENSE>
-__device__ __forceinline__ int pair_len(const AttnArgs& a, int p) {
-  if (DENSE) return (cached_len(a, p / a.Hkv) + kBlock - 1) / kBlock;
-  const int n = a.counts[p];
-  return n < 0 ? 0 : (n > a.max_blocks ? a.max_blocks : n);
+__device__ __forceinline__ PairList pair_list(const AttnArgs& a, int p) {
+  PairList r;
+  r.T = cached_len(a, p / a.Hkv);
+  r.tw = DENSE ? 0 : (r.T - a.window > 0 ? r.T - a.window : 0);
+  r.ncache = 0;
+  if (!DENSE) {
+    const int c = a.counts[p];
+    r.ncache = c < 0 ? 0 : (c > a.max_blocks ? a.max_blocks : c);
+  }
+  const int wb = r.T > r.tw ? ((r.T - 1) >> 4) - (r.tw >> 4) + 1 : 0;
+  r.n = r.ncache + wb;
+  return r;
 }
 
-// Up to 64 pairs: every wave computes the whole assignment by itself (one
+// Workgroups per pair and this workgroup's share. With per = ceil(total /
+// nwg), pair p gets S_p = max(1, round(n_p / per)) workgroups (0 when
+// n_p = 0), each an equal slice of its list. Workgroup 0 publishes the first
+// workgroup of every pair for the combine kernel. Returns false when this
+// workgroup has no work (uniform over the workgroup).
+//
+// Up to 64 pairs every wave computes the whole assignment by itself (one
 // pair per lane, DPP scans), with no LDS and no workgroup barrier.
 template <bool DENSE>
 __device__ bool assign_work_wave(const AttnArgs& a, Assign* as) {
   const int P = a.B * a.Hkv;
   const int lane = threadIdx.x & 63, w = blockIdx.x;
-  const int n = lane < P ? pair_len<DENSE>(a, lane) : 0;
+  PairList pl{0, 0, 0, 0};
+  if (lane < P) pl = pair_list<DENSE>(a, lane);
+  const int n = pl.n;
   const int total = wave_sum(n);
   const int per = total > 0 ? (total + a.nwg - 1) / a.nwg : 1;
   const int S = n > 0 ? max(1, (n + per / 2) / per) : 0;
@@ -112,12 +129,16 @@ __device__ bool assign_work_wave(const AttnArgs& a, Assign* as) {
   const int Sp = __builtin_amdgcn_readlane(S, p);
   const int64_t np = __builtin_amdgcn_readlane(n, p);
   as->p = p;
-  as->T = DENSE ? cached_len(a, p / a.Hkv) : 0;
+  as->T = __builtin_amdgcn_readlane(pl.T, p);
+  as->tw = __builtin_amdgcn_readlane(pl.tw, p);
+  as->ncache = __builtin_amdgcn_readlane(pl.ncache, p);
   as->lo = static_cast<int>(r * np / Sp);
   as->hi = static_cast<int>((r + 1) * np / Sp);
   return true;
 }
 
+// More pairs: thread t owns a contiguous run of pairs; workgroup sums and
+// scans through LDS.
 template <bool DENSE>
 __device__ bool assign_work(const AttnArgs& a, int* tmp_n, int* tmp_s, int* sh, Assign* as) {
   const int P = a.B * a.Hkv;
@@ -131,7 +152,7 @@ __device__ bool assign_work(const AttnArgs& a, int* tmp_n, int* tmp_s, int* sh, 
   for (int j = 0; j < kPairsPerThread; ++j) {
     const int p = p0 + j;
     int n = 0;
-    if (j < per_t && p < P) n = pair_len<DENSE>(a, p);
+    if (j < per_t && p < P) n = pair_list<DENSE>(a, p).n;
     nreg[j] = n;
     mine += n;
   }
@@ -143,7 +164,7 @@ __device__ bool assign_work(const AttnArgs& a, int* tmp_n, int* tmp_s, int* sh, 
 #pragma unroll
   for (int v = 0; v < kWaves; ++v) total += tmp_n[v];
   const int per = total > 0 ? (total + a.nwg - 1) / a.nwg : 1;
-  // workgroups per pair, prefix over pairs (thread t owns a contiguous run)
+  // workgroups per pair, prefix over pairs
   int ms = 0;
 #pragma unroll
   for (int j = 0; j < kPairsPerThread; ++j)
@@ -164,10 +185,14 @@ __device__ bool assign_work(const AttnArgs& a, int* tmp_n, int* tmp_s, int* sh, 
       const int n = nreg[j];
       const int S = n > 0 ? max(1, (n + per / 2) / per) : 0;
       if (w >= run && w < run + S) {
+        const PairList pl = pair_list<DENSE>(a, p);  // this thread read it a moment ago
         sh[0] = p;
         sh[1] = w - run;
         sh[2] = S;
         sh[3] = n;
+        sh[4] = pl.T;
+        sh[5] = pl.tw;
+        sh[6] = pl.ncache;
       }
       if (w == 0) a.ws_pref[p] = run;
       run += S;
@@ -179,7 +204,9 @@ __device__ bool assign_work(const AttnArgs& a, int* tmp_n, int* tmp_s, int* sh, 
   const int p = sh[0], r = sh[1], S = sh[2];
   const int64_t n = sh[3];
   as->p = p;
-  as->T = DENSE ? cached_len(a, p / a.Hkv) : 0;
+  as->T = sh[4];
+  as->tw = sh[5];
+  as->ncache = sh[6];
   as->lo = static_cast<int>(r * n / S);
   as->hi = static_cast<int>((r + 1) * n / S);
   return true;
@@ -195,14 +222,18 @@ __device__ __forceinline__ void resolve_entry(const AttnArgs& a, const Assign& a
   if (j < 0) return;
   int blk;
   uint32_t m;
-  if (DENSE) {
-    blk = a.block_table[static_cast<size_t>(b) * a.max_blocks + j];
-    const int rest = as.T - j * kBlock;
-    m = rest >= kBlock ? 0xffffu : ((1u << rest) - 1u);
-  } else {
+  if (!DENSE && j < as.ncache) {
     const int2 e = a.entries[static_cast<size_t>(as.p) * a.max_blocks + j];
     blk = e.x;
     m = static_cast<uint32_t>(e.y) & 0xffffu;
+  } else {
+    // window block: slots of [tw, T) in logical block lb
+    const int lb = (as.tw >> 4) + (j - as.ncache);
+    const int b0 = lb << 4;
+    const int from = (as.tw > b0 ? as.tw : b0) - b0;
+    const int to = (as.T < b0 + kBlock ? as.T : b0 + kBlock) - b0;
+    blk = a.block_table[static_cast<size_t>(b) * a.max_blocks + lb];
+    m = ((1u << to) - 1u) & ~((1u << from) - 1u);
   }
   if (blk < 0 || blk >= a.num_blocks) return;
   *pb = blk;
@@ -403,7 +434,7 @@ attn_mfma_kernel(AttnArgs a) {
   __shared__ float red_l[kWaves][G];
   __shared__ float red_o[kWaves][G][D];
   __shared__ int tmp_n[kWaves], tmp_s[kWaves];
-  __shared__ int sh_as[4];
+  __shared__ int sh_as[8];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
@@ -494,7 +525,7 @@ attn_valu_kernel(AttnArgs a) {
   __shared__ float red_o[kWaves][G][D];
   __shared__ float p_lds[kWaves][NBW * kBlock][G];
   __shared__ int tmp_n[kWaves], tmp_s[kWaves];
-  __shared__ int sh_as[4];
+  __shared__ int sh_as[8];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   Assign as;
@@ -641,38 +672,38 @@ attn_valu_kernel(AttnArgs a) {
 // Combine: merge the partials of pair (b, g) (workgroups [ws_pref[p],
 // ws_pref[p+1])) by log-sum-exp,
 //   out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s,  M = max_s m_s.
-// Each thread owns (head, dim) outputs and reads a tile of partials with
-// independent loads, merging tiles online.
+// Each thread owns four consecutive dimensions of one head and reads a tile
+// of partials with independent 16-byte loads (slot indices clamped, so the
+// loads need no branches), merging tiles online.
 // ---------------------------------------------------------------------------
-constexpr int kCombineTile = 16;
+constexpr int kCombineTile = 8;
 
 template <int G, int D>
 __global__ void __launch_bounds__(kThreads)
 attn_combine_kernel(AttnArgs a) {
+  constexpr int D4 = D / 4, ITEMS = G * D4, PER = (ITEMS + kThreads - 1) / kThreads;
   const int g = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
   const int p = b * a.Hkv + g;
   const int s0 = a.ws_pref[p], s1 = a.ws_pref[p + 1];
-  constexpr int PER = (G * D + kThreads - 1) / kThreads;
-  float* out = a.out + (static_cast<size_t>(b) * a.Hq + g * G) * D;
+  float4* out4 = reinterpret_cast<float4*>(a.out + (static_cast<size_t>(b) * a.Hq + g * G) * D);
+  const float4* acc4 = reinterpret_cast<const float4*>(a.ws_acc);
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
     const int idx = t + j * kThreads;
-    if (idx >= G * D) continue;
-    const int h = idx / D, e = idx % D;
-    float M = kNegInf, Lsum = 0.f, A = 0.f;
+    if (idx >= ITEMS) continue;
+    const int h = idx / D4, e4 = idx % D4;
+    float M = kNegInf, Lsum = 0.f;
+    float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int c0 = s0; c0 < s1; c0 += kCombineTile) {
-      float ms[kCombineTile], ls[kCombineTile], vs[kCombineTile];
+      float ms[kCombineTile], ls[kCombineTile];
+      float4 vs[kCombineTile];
 #pragma unroll
       for (int u = 0; u < kCombineTile; ++u) {
-        const int s = c0 + u;
-        ms[u] = kNegInf;
-        ls[u] = 0.f;
-        vs[u] = 0.f;
-        if (s < s1) {
-          ms[u] = a.ws_m[static_cast<size_t>(s) * G + h];
-          ls[u] = a.ws_l[static_cast<size_t>(s) * G + h];
-          vs[u] = a.ws_acc[(static_cast<size_t>(s) * G + h) * D + e];
-        }
+        const size_t s = static_cast<size_t>(c0 + u < s1 ? c0 + u : s1 - 1);
+        ms[u] = a.ws_m[s * G + h];
+        ls[u] = a.ws_l[s * G + h];
+        vs[u] = acc4[(s * G + h) * D4 + e4];
+        if (c0 + u >= s1) ms[u] = kNegInf;
       }
       float mt = M;
 #pragma unroll
@@ -680,18 +711,24 @@ attn_combine_kernel(AttnArgs a) {
       if (mt == kNegInf) continue;
       const float alpha = M == kNegInf ? 0.f : exp2f(M - mt);
       Lsum *= alpha;
-      A *= alpha;
+      A.x *= alpha;
+      A.y *= alpha;
+      A.z *= alpha;
+      A.w *= alpha;
 #pragma unroll
       for (int u = 0; u < kCombineTile; ++u) {
-        if (ms[u] != kNegInf) {
-          const float w = exp2f(ms[u] - mt);
-          Lsum = fmaf(ls[u], w, Lsum);
-          A = fmaf(vs[u], w, A);
-        }
+        const float w = ms[u] != kNegInf ? exp2f(ms[u] - mt) : 0.f;
+        Lsum = fmaf(ls[u], w, Lsum);
+        A.x = fmaf(vs[u].x, w, A.x);
+        A.y = fmaf(vs[u].y, w, A.y);
+        A.z = fmaf(vs[u].z, w, A.z);
+        A.w = fmaf(vs[u].w, w, A.w);
       }
       M = mt;
     }
-    out[idx] = Lsum > 0.f ? A / Lsum : 0.f;
+    const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
+    out4[idx] = Lsum > 0.f ? make_float4(A.x * inv, A.y * inv, A.z * inv, A.w * inv)
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
   }
 }
 

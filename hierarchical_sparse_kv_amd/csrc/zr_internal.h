@@ -136,9 +136,10 @@ struct PairArgs {
 };
 
 // Attention launch parameters (device pointers + sizes), passed by value.
-// Pair p = b * Hkv + g has counts[p] entries entries[p][0..) (sparse; the
-// dense kernel reads the block table directly). Partial results are indexed
-// by workgroup; workgroups [ws_pref[p], ws_pref[p + 1]) hold pair p's.
+// Pair p = b * Hkv + g attends its counts[p] list entries entries[p][0..)
+// (sparse only) and then the blocks of its window [T - window, T) (dense:
+// [0, T)), read from the block table. Partial results are indexed by
+// workgroup; workgroups [ws_pref[p], ws_pref[p + 1]) hold pair p's.
 struct AttnArgs {
   const void* q;
   const void* k_pool;
@@ -153,6 +154,7 @@ struct AttnArgs {
   float* ws_acc;             // [nwg + P][G][D]
   float* out;                // [B][Hq][D]
   int32_t B, Hq, Hkv, max_blocks, num_blocks;
+  int32_t window;            // sparse: window tokens appended after the cached entries
   int32_t nwg;               // target workgroups; the grid has nwg + P
   float scale_log2;          // scale * log2(e)
 };

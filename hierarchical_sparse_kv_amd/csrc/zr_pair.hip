@@ -19,12 +19,14 @@
 //
 // The attended set is the union of the window [T - W, T) and the selected
 // thoughts' spans clipped below T - W (ZoomR Sec. 3.3 eq. I_f restricted to
-// the window and full-resolution spans). It is built as a bitmap of slot
-// masks, one 16-bit mask per logical block of the paged cache, so tokens
-// shared by several spans count once whatever the order of `sel`. The
-// non-empty blocks, resolved through the block table (KV-cache management
-// page, paged KV cache, eq. 4), form the pair's list of (physical block,
-// slot mask) entries for the attention kernel.
+// the window and full-resolution spans). The spans part is built here as a
+// bitmap of slot masks, one 16-bit mask per logical block of the paged
+// cache, so tokens shared by several spans count once whatever the order of
+// `sel`. The non-empty blocks, resolved through the block table (KV-cache
+// management page, paged KV cache, eq. 4), form the pair's list of (physical
+// block, slot mask) entries; the attention kernel appends the window's
+// blocks itself, so a list stays valid while the window grows between
+// semantic boundaries (ZoomR Sec. 3.4).
 //
 // The four modes (template flags) share this code:
 //   SCORE            scores only                       (zr_coarse_score)
@@ -270,7 +272,9 @@ __device__ void select_by_radix(const PairLds& L, int n, int k, int32_t* out, ui
 // ---------------------------------------------------------------------------
 // The pair kernel: one 256-thread workgroup per pair p = b * Hkv + g.
 // ---------------------------------------------------------------------------
-template <typename E, int D, bool SCORE, bool SELECT, bool PLAN>
+// STH: the thought spans are staged in LDS (a template flag, so that the
+// span reads stay LDS reads and never wait on outstanding global stores).
+template <typename E, int D, bool SCORE, bool SELECT, bool PLAN, bool STH>
 __global__ void __launch_bounds__(kPairThreads)
 pair_kernel(PairArgs a) {
   constexpr int VPL = 16 / E::kBytes;  // elements per 16-byte load
@@ -285,7 +289,7 @@ pair_kernel(PairArgs a) {
 
   const int p = blockIdx.x, t = threadIdx.x;
   const int b = p / a.Hkv, g = p - b * a.Hkv;
-  const PairLds L = pair_lds(dyn, a.max_per_seq, a.k, a.max_blocks, SELECT, PLAN, a.stage_th);
+  const PairLds L = pair_lds(dyn, a.max_per_seq, a.k, a.max_blocks, SELECT, PLAN, STH);
 
   using St = typename E::storage;
   const int c = t % LPT, r0 = t / LPT;
@@ -328,7 +332,7 @@ pair_kernel(PairArgs a) {
   hi = hi < lo ? lo : (hi > a.n_total ? a.n_total : hi);
   const int n = hi - lo < a.max_per_seq ? hi - lo : a.max_per_seq;
   int ths0 = 0, thl0 = 0;
-  if (PLAN && a.stage_th && t < n) {
+  if (PLAN && STH && t < n) {
     ths0 = a.th_start[lo + t];
     thl0 = a.th_len[lo + t];
   }
@@ -359,7 +363,7 @@ pair_kernel(PairArgs a) {
         if (i < a.k) L.sel_l[i] = selr[j];
       }
     }
-    if (a.stage_th) {
+    if (STH) {
       if (t < n) {
         L.th_s[t] = ths0;
         L.th_l[t] = thl0;
@@ -431,26 +435,29 @@ pair_kernel(PairArgs a) {
   }
 
   if (PLAN) {
-    // spans: 0..k-1 the selected thoughts, k the window; thread t owns a
-    // contiguous run of spans so the block-count scan follows span order
-    const int nsp = a.k + 1;
+    // spans: the selected thoughts, clipped below the window start (the
+    // attention kernel adds the window itself); thread t owns a contiguous
+    // run of spans so the block-count scan follows span order
+    const int nsp = a.k;
     const int per_s = (nsp + kPairThreads - 1) / kPairThreads;
     const int s0 = t * per_s, s1 = s0 + per_s < nsp ? s0 + per_s : nsp;
     int cnt = 0;
     for (int i = s0; i < s1; ++i) {
-      int s = tw, e = T;
-      if (i < a.k) {
-        s = 0;
-        e = 0;
-        const int th = L.sel_l[i];
-        if (th >= 0 && th < n) {
-          const int ts = a.stage_th ? L.th_s[th] : a.th_start[lo + th];
-          const int tl = a.stage_th ? L.th_l[th] : a.th_len[lo + th];
-          s = ts > 0 ? ts : 0;
-          e = tl > 0 ? ts + tl : s;
-          e = e < tw ? e : tw;
-          e = e > s ? e : s;
+      int s = 0, e = 0;
+      const int th = L.sel_l[i];
+      if (th >= 0 && th < n) {
+        int ts, tl;
+        if (STH) {
+          ts = L.th_s[th];
+          tl = L.th_l[th];
+        } else {
+          ts = a.th_start[lo + th];
+          tl = a.th_len[lo + th];
         }
+        s = ts > 0 ? ts : 0;
+        e = tl > 0 ? ts + tl : s;
+        e = e < tw ? e : tw;
+        e = e > s ? e : s;
       }
       L.sp_s[i] = s;
       L.sp_e[i] = e;
@@ -550,8 +557,13 @@ static hipError_t launch_pair_t(const zr_geom& gm, PairArgs a, hipStream_t s) {
   }
   const size_t lds = pair_dyn_lds(a, SELECT, PLAN);
   if (kPairStaticLds + lds > kPairLdsLimit) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((pair_kernel<E, D, SCORE, SELECT, PLAN>),
-                     dim3(gm.batch * gm.n_kv_heads), dim3(kPairThreads), lds, s, a);
+  const dim3 grid(gm.batch * gm.n_kv_heads);
+  if (a.stage_th)
+    hipLaunchKernelGGL((pair_kernel<E, D, SCORE, SELECT, PLAN, true>), grid, dim3(kPairThreads),
+                       lds, s, a);
+  else
+    hipLaunchKernelGGL((pair_kernel<E, D, SCORE, SELECT, PLAN, false>), grid, dim3(kPairThreads),
+                       lds, s, a);
   return hipGetLastError();
 }
 

@@ -55,6 +55,9 @@ _SIGS = {
     "zr_sparse_decode_step": (ctypes.c_int, [_G, _P, _P, _P, _P, _P, _T, ctypes.c_int32,
                                              ctypes.c_int32, ctypes.c_float, ctypes.c_int32,
                                              _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "zr_sparse_decode_attn_cached": (ctypes.c_int, [_G, _P, _P, _P, _P, _P, ctypes.c_int32,
+                                                    ctypes.c_float, ctypes.c_int32, _P, _P,
+                                                    ctypes.c_size_t, _P]),
     "zr_dense_paged_decode_attn": (ctypes.c_int, [_G, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P,
                                                   ctypes.c_size_t, _P]),
     "zr_workspace_bytes": (ctypes.c_size_t, [_G, ctypes.c_int32]),
@@ -118,6 +121,14 @@ def zr_sparse_decode_step(geom, q, k_pool, v_pool, block_table, seq_lens, th, k,
                                        seq_lens, ctypes.byref(th), int(k), int(window),
                                        float(scale), int(max_attended), scores, sel, out,
                                        workspace, int(ws_bytes), stream)
+
+
+def zr_sparse_decode_attn_cached(geom, q, k_pool, v_pool, block_table, seq_lens, window, scale,
+                                 max_attended, out, workspace, ws_bytes, stream=None) -> int:
+    return lib().zr_sparse_decode_attn_cached(ctypes.byref(geom), q, k_pool, v_pool, block_table,
+                                              seq_lens, int(window), float(scale),
+                                              int(max_attended), out, workspace, int(ws_bytes),
+                                              stream)
 
 
 def zr_dense_paged_decode_attn(geom, q, k_pool, v_pool, block_table, seq_lens, scale, out,
@@ -201,6 +212,17 @@ class DeviceStep:
             _ptr(sel) if self.k else None, self.k, self.window, self.scale, self.max_attended,
             _ptr(out), _ptr(self.workspace), self.workspace.numel(), _stream()))
 
+    def cached_attn(self, window, seq_lens=None, q=None, out=None):
+        """Attention on the selection cached in the workspace by the last
+        sparse_attn / step call, with window `window` over `seq_lens`."""
+        seq_lens = self.seq_lens if seq_lens is None else seq_lens
+        q = self.q if q is None else q
+        out = self.out if out is None else out
+        check("zr_sparse_decode_attn_cached", zr_sparse_decode_attn_cached(
+            self.geom, _ptr(q), _ptr(self.k_pool), _ptr(self.v_pool), _ptr(self.block_table),
+            _ptr(seq_lens), int(window), self.scale, self.max_attended, _ptr(out),
+            _ptr(self.workspace), self.workspace.numel(), _stream()))
+
     def dense_attn(self, out=None):
         out = self.out if out is None else out
         check("zr_dense_paged_decode_attn", zr_dense_paged_decode_attn(
@@ -208,14 +230,15 @@ class DeviceStep:
             _ptr(self.block_table), _ptr(self.seq_lens), self.scale, _ptr(out),
             _ptr(self.workspace), self.workspace.numel(), _stream()))
 
-    def step(self, scores=None, sel=None, out=None):
+    def step(self, scores=None, sel=None, out=None, seq_lens=None):
         """One sparse decode step as one call (zr_sparse_decode_step)."""
+        seq_lens = self.seq_lens if seq_lens is None else seq_lens
         scores = self.scores if scores is None else scores
         sel = self.sel if sel is None else sel
         out = self.out if out is None else out
         check("zr_sparse_decode_step", zr_sparse_decode_step(
             self.geom, _ptr(self.q), _ptr(self.k_pool), _ptr(self.v_pool),
-            _ptr(self.block_table), _ptr(self.seq_lens), self.th, self.k, self.window,
+            _ptr(self.block_table), _ptr(seq_lens), self.th, self.k, self.window,
             self.scale, self.max_attended, _ptr(scores), _ptr(sel) if self.k else None,
             _ptr(out), _ptr(self.workspace), self.workspace.numel(), _stream()))
 

@@ -16,6 +16,10 @@
  *                        "Paged KV cache (PagedAttention)").
  *   zr_sparse_decode_step runs steps 1-3 as one call (fewer launches and
  *   dependent memory round trips; same results as the three calls).
+ *   zr_sparse_decode_attn_cached repeats step 3 on the selection kept in
+ *   the workspace, for the decode steps between semantic boundaries, where
+ *   ZoomR keeps the attended set and only the recent tokens grow (ZoomR
+ *   Sec. 3.4 and Appendix A.3; Algorithm 1 rebuilds it at boundaries only).
  *   zr_dense_paged_decode_attn is the dense baseline: attention over every
  *   cached token through the same block table (same page, eq. 4).
  *
@@ -34,6 +38,8 @@
  *     16 * max_blocks_per_seq, sel entries in [-1, N_b)). The kernels clamp
  *     or skip entries outside these ranges so that no access leaves the
  *     buffers, but the result for such entries is unspecified.
+ *   - q, k_pool, v_pool, summary_keys and out must be 16-byte aligned
+ *     (ZR_E_ALIGN otherwise), the workspace too (ZR_E_WORKSPACE).
  *   - Calls on one stream run in order; calls that write the same buffers on
  *     different streams race.
  *
@@ -76,7 +82,7 @@ typedef enum {
   ZR_E_UNSUPPORTED = 3, /* valid request this build has no kernel for */
   ZR_E_WORKSPACE = 4,   /* workspace NULL or smaller than zr_workspace_bytes() */
   ZR_E_LAUNCH = 5,      /* the HIP runtime reported an error */
-  ZR_E_ALIGN = 6        /* q, pools or summary keys not 16-byte aligned */
+  ZR_E_ALIGN = 6        /* q, pools, out or summary keys not 16-byte aligned */
 } zr_status;
 
 typedef enum { ZR_F32 = 0, ZR_BF16 = 1 } zr_dtype;
@@ -164,6 +170,28 @@ zr_status zr_sparse_decode_attn(const zr_geom* geom, const void* q, const void* 
                                 const int32_t* sel, int32_t k, int32_t window, float scale,
                                 int32_t max_attended, float* out, void* workspace,
                                 size_t ws_bytes, void* stream);
+
+/*
+ * Sparse attention on a cached selection. `workspace` must hold the block
+ * lists written by the last zr_sparse_decode_attn or zr_sparse_decode_step
+ * that used it (same geom; the block-table rows of those spans unchanged):
+ * the selected thoughts' spans, clipped below that call's window start
+ * T0 - window0. This call attends those spans plus its own window
+ * [T - window, T) of the current seq_lens. Between semantic boundaries pass
+ * window = window0 + (T - T0), so that the window keeps the start it had at
+ * the boundary and every token decoded since is attended (ZoomR Sec. 3.4:
+ * the attended set is recomputed only at semantic boundaries); the result
+ * then equals zr_sparse_decode_attn with the same selection and that window.
+ * A smaller window leaves the tokens between the two window starts out.
+ * Workspace and errors as zr_sparse_decode_attn (ws_bytes >=
+ * zr_workspace_bytes(geom, max_attended); the lists do not depend on
+ * max_attended).
+ */
+zr_status zr_sparse_decode_attn_cached(const zr_geom* geom, const void* q, const void* k_pool,
+                                       const void* v_pool, const int32_t* block_table,
+                                       const int32_t* seq_lens, int32_t window, float scale,
+                                       int32_t max_attended, float* out, void* workspace,
+                                       size_t ws_bytes, void* stream);
 
 /*
  * One whole sparse decode step: zr_coarse_score, zr_select_topk and

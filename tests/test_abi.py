@@ -23,8 +23,9 @@ def L():
 def test_exports_every_declared_symbol(L):
     declared = zr.header_symbols()
     assert declared == sorted(["zr_coarse_score", "zr_select_topk", "zr_sparse_decode_attn",
-                               "zr_sparse_decode_step", "zr_dense_paged_decode_attn",
-                               "zr_workspace_bytes", "zr_status_string"])
+                               "zr_sparse_decode_attn_cached", "zr_sparse_decode_step",
+                               "zr_dense_paged_decode_attn", "zr_workspace_bytes",
+                               "zr_status_string"])
     out = subprocess.run(["nm", "-D", "--defined-only", zr.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = sorted(l.split()[-1] for l in out.splitlines() if l.split()[-2] == "T")
@@ -92,6 +93,8 @@ def test_geometry_rejected(L, kw, code):
                                          1 << 20) == code
     assert zr.zr_sparse_decode_step(g, FAKE, FAKE, FAKE, FAKE, FAKE, _th(), 2, 16, 0.1, 100,
                                     FAKE, FAKE, FAKE, FAKE, 1 << 20) == code
+    assert zr.zr_sparse_decode_attn_cached(g, FAKE, FAKE, FAKE, FAKE, FAKE, 16, 0.1, 100, FAKE,
+                                           FAKE, 1 << 20) == code
 
 
 def test_null_and_range_errors(L):
@@ -117,6 +120,7 @@ def test_null_and_range_errors(L):
     assert sp(sel=None) == zr.ZR_E_NULL
     assert sp(out=None) == zr.ZR_E_NULL
     assert sp(v_pool=FAKE + 8) == zr.ZR_E_ALIGN
+    assert sp(out=FAKE + 4) == zr.ZR_E_ALIGN
     assert sp(workspace=None) == zr.ZR_E_WORKSPACE
     assert sp(ws_bytes=16) == zr.ZR_E_WORKSPACE
     need = zr.zr_workspace_bytes(g, 100)
@@ -142,3 +146,15 @@ def test_step_errors(L):
     assert st(ws_bytes=zr.zr_workspace_bytes(g, 100) - 1) == zr.ZR_E_WORKSPACE
     # block lists too large for the pair kernel's on-chip memory
     assert st(geom=_geom(max_blocks_per_seq=60000, batch=1), ws_bytes=1 << 30) == zr.ZR_E_UNSUPPORTED
+
+
+def test_cached_errors(L):
+    g = _geom()
+    c = lambda **kw: zr.zr_sparse_decode_attn_cached(**dict(dict(
+        geom=g, q=FAKE, k_pool=FAKE, v_pool=FAKE, block_table=FAKE, seq_lens=FAKE, window=16,
+        scale=0.1, max_attended=100, out=FAKE, workspace=FAKE, ws_bytes=1 << 20), **kw))
+    assert c(window=-1) == zr.ZR_E_SHAPE
+    assert c(seq_lens=None) == zr.ZR_E_NULL
+    assert c(q=FAKE + 2) == zr.ZR_E_ALIGN
+    assert c(workspace=None) == zr.ZR_E_WORKSPACE
+    assert c(scale=float("inf")) == zr.ZR_E_SHAPE

@@ -253,3 +253,40 @@ def test_wide_block_table_and_unstaged_spans():
     ref_d = O.dense_decode_step(h["q"], h["k_pool"], h["v_pool"], w.block_table, w.seq_lens,
                                 w.scale)
     assert np.max(np.abs(st.out.cpu().numpy() - ref_d)) <= P.TOL[w.dtype]
+
+
+def test_cached_selection_between_boundaries():
+    """Selection made at a boundary (T0), then decode steps T0 + i with new
+    queries: zr_sparse_decode_attn_cached with window W + i equals the oracle
+    run on the same selection with that window, and zr_sparse_decode_attn
+    with the same arguments bit for bit."""
+    w = _small(1, k=4, seq_len=("uniform", 600, 900), window=32)
+    T0 = np.maximum(w.seq_lens - 6, 0).astype(np.int32)
+    st = zr.DeviceStep(w.q, w.k_pool, w.v_pool, w.block_table, T0, w.seq_ptr, w.th_start,
+                       w.th_len, w.summary_keys, w.max_per_seq, w.k, w.window, w.scale,
+                       int(w.seq_lens.max()))
+    st.step()
+    torch.cuda.synchronize()
+    sel = st.sel.clone()
+    h = P.host(w)
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    for i in range(1, 6):
+        Ti = torch.as_tensor(T0 + i, dtype=torch.int32, device="cuda")
+        qi = torch.randn(w.q.shape, generator=gen, device="cuda").to(w.q.dtype)
+        st.cached_attn(w.window + i, seq_lens=Ti, q=qi)
+        torch.cuda.synchronize()
+        got = st.out.clone()
+        hq = dict(h, q=synth.to_numpy_f32(qi))
+        ref = O.sparse_decode_step(hq["q"], hq["k_pool"], hq["v_pool"], w.block_table, T0 + i,
+                                   w.seq_ptr, w.th_start, w.th_len, hq["kbar"], w.k,
+                                   w.window + i, w.scale, sel=sel.cpu().numpy())
+        err = np.max(np.abs(got.cpu().numpy() - ref["out"]))
+        say(f"[gpu] cached step {i}: max|out-oracle| = {err:.3e}")
+        assert err <= P.TOL[w.dtype]
+        # the same attention with the selection passed explicitly
+        st2 = zr.DeviceStep(qi, w.k_pool, w.v_pool, w.block_table, T0 + i, w.seq_ptr,
+                            w.th_start, w.th_len, w.summary_keys, w.max_per_seq, w.k,
+                            w.window + i, w.scale, int(w.seq_lens.max()))
+        st2.sparse_attn(sel=sel)
+        torch.cuda.synchronize()
+        assert torch.equal(st2.out, got), i
