@@ -197,6 +197,28 @@ def main():
     torch.cuda.synchronize()
     period_us = timed(g_period, L * R)
 
+    # append path: one token per sequence into a paged cache with on-demand
+    # blocks (zr_append_kv), and mean summary keys of one completed thought per
+    # sequence (zr_summary_keys), same head shapes
+    wa = synth.make_workload(1, seed=1, device=dev, overrides=dict(
+        seq_len=("fixed", 1024), extra_tokens=args.steps + 16,
+        spare_blocks=w0.B * ((args.steps + 15) // 16 + 2)))
+    sa = zr.step_from_workload(wa)
+    free_np = wa.extra["free_blocks"]
+    free = torch.as_tensor(free_np, device=dev)
+    free_count = torch.tensor([len(free_np)], dtype=torch.int32, device=dev)
+    app_status = torch.empty(wa.B, dtype=torch.int32, device=dev)
+    kn = torch.randn((wa.B, wa.Hkv, wa.d), device=dev).to(wa.k_pool.dtype)
+    vn = torch.randn((wa.B, wa.Hkv, wa.d), device=dev).to(wa.k_pool.dtype)
+    g_app = capture(lambda i: sa.append(kn, vn, free, free_count, app_status), args.steps)
+    append_us = timed(g_app, args.steps)
+    assert int((app_status != 0).sum()) == 0, "append failed"
+    which_np = np.array([int(w0.seq_ptr[b]) + 10 for b in range(w0.B)], np.int32)
+    which = torch.as_tensor(which_np, device=dev)
+    kb_out = torch.empty_like(steps[0].summary_keys)
+    g_sum = capture(lambda i: steps[i % L].compute_summary_keys(which, out=kb_out), args.steps)
+    summary_us = timed(g_sum, args.steps)
+
     # dense baseline (same caches, every token) for context
     dense_us = timed(g_dense, L)
     dense_bytes = int(w0.seq_lens.sum()) * w0.Hkv * 2 * d * s_bytes
@@ -240,6 +262,10 @@ def main():
         "selection_reuse": {"period_steps": R, "us_per_step": round(period_us, 3),
                             "steps_per_s": round(1e6 / period_us, 1)},
         "speedup_vs_dense_attention": round(dense_us / attn_us, 3),
+        "append_path": {"append_kv_us": round(append_us, 3),
+                        "summary_keys_us": round(summary_us, 3),
+                        "summary_thoughts_per_call": int(w0.B),
+                        "summary_tokens_per_call": int(w0.th_len[which_np].sum())},
         "effective_kv_gbs": round(achieved, 1),
         "kv_tokens_per_step": int(np.mean([a.sum() for a in att])),
         "q_out_bytes_per_step": q_out_bytes,

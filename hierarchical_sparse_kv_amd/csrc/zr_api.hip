@@ -242,6 +242,69 @@ ZR_API zr_status zr_sparse_decode_attn_cached(const zr_geom* geom, const void* q
   return ZR_OK;
 }
 
+ZR_API zr_status zr_append_kv(const zr_geom* geom, void* k_pool, void* v_pool,
+                              int32_t* block_table, int32_t* seq_lens, const void* k_new,
+                              const void* v_new, const int32_t* free_blocks,
+                              int32_t* free_count, int32_t* status, void* stream) {
+  zr_status st = check_geom(geom);
+  if (st != ZR_OK) return st;
+  if (geom->batch == 0) return ZR_OK;
+  if (!k_pool || !v_pool || !block_table || !seq_lens || !k_new || !v_new || !free_blocks ||
+      !free_count || !status)
+    return ZR_E_NULL;
+  if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(k_new) || !aligned16(v_new))
+    return ZR_E_ALIGN;
+  zr::AppendArgs a{};
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.free_blocks = free_blocks;
+  a.free_count = free_count;
+  a.status = status;
+  a.Hkv = geom->n_kv_heads;
+  a.D = geom->head_dim;
+  a.max_blocks = geom->max_blocks_per_seq;
+  a.num_blocks = geom->num_blocks;
+  if (zr::launch_append(*geom, a, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return ZR_E_LAUNCH;
+  return ZR_OK;
+}
+
+ZR_API zr_status zr_summary_keys(const zr_geom* geom, const void* k_pool,
+                                 const int32_t* block_table, const zr_thoughts* th,
+                                 const int32_t* which, int32_t n_which, void* summary_keys,
+                                 void* stream) {
+  zr_status st = check_geom(geom);
+  if (st != ZR_OK) return st;
+  st = check_thoughts(th, false);
+  if (st != ZR_OK) return st;
+  if (n_which < 0) return ZR_E_SHAPE;
+  if (n_which == 0 || geom->batch == 0) return ZR_OK;
+  if (!k_pool || !block_table || !which || !summary_keys) return ZR_E_NULL;
+  if (!aligned16(k_pool) || !aligned16(summary_keys)) return ZR_E_ALIGN;
+  if (n_which > 65535 * 1024) return ZR_E_UNSUPPORTED;
+  zr::SummaryArgs a{};
+  a.k_pool = k_pool;
+  a.block_table = block_table;
+  a.seq_ptr = th->seq_ptr;
+  a.th_start = th->start;
+  a.th_len = th->len;
+  a.which = which;
+  a.out = summary_keys;
+  a.B = geom->batch;
+  a.Hkv = geom->n_kv_heads;
+  a.max_blocks = geom->max_blocks_per_seq;
+  a.num_blocks = geom->num_blocks;
+  a.n_total = th->n_total;
+  if (zr::launch_summary_keys(*geom, a, n_which, static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return ZR_E_LAUNCH;
+  return ZR_OK;
+}
+
 ZR_API zr_status zr_dense_paged_decode_attn(const zr_geom* geom, const void* q,
                                             const void* k_pool, const void* v_pool,
                                             const int32_t* block_table, const int32_t* seq_lens,

@@ -159,7 +159,35 @@ struct AttnArgs {
   float scale_log2;          // scale * log2(e)
 };
 
+// Append path (zr_append.hip).
+struct AppendArgs {
+  void* k_pool;
+  void* v_pool;
+  int32_t* block_table;       // [B][max_blocks]: a popped block is written here
+  int32_t* seq_lens;          // [B]: grows by one per appended token
+  const void* k_new;          // [B][Hkv][D]
+  const void* v_new;          // [B][Hkv][D]
+  const int32_t* free_blocks; // free stack; entries [0, *free_count) are free, top last
+  int32_t* free_count;        // [1]
+  int32_t* status;            // [B] ZR_APPEND_*
+  int32_t Hkv, D, max_blocks, num_blocks;
+};
+
+struct SummaryArgs {
+  const void* k_pool;
+  const int32_t* block_table;
+  const int32_t* seq_ptr;
+  const int32_t* th_start;
+  const int32_t* th_len;
+  const int32_t* which;       // [n_which] global thought indices
+  void* out;                  // summary keys [n_total][Hkv][D]: rows `which` written
+  int32_t B, Hkv, max_blocks, num_blocks, n_total;
+};
+
 // Host-side launchers (defined next to their kernels).
+hipError_t launch_append(const zr_geom& g, const AppendArgs& a, hipStream_t s);
+hipError_t launch_summary_keys(const zr_geom& g, const SummaryArgs& a, int n_which,
+                               hipStream_t s);
 hipError_t launch_pair(const zr_geom& g, const PairArgs& a, int mode, hipStream_t s);
 // Whether the pair kernel's LDS fits (with nothing optional staged).
 bool pair_lds_ok(const zr_geom& g, int max_per_seq, int k, bool select, bool plan);

@@ -24,6 +24,9 @@ hundred tokens as in ZoomR Sec. 3.5's worked example):
 * Paging: "permuted" = one seeded permutation of every physical block id;
   "interleaved" = sequences allocate blocks in lockstep, one block per
   sequence per round, so consecutive blocks of a sequence are far apart.
+* Room to grow (append tests): ``extra_tokens`` widens the block table by that
+  many tokens per sequence and ``spare_blocks`` adds unused physical blocks,
+  returned as a free stack (``free_blocks``, top = last entry).
 
 Large random tensors are drawn with a torch.Generator on the target device;
 integer structure (lengths, tables, planted choices) with numpy from the same
@@ -153,8 +156,10 @@ def make_structure(cfg: dict, seed: int, seq_lens=None):
             s += ln
         ptr.append(len(starts))
     nblk = [(int(t) + BLOCK_SIZE - 1) // BLOCK_SIZE for t in seq_lens]
-    max_blocks = max(1, max(nblk))
-    num_blocks = max(1, sum(nblk))
+    extra = int(cfg.get("extra_tokens", 0))
+    spare = int(cfg.get("spare_blocks", 0))
+    max_blocks = max(1, max((int(t) + extra + BLOCK_SIZE - 1) // BLOCK_SIZE for t in seq_lens))
+    num_blocks = max(1, sum(nblk) + spare)
     table = np.full((B, max_blocks), -1, dtype=np.int32)
     if cfg["paging"] == "permuted":
         perm = rng.permutation(num_blocks).astype(np.int32)
@@ -162,6 +167,7 @@ def make_structure(cfg: dict, seed: int, seq_lens=None):
         for b in range(B):
             table[b, :nblk[b]] = perm[pos:pos + nblk[b]]
             pos += nblk[b]
+        free_blocks = perm[pos:].copy()
     elif cfg["paging"] == "interleaved":
         nxt = 0
         for j in range(max_blocks):
@@ -169,8 +175,11 @@ def make_structure(cfg: dict, seed: int, seq_lens=None):
                 if j < nblk[b]:
                     table[b, j] = nxt
                     nxt += 1
+        free_blocks = np.arange(nxt, num_blocks, dtype=np.int32)
     else:
         raise ValueError(cfg["paging"])
+    if spare == 0:
+        free_blocks = np.zeros(0, dtype=np.int32)
     n_pl = cfg["planted"]
     planted = np.full((B, cfg["Hkv"], n_pl), -1, dtype=np.int32)
     for b in range(B):
@@ -180,6 +189,7 @@ def make_structure(cfg: dict, seed: int, seq_lens=None):
                 m = min(n_pl, n_b)
                 planted[b, g, :m] = np.sort(rng.choice(n_b, size=m, replace=False))
     return dict(seq_lens=seq_lens, block_table=table, num_blocks=num_blocks,
+                free_blocks=free_blocks.astype(np.int32),
                 seq_ptr=np.array(ptr, dtype=np.int32),
                 th_start=np.array(starts, dtype=np.int32),
                 th_len=np.array(lens, dtype=np.int32), planted=planted)
@@ -253,7 +263,7 @@ def make_workload(cfg_id, seed=None, device="cpu", overrides=None, seq_lens=None
                     block_table=st["block_table"], num_blocks=st["num_blocks"],
                     seq_ptr=st["seq_ptr"], th_start=st["th_start"], th_len=st["th_len"],
                     planted=st["planted"], k_pool=k_pool, v_pool=v_pool, summary_keys=kbar,
-                    q=q, extra={"cfg": cfg})
+                    q=q, extra={"cfg": cfg, "free_blocks": st["free_blocks"]})
 
 
 def to_numpy_f32(t: torch.Tensor) -> np.ndarray:

@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(PKG, "libzr.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "zr.h")
 
 ZR_OK, ZR_E_NULL, ZR_E_SHAPE, ZR_E_UNSUPPORTED, ZR_E_WORKSPACE, ZR_E_LAUNCH, ZR_E_ALIGN = range(7)
+ZR_APPEND_OK, ZR_APPEND_NO_FREE_BLOCK, ZR_APPEND_TABLE_FULL, ZR_APPEND_BAD_BLOCK = range(4)
 ZR_F32, ZR_BF16 = 0, 1
 DTYPE_CODE = {torch.float32: ZR_F32, torch.bfloat16: ZR_BF16}
 
@@ -58,6 +59,8 @@ _SIGS = {
     "zr_sparse_decode_attn_cached": (ctypes.c_int, [_G, _P, _P, _P, _P, _P, ctypes.c_int32,
                                                     ctypes.c_float, ctypes.c_int32, _P, _P,
                                                     ctypes.c_size_t, _P]),
+    "zr_append_kv": (ctypes.c_int, [_G, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "zr_summary_keys": (ctypes.c_int, [_G, _P, _P, _T, _P, ctypes.c_int32, _P, _P]),
     "zr_dense_paged_decode_attn": (ctypes.c_int, [_G, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P,
                                                   ctypes.c_size_t, _P]),
     "zr_workspace_bytes": (ctypes.c_size_t, [_G, ctypes.c_int32]),
@@ -129,6 +132,18 @@ def zr_sparse_decode_attn_cached(geom, q, k_pool, v_pool, block_table, seq_lens,
                                               seq_lens, int(window), float(scale),
                                               int(max_attended), out, workspace, int(ws_bytes),
                                               stream)
+
+
+def zr_append_kv(geom, k_pool, v_pool, block_table, seq_lens, k_new, v_new, free_blocks,
+                 free_count, status, stream=None) -> int:
+    return lib().zr_append_kv(ctypes.byref(geom), k_pool, v_pool, block_table, seq_lens, k_new,
+                              v_new, free_blocks, free_count, status, stream)
+
+
+def zr_summary_keys(geom, k_pool, block_table, th, which, n_which, summary_keys,
+                    stream=None) -> int:
+    return lib().zr_summary_keys(ctypes.byref(geom), k_pool, block_table, ctypes.byref(th),
+                                 which, int(n_which), summary_keys, stream)
 
 
 def zr_dense_paged_decode_attn(geom, q, k_pool, v_pool, block_table, seq_lens, scale, out,
@@ -222,6 +237,22 @@ class DeviceStep:
             self.geom, _ptr(q), _ptr(self.k_pool), _ptr(self.v_pool), _ptr(self.block_table),
             _ptr(seq_lens), int(window), self.scale, self.max_attended, _ptr(out),
             _ptr(self.workspace), self.workspace.numel(), _stream()))
+
+    def append(self, k_new, v_new, free_blocks, free_count, status):
+        """Append one token per sequence (zr_append_kv); updates this step's
+        block table and sequence lengths in place."""
+        check("zr_append_kv", zr_append_kv(
+            self.geom, _ptr(self.k_pool), _ptr(self.v_pool), _ptr(self.block_table),
+            _ptr(self.seq_lens), _ptr(k_new.contiguous()), _ptr(v_new.contiguous()),
+            _ptr(free_blocks), _ptr(free_count), _ptr(status), _stream()))
+
+    def compute_summary_keys(self, which, out=None):
+        """Mean summary keys of the thoughts `which` (zr_summary_keys), written
+        into `out` (default: this step's summary keys)."""
+        out = self.summary_keys if out is None else out
+        check("zr_summary_keys", zr_summary_keys(
+            self.geom, _ptr(self.k_pool), _ptr(self.block_table), self.th, _ptr(which),
+            which.numel(), _ptr(out), _stream()))
 
     def dense_attn(self, out=None):
         out = self.out if out is None else out

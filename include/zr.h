@@ -22,6 +22,9 @@
  *   Sec. 3.4 and Appendix A.3; Algorithm 1 rebuilds it at boundaries only).
  *   zr_dense_paged_decode_attn is the dense baseline: attention over every
  *   cached token through the same block table (same page, eq. 4).
+ *   zr_append_kv and zr_summary_keys are the append path that precedes a
+ *   step: the new token's K/V into the paged cache (with on-demand block
+ *   allocation) and the mean summary key of a thought once it is complete.
  *
  * Conventions shared by every entry point
  *   - All array arguments are DEVICE pointers (memory of the current HIP
@@ -92,6 +95,12 @@ typedef enum { ZR_F32 = 0, ZR_BF16 = 1 } zr_dtype;
 #define ZR_MAX_K 1024                 /* k of zr_select_topk / zr_sparse_decode_attn */
 #define ZR_MAX_THOUGHTS_PER_SEQ 8192  /* zr_thoughts.max_per_seq */
 #define ZR_MAX_PAIRS 4096             /* batch * n_kv_heads of the attention and step calls */
+
+/* Per-sequence results of zr_append_kv. */
+#define ZR_APPEND_OK 0              /* token appended, seq_lens[b] grew by one */
+#define ZR_APPEND_NO_FREE_BLOCK 1   /* a new block was needed and the free stack was empty */
+#define ZR_APPEND_TABLE_FULL 2      /* block_table[b] has no column for the token */
+#define ZR_APPEND_BAD_BLOCK 3       /* a block id outside [0, num_blocks) was met */
 
 typedef struct {
   int32_t batch;              /* B >= 0 (B = 0: every call is a no-op) */
@@ -223,6 +232,51 @@ zr_status zr_dense_paged_decode_attn(const zr_geom* geom, const void* q, const v
                                      const void* v_pool, const int32_t* block_table,
                                      const int32_t* seq_lens, float scale, float* out,
                                      void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Append one decode token per sequence to the paged cache (ZoomR Algorithm 1:
+ * the new k_t, v_t enter the cache before scoring; KV-cache management page,
+ * paged KV cache: a block is allocated on demand, only when the sequence's
+ * last block is full). For every sequence b with T = seq_lens[b]:
+ *   - if T % 16 == 0, pop the top of the free stack (free_blocks[*free_count
+ *     - 1], then *free_count decreases) into block_table[b][T / 16];
+ *   - write k_new[b][g][:] to key slot T % 16 and v_new[b][g][:] to value
+ *     slot T % 16 of block block_table[b][T / 16], every KV head g;
+ *   - seq_lens[b] = T + 1; status[b] = ZR_APPEND_OK.
+ * On ZR_APPEND_NO_FREE_BLOCK / TABLE_FULL / BAD_BLOCK nothing of sequence b
+ * changes (a BAD_BLOCK pop still consumes the stack entry). When several
+ * sequences need a block in one call, which of the popped blocks each gets
+ * is unspecified (they pop concurrently); each popped block goes to exactly
+ * one sequence. Blocks are returned to the stack by the caller (writing
+ * free_blocks and *free_count between calls).
+ * Layouts: k_new, v_new [batch][n_kv_heads][head_dim] dtype (16-byte
+ * aligned, like the pools); free_blocks [capacity] int32; free_count [1]
+ * int32; status [batch] int32; block_table and seq_lens are updated in place.
+ * Errors: ZR_E_NULL, ZR_E_SHAPE, ZR_E_UNSUPPORTED, ZR_E_ALIGN, ZR_E_LAUNCH.
+ */
+zr_status zr_append_kv(const zr_geom* geom, void* k_pool, void* v_pool, int32_t* block_table,
+                       int32_t* seq_lens, const void* k_new, const void* v_new,
+                       const int32_t* free_blocks, int32_t* free_count, int32_t* status,
+                       void* stream);
+
+/*
+ * Mean summary keys of completed thoughts (ZoomR, Sec. 3.3, eq. for the mean
+ * summary key; computed over the thought's own cached keys). For every
+ * w < n_which, i = which[w] (a global thought index of `th`), b its sequence
+ * and every KV head g:
+ *   summary_keys[i][g][:] = mean over j in [start_i, start_i + len_i) of the
+ *                           cached key K[b][g][j]
+ * summed in float64, divided once, rounded to float32 and then, for bf16
+ * caches, to bf16 (nearest even). Reads k_pool through block_table; writes
+ * only the rows `which` of summary_keys ([n_total][n_kv_heads][head_dim]
+ * dtype, 16-byte aligned; th->summary_keys is not read). An index outside
+ * [0, n_total) is skipped.
+ * Errors: ZR_E_NULL, ZR_E_SHAPE (n_which < 0), ZR_E_UNSUPPORTED, ZR_E_ALIGN,
+ * ZR_E_LAUNCH.
+ */
+zr_status zr_summary_keys(const zr_geom* geom, const void* k_pool, const int32_t* block_table,
+                          const zr_thoughts* th, const int32_t* which, int32_t n_which,
+                          void* summary_keys, void* stream);
 
 /* Workspace bytes the attention calls need for a grid sized for
  * `max_attended` tokens per (sequence, KV head): per-(b, g) block lists

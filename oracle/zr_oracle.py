@@ -31,6 +31,19 @@ which convert to float64 exactly):
 5. ``attend``          - softmax(q K^T * scale) V over exactly those tokens
    (ZoomR, Sec. 2, eq. for A), two passes: max, then exp / sum / weighted V.
 
+The append path (before a step's attention):
+
+6. ``append_kv``       - write one new token's key and value per sequence
+   into its paged cache, taking a fresh physical block from a free stack
+   when the last block is full or the sequence has none (KV-cache
+   management page, "Paged KV cache (PagedAttention)": allocation on demand,
+   a new block only when the last one fills; ZoomR Algorithm 1, the append
+   of k_t and v_t before scoring).
+7. ``summary_keys``    - mean key of a completed thought per KV head
+   (ZoomR, Sec. 3.3, eq. for the mean summary key; here the mean runs over
+   the thought's own cached keys, reading R11), float64, rounded to float32
+   and then to the cache dtype (bf16: round to nearest even).
+
 Accounting helpers pinned to printed figures:
 ``memory_savings`` (ZoomR, Sec. 3.5, eq. MS) and ``dense_kv_bytes`` (the
 dense-cache sizing formula on the KV-cache management page, "Sizing the dense
@@ -256,6 +269,78 @@ def dense_decode_step(q, k_pool, v_pool, block_table, seq_lens, scale, pairs=Non
 # --------------------------------------------------------------------------
 # Accounting
 # --------------------------------------------------------------------------
+# --------------------------------------------------------------------------
+# 6-7. Append path
+# --------------------------------------------------------------------------
+APPEND_OK, APPEND_NO_FREE_BLOCK, APPEND_TABLE_FULL = 0, 1, 2
+
+
+def append_kv(k_pool, v_pool, block_table, seq_lens, k_new, v_new, free_blocks, free_count):
+    """Append token T_b = seq_lens[b] of every sequence b, in order b = 0, 1, ...
+
+    Before the write, a sequence whose cached length is a multiple of 16 (its
+    last block is full, or it has none) pops the top of the free stack
+    ``free_blocks[:free_count]`` into block_table[b][T_b // 16] (allocation
+    on demand, KV-cache management page, paged KV cache). Then key row
+    k_new[b][g] goes to k_pool[block][g][T_b % 16] and value v_new[b][g] to
+    v_pool[block][g][:, T_b % 16] (dimension-major values), and seq_lens[b]
+    grows by one. A sequence that needs a block when the stack is empty gets
+    status 1, one whose table has no column left status 2; nothing of it
+    changes. Works on copies; returns (k_pool, v_pool, block_table, seq_lens,
+    free_count, status).
+    """
+    k_pool = np.array(k_pool, copy=True)
+    v_pool = np.array(v_pool, copy=True)
+    table = np.array(block_table, copy=True)
+    lens = np.array(seq_lens, copy=True)
+    status = np.zeros(len(lens), dtype=np.int32)
+    top = int(free_count)
+    for b in range(len(lens)):
+        T = int(lens[b])
+        col = T // BLOCK_SIZE
+        if col >= table.shape[1]:
+            status[b] = APPEND_TABLE_FULL
+            continue
+        if T % BLOCK_SIZE == 0:
+            if top == 0:
+                status[b] = APPEND_NO_FREE_BLOCK
+                continue
+            top -= 1
+            table[b, col] = free_blocks[top]
+        blk, slot = int(table[b, col]), T % BLOCK_SIZE
+        k_pool[blk, :, slot, :] = k_new[b]
+        v_pool[blk, :, :, slot] = v_new[b]
+        lens[b] = T + 1
+    return k_pool, v_pool, table, lens, top, status
+
+
+def _round_bf16(x32: np.ndarray) -> np.ndarray:
+    """float32 -> nearest bfloat16 (ties to even), returned as float32."""
+    u = np.asarray(x32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32)
+
+
+def summary_keys(k_pool, block_table, seq_ptr, starts, lens, which, dtype):
+    """Mean summary key of each thought in ``which`` (global indices): for
+    every KV head g, the mean of the thought's cached keys K[b, g, j] over
+    j in [start, start + len) (ZoomR, Sec. 3.3, eq. for the mean summary key,
+    over the thought's own keys: reading R11). float64 mean, rounded to
+    float32, then to ``dtype`` ("bf16": nearest even). Returns
+    float32 [len(which)][Hkv][d] holding the rounded values."""
+    seq_ptr = np.asarray(seq_ptr)
+    out = []
+    for i in which:
+        i = int(i)
+        b = int(np.searchsorted(seq_ptr, i, side="right") - 1)
+        s, n = int(starts[i]), int(lens[i])
+        rows = gather_keys(k_pool, block_table[b], s + n)[s:s + n]
+        m = rows.mean(axis=0).astype(np.float32)
+        out.append(_round_bf16(m) if dtype == "bf16" else m)
+    return np.array(out, dtype=np.float32).reshape(len(out), *np.asarray(k_pool).shape[1:2],
+                                                   np.asarray(k_pool).shape[3])
+
+
 def memory_savings(n_prompt, n_gen, n_window, c, len_regular, len_summary, n_all):
     """ZoomR Sec. 3.5, eq. MS: full-cache tokens over the tokens the selection
     keeps (prompt + c full segments + the other candidates' summaries + window)."""

@@ -24,8 +24,8 @@ def test_exports_every_declared_symbol(L):
     declared = zr.header_symbols()
     assert declared == sorted(["zr_coarse_score", "zr_select_topk", "zr_sparse_decode_attn",
                                "zr_sparse_decode_attn_cached", "zr_sparse_decode_step",
-                               "zr_dense_paged_decode_attn", "zr_workspace_bytes",
-                               "zr_status_string"])
+                               "zr_dense_paged_decode_attn", "zr_append_kv", "zr_summary_keys",
+                               "zr_workspace_bytes", "zr_status_string"])
     out = subprocess.run(["nm", "-D", "--defined-only", zr.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = sorted(l.split()[-1] for l in out.splitlines() if l.split()[-2] == "T")
@@ -158,3 +158,23 @@ def test_cached_errors(L):
     assert c(q=FAKE + 2) == zr.ZR_E_ALIGN
     assert c(workspace=None) == zr.ZR_E_WORKSPACE
     assert c(scale=float("inf")) == zr.ZR_E_SHAPE
+
+
+def test_append_and_summary_errors(L):
+    g = _geom()
+    ap = lambda **kw: zr.zr_append_kv(**dict(dict(
+        geom=g, k_pool=FAKE, v_pool=FAKE, block_table=FAKE, seq_lens=FAKE, k_new=FAKE,
+        v_new=FAKE, free_blocks=FAKE, free_count=FAKE, status=FAKE), **kw))
+    assert ap(free_count=None) == zr.ZR_E_NULL
+    assert ap(status=None) == zr.ZR_E_NULL
+    assert ap(k_new=FAKE + 2) == zr.ZR_E_ALIGN
+    assert ap(geom=_geom(head_dim=96)) == zr.ZR_E_UNSUPPORTED
+    assert ap(geom=_geom(batch=0), k_pool=None) == zr.ZR_OK  # nothing to do
+    sk = lambda **kw: zr.zr_summary_keys(**dict(dict(
+        geom=g, k_pool=FAKE, block_table=FAKE, th=_th(), which=FAKE, n_which=3,
+        summary_keys=FAKE), **kw))
+    assert sk(n_which=-1) == zr.ZR_E_SHAPE
+    assert sk(which=None) == zr.ZR_E_NULL
+    assert sk(summary_keys=FAKE + 8) == zr.ZR_E_ALIGN
+    assert sk(th=_th(len=None)) == zr.ZR_E_NULL
+    assert sk(n_which=0, which=None) == zr.ZR_OK

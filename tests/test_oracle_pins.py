@@ -317,3 +317,110 @@ def test_sparse_step_equals_masked_sdpa(seed):
                        for i in range(len(starts))])
         best = sorted(range(len(sc)), key=lambda i: (-sc[i], i))[:k]
         assert sorted(best) == chosen
+
+
+# --------------------------------------------------------------------------
+# Append path: append_kv and summary_keys
+# --------------------------------------------------------------------------
+def test_round_bf16_matches_torch():
+    """float32 -> bf16 nearest-even, against torch's conversion (a library
+    routine), on random values, exact halfway cases and both signs."""
+    import torch
+    rng = np.random.default_rng(3)
+    x = np.concatenate([rng.normal(size=4000).astype(np.float32) * 10,
+                        np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -1.0 - 2.0 ** -8,
+                                  0.0, -0.0, 65504.0], np.float32)])
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    assert np.array_equal(O._round_bf16(x).view(np.uint32), ref.view(np.uint32))
+
+
+def _tiny_cache(n_blocks=12, Hkv=2, d=4, seed=0):
+    rng = np.random.default_rng(seed)
+    k = rng.normal(size=(n_blocks, Hkv, 16, d)).astype(np.float32)
+    v = rng.normal(size=(n_blocks, Hkv, d, 16)).astype(np.float32)
+    return k, v
+
+
+def test_append_builds_the_logical_sequence():
+    """Appending tokens one by one to sequences of lengths 0, 5, 16 and 31
+    gives, read back through the table, the old tokens followed by the new
+    ones in order; blocks are taken from the top of the stack only when a
+    length is a multiple of 16."""
+    k, v = _tiny_cache(n_blocks=16)
+    lens0 = np.array([0, 5, 16, 31], np.int32)
+    table = np.full((4, 5), -1, np.int32)
+    table[1, 0] = 0
+    table[2, 0] = 1
+    table[3, :2] = [2, 3]
+    free = np.arange(15, 3, -1, dtype=np.int32)  # top = last entry (4)
+    top = len(free)
+    old = [O.gather_keys(k, table[b], int(lens0[b])) for b in range(4)]
+    rng = np.random.default_rng(9)
+    new_k = rng.normal(size=(20, 4, 2, 4)).astype(np.float32)
+    new_v = rng.normal(size=(20, 4, 2, 4)).astype(np.float32)
+    lens = lens0
+    pops = 0
+    for step in range(20):
+        need = int(np.sum(lens % 16 == 0))
+        k, v, table, lens, top2, st = O.append_kv(k, v, table, lens, new_k[step], new_v[step],
+                                                  free, top)
+        assert np.all(st == 0)
+        assert top2 == top - need
+        pops += need
+        top = top2
+    assert np.array_equal(lens, lens0 + 20)
+    for b in range(4):
+        got_k = O.gather_keys(k, table[b], int(lens[b]))
+        got_v = O.gather_values(v, table[b], int(lens[b]))
+        assert np.array_equal(got_k[:lens0[b]], old[b])
+        assert np.array_equal(got_k[lens0[b]:], new_k[:, b].astype(np.float64))
+        assert np.array_equal(got_v[lens0[b]:], new_v[:, b].astype(np.float64))
+    # blocks 0..3 were in use; the pops took the stack's top entries in order
+    used = set(table[table >= 0].tolist())
+    assert used == set(range(4)) | set(free[len(free) - pops:].tolist())
+    # ceil((T + 20) / 16) - ceil(T / 16) new blocks per sequence: 2 + 1 + 2 + 2
+    assert pops == 7
+
+
+def test_append_failures_change_nothing():
+    k, v = _tiny_cache(n_blocks=4)
+    table = np.array([[0, -1], [1, 2]], np.int32)
+    lens = np.array([16, 32], np.int32)          # both need a block; sequence 1's table is full
+    kn = np.ones((2, 2, 4), np.float32)
+    free = np.array([3], np.int32)
+    k2, v2, t2, l2, top, st = O.append_kv(k, v, table, lens, kn, kn, free, 0)  # empty stack
+    assert list(st) == [O.APPEND_NO_FREE_BLOCK, O.APPEND_TABLE_FULL]
+    assert np.array_equal(k2, k) and np.array_equal(t2, table) and np.array_equal(l2, lens)
+    k2, v2, t2, l2, top, st = O.append_kv(k, v, table, lens, kn, kn, free, 1)
+    assert list(st) == [0, O.APPEND_TABLE_FULL] and top == 0 and t2[0, 1] == 3
+    assert list(l2) == [17, 32]
+
+
+def test_summary_keys_closed_forms():
+    """Constant keys average to the constant; keys equal to the token index
+    average to start + (len - 1) / 2; a one-token thought returns its key;
+    the result does not depend on where the blocks sit in the pool."""
+    n_blocks, Hkv, d = 8, 2, 4
+    table = np.array([[5, 2, 7, 0], [1, 3, 4, 6]], np.int32)
+    seq_ptr = np.array([0, 3, 5], np.int32)
+    starts = np.array([0, 10, 40, 0, 63], np.int32)
+    lens = np.array([10, 30, 1, 63, 1], np.int32)
+    k = np.zeros((n_blocks, Hkv, 16, d), np.float32)
+    for b in range(2):
+        for j in range(64):
+            k[table[b, j // 16], :, j % 16, :] = j
+    got = O.summary_keys(k, table, seq_ptr, starts, lens, range(5), "f32")
+    want = starts + (lens - 1) / 2.0
+    assert np.array_equal(got, np.broadcast_to(want[:, None, None], got.shape).astype(np.float32))
+    k.fill(0.375)
+    assert np.all(O.summary_keys(k, table, seq_ptr, starts, lens, [1, 3], "bf16") == 0.375)
+    rng = np.random.default_rng(1)
+    k = rng.normal(size=k.shape).astype(np.float32)
+    one = O.summary_keys(k, table, seq_ptr, starts, lens, [2], "f32")
+    assert np.array_equal(one[0], k[table[0, 40 // 16], :, 40 % 16, :])
+    perm = rng.permutation(n_blocks)
+    k2 = np.empty_like(k)
+    k2[perm] = k
+    a = O.summary_keys(k, table, seq_ptr, starts, lens, range(5), "bf16")
+    b = O.summary_keys(k2, perm[table], seq_ptr, starts, lens, range(5), "bf16")
+    assert np.array_equal(a, b)
