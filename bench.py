@@ -85,6 +85,8 @@ def main():
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-zoom", action="store_true",
+                    help="skip the multi-granularity (consensus) figure")
     ap.add_argument("--period", type=int, default=35,
                     help="decode steps per semantic boundary for the selection-reuse figure")
     ap.add_argument("--copy-calibrate", action="store_true",
@@ -219,6 +221,66 @@ def main():
     g_sum = capture(lambda i: steps[i % L].compute_summary_keys(which, out=kb_out), args.steps)
     summary_us = timed(g_sum, args.steps)
 
+    # ZoomR's multi-granularity set (Sec. 3.3): per-layer scores and top-k,
+    # votes over all layers and KV heads, the consensus set, and each layer's
+    # attention over prompt + window + consensus thoughts + other summaries,
+    # on L layer caches with the worked example's layout (Sec. 3.5)
+    zoom = None
+    if not args.no_zoom:
+        zl = [synth.make_workload(5, value_seed=2000 + l, device=dev) for l in range(L)]
+        wz = zl[0]
+        zs = [zr.step_from_workload(w) for w in zl]
+        cz, npz = wz.extra["c"], wz.extra["prompt"]
+        ss = torch.as_tensor(wz.extra["sum_start"], device=dev)
+        sl = torch.as_tensor(wz.extra["sum_len"], device=dev)
+        votes = torch.empty(wz.n_total, dtype=torch.int32, device=dev)
+        cons = torch.empty((wz.B, cz), dtype=torch.int32, device=dev)
+        agree = torch.empty(wz.B, dtype=torch.float32, device=dev)
+        sel_stack = torch.empty((L,) + tuple(zs[0].sel.shape), dtype=torch.int32, device=dev)
+
+        def boundary(_):
+            for l, st in enumerate(zs):
+                st.coarse_score()
+                st.select_topk()
+                sel_stack[l].copy_(st.sel)
+            zs[0].consensus(sel_stack, cz, votes, cons, agree)
+            for st in zs:
+                st.zoom_attn(ss, sl, votes, cons, cz, npz)
+
+        g_bound = capture(boundary, 1)
+        g_bound.replay()
+        torch.cuda.synchronize()
+        bound_us = timed(g_bound, L)
+        g_between = capture(lambda i: zs[i % L].cached_attn(wz.window), args.steps)
+        between_us = timed(g_between, args.steps)
+        v_h, c_h = votes.cpu().numpy(), cons.cpu().numpy()
+        n_att = []
+        for b in range(wz.B):
+            lo, hi = int(wz.seq_ptr[b]), int(wz.seq_ptr[b + 1])
+            cset = set(int(x) for x in c_h[b] if x >= 0)
+            T = int(wz.seq_lens[b])
+            toks = np.zeros(T, bool)
+            toks[:min(npz, T)] = True
+            toks[max(0, T - wz.window):] = True
+            for i in range(hi - lo):
+                if v_h[lo + i] > 0:
+                    s0 = int(wz.th_start[lo + i] if i in cset else wz.extra["sum_start"][lo + i])
+                    ln = int(wz.th_len[lo + i] if i in cset else wz.extra["sum_len"][lo + i])
+                    toks[s0:s0 + ln] = True
+            n_att.append(int(toks.sum()))
+        zbytes = int(sum(n_att)) * wz.Hkv * 2 * d * s_bytes
+        zoom = {"workload": "zoomr-16k-b8: batch 8, 32/8 heads, d 128, 16384 tokens = 512 prompt "
+                            "+ regular U[100,400] / summary U[10,30] segments, top-8 per head, "
+                            "c 2, window 512, bf16",
+                "layers": L, "votes_per_thought_max": int(v_h.max()),
+                "thoughts_voted": int((v_h > 0).sum()), "thoughts": int(wz.n_total),
+                "attended_tokens_per_seq": round(float(np.mean(n_att)), 1),
+                "kv_reduction": round(float(wz.seq_lens.sum()) / float(sum(n_att)), 3),
+                "agreement_mean": round(float(agree.mean().item()), 4),
+                "boundary_us_per_layer": round(bound_us, 3),
+                "between_us_per_layer": round(between_us, 3),
+                "between_gbs": round(zbytes / (between_us * 1e-6) / 1e9, 1)}
+
     # dense baseline (same caches, every token) for context
     dense_us = timed(g_dense, L)
     dense_bytes = int(w0.seq_lens.sum()) * w0.Hkv * 2 * d * s_bytes
@@ -262,6 +324,7 @@ def main():
         "selection_reuse": {"period_steps": R, "us_per_step": round(period_us, 3),
                             "steps_per_s": round(1e6 / period_us, 1)},
         "speedup_vs_dense_attention": round(dense_us / attn_us, 3),
+        "zoomr_consensus": zoom,
         "append_path": {"append_kv_us": round(append_us, 3),
                         "summary_keys_us": round(summary_us, 3),
                         "summary_thoughts_per_call": int(w0.B),

@@ -305,6 +305,73 @@ ZR_API zr_status zr_summary_keys(const zr_geom* geom, const void* k_pool,
   return ZR_OK;
 }
 
+ZR_API zr_status zr_consensus(const zr_geom* geom, const zr_thoughts* th, const int32_t* sel,
+                              int32_t n_layers, int32_t k, int32_t c, int32_t* votes,
+                              int32_t* cons, float* agree, void* stream) {
+  zr_status st = check_geom(geom);
+  if (st != ZR_OK) return st;
+  st = check_thoughts(th, false);
+  if (st != ZR_OK) return st;
+  if (n_layers < 0 || k < 0 || k > ZR_MAX_K || c < 0 || c > ZR_MAX_K) return ZR_E_SHAPE;
+  if (geom->batch == 0) return ZR_OK;
+  if (!votes || !agree || (c > 0 && !cons) || (n_layers > 0 && k > 0 && !sel))
+    return ZR_E_NULL;
+  if (!zr::consensus_lds_ok(th->max_per_seq, c)) return ZR_E_UNSUPPORTED;
+  zr::ConsArgs a{};
+  a.seq_ptr = th->seq_ptr;
+  a.sel = sel;
+  a.votes = votes;
+  a.cons = cons;
+  a.agree = agree;
+  a.B = geom->batch;
+  a.Hkv = geom->n_kv_heads;
+  a.k = (n_layers > 0 && sel) ? k : 0;
+  a.n_layers = n_layers;
+  a.c = c;
+  a.n_total = th->n_total;
+  a.max_per_seq = th->max_per_seq;
+  if (zr::launch_consensus(a, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return ZR_E_LAUNCH;
+  return ZR_OK;
+}
+
+ZR_API zr_status zr_zoom_decode_attn(const zr_geom* geom, const void* q, const void* k_pool,
+                                     const void* v_pool, const int32_t* block_table,
+                                     const int32_t* seq_lens, const zr_thoughts* th,
+                                     const int32_t* sum_start, const int32_t* sum_len,
+                                     const int32_t* votes, const int32_t* cons, int32_t c,
+                                     int32_t n_prompt, int32_t window, float scale,
+                                     int32_t max_attended, float* out, void* workspace,
+                                     size_t ws_bytes, void* stream) {
+  zr_status st = check_geom(geom);
+  if (st != ZR_OK) return st;
+  st = check_thoughts(th, false);
+  if (st != ZR_OK) return st;
+  if (c < 0 || c > ZR_MAX_K || n_prompt < 0 || window < 0) return ZR_E_SHAPE;
+  if (!sum_start || !sum_len || !votes || (c > 0 && !cons)) return ZR_E_NULL;
+  zr::AttnArgs a{};
+  st = attention_common(geom, q, k_pool, v_pool, block_table, seq_lens, scale, out, workspace,
+                        ws_bytes, max_attended, &a);
+  if (st != ZR_OK) return st;
+  if (!zr::zoom_lds_ok(*geom, th->max_per_seq)) return ZR_E_UNSUPPORTED;
+  zr::PairArgs pa{};
+  pa.seq_ptr = th->seq_ptr;
+  pa.th_start = th->start;
+  pa.th_len = th->len;
+  pa.sum_start = sum_start;
+  pa.sum_len = sum_len;
+  pa.votes = votes;
+  pa.cons = cons;
+  pa.c = c;
+  pa.n_prompt = n_prompt;
+  fill_plan(*geom, *th, 0, window, block_table, seq_lens, a, &pa);
+  a.window = window;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (zr::launch_zoom_plan(*geom, pa, s) != hipSuccess) return ZR_E_LAUNCH;
+  if (zr::launch_attention(*geom, a, false, s) != hipSuccess) return ZR_E_LAUNCH;
+  return ZR_OK;
+}
+
 ZR_API zr_status zr_dense_paged_decode_attn(const zr_geom* geom, const void* q,
                                             const void* k_pool, const void* v_pool,
                                             const int32_t* block_table, const int32_t* seq_lens,

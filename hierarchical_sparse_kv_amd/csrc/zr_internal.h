@@ -133,6 +133,22 @@ struct PairArgs {
   int32_t n_total, max_per_seq, Hq, Hkv, k, window, max_blocks, num_blocks;
   int32_t bt_per;             // block-table entries per thread: ceil(max_blocks / 256)
   int32_t stage_th;           // 1: thought spans staged in LDS
+  // multi-granularity plan (zoom): votes, consensus set, summary spans, prompt
+  const int32_t* votes;       // [n_total]
+  const int32_t* cons;        // [B][c]
+  const int32_t* sum_start;   // [n_total]
+  const int32_t* sum_len;     // [n_total]
+  int32_t c, n_prompt;
+};
+
+// Votes, consensus set and agreement of every sequence (zr_pair.hip).
+struct ConsArgs {
+  const int32_t* seq_ptr;
+  const int32_t* sel;         // [n_layers][B][Hkv][k]
+  int32_t* votes;             // [n_total]
+  int32_t* cons;              // [B][c]
+  float* agree;               // [B]
+  int32_t B, Hkv, k, n_layers, c, n_total, max_per_seq;
 };
 
 // Attention launch parameters (device pointers + sizes), passed by value.
@@ -191,6 +207,11 @@ hipError_t launch_summary_keys(const zr_geom& g, const SummaryArgs& a, int n_whi
 hipError_t launch_pair(const zr_geom& g, const PairArgs& a, int mode, hipStream_t s);
 // Whether the pair kernel's LDS fits (with nothing optional staged).
 bool pair_lds_ok(const zr_geom& g, int max_per_seq, int k, bool select, bool plan);
+hipError_t launch_consensus(const ConsArgs& a, hipStream_t s);
+bool consensus_lds_ok(int max_per_seq, int c);
+// Block lists of the multi-granularity set (same list for every KV head).
+hipError_t launch_zoom_plan(const zr_geom& g, const PairArgs& a, hipStream_t s);
+bool zoom_lds_ok(const zr_geom& g, int max_per_seq);
 // Workgroups of the attention kernel for a bound of `max_attended` tokens per
 // (sequence, KV head); the workspace layout depends on it.
 int attn_workgroups(const zr_geom& g, int32_t max_attended);

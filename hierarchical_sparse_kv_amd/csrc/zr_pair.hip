@@ -270,6 +270,70 @@ __device__ void select_by_radix(const PairLds& L, int n, int k, int32_t* out, ui
 }
 
 // ---------------------------------------------------------------------------
+// Block lists from a slot bitmap
+// ---------------------------------------------------------------------------
+
+// OR the slots of tokens [s, e) into the bitmap, blocks j0, j0 + step, ...
+// of the span (so a workgroup can share one span's blocks).
+__device__ __forceinline__ void or_span(uint32_t* bmask, int s, int e, int j0, int step) {
+  const int nbk = blocks_of_span(s, e);
+  for (int j = j0; j < nbk; j += step) {
+    const int lb = (s >> 4) + j;
+    const int b0 = lb << 4;
+    const int from = (s > b0 ? s : b0) - b0;
+    const int to = (e < b0 + kBlock ? e : b0 + kBlock) - b0;
+    const uint32_t m = ((1u << to) - 1u) & ~((1u << from) - 1u);
+    atomicOr(&bmask[lb >> 1], m << (16 * (lb & 1)));
+  }
+}
+
+// The non-empty blocks of the bitmap in logical order -> the pair's list of
+// (physical block, slot mask) entries and its length. Block ids come from
+// the registers prefetched at kernel start (bt_pref) or from the table.
+// Contains barriers: every thread must call it.
+__device__ void emit_list(const PairArgs& a, const PairLds& L, int p, int b, int nb,
+                          bool bt_pref, const int (&btr)[kBtRegs], int* wtmp) {
+  const int t = threadIdx.x;
+  const int bl0 = t * a.bt_per;
+  int nz = 0;
+  for (int j = 0; j < a.bt_per; ++j) {
+    const int lb = bl0 + j;
+    if (lb < nb) nz += ((L.bmask[lb >> 1] >> (16 * (lb & 1))) & 0xffffu) != 0u;
+  }
+  int n_list;
+  int pos = pair_exclusive_scan(nz, wtmp, &n_list);
+  int2* ent = a.entries + static_cast<size_t>(p) * a.max_blocks;
+  const int32_t* row = a.block_table + static_cast<size_t>(b) * a.max_blocks;
+  if (bt_pref) {
+#pragma unroll
+    for (int j = 0; j < kBtRegs; ++j) {
+      const int lb = bl0 + j;
+      if (j < a.bt_per && lb < nb) {
+        const uint32_t m = (L.bmask[lb >> 1] >> (16 * (lb & 1))) & 0xffffu;
+        if (m) {
+          const int pb = btr[j];
+          const bool ok = pb >= 0 && pb < a.num_blocks;
+          ent[pos++] = ok ? make_int2(pb, static_cast<int>(m)) : make_int2(0, 0);
+        }
+      }
+    }
+  } else {
+    for (int j = 0; j < a.bt_per; ++j) {
+      const int lb = bl0 + j;
+      if (lb < nb) {
+        const uint32_t m = (L.bmask[lb >> 1] >> (16 * (lb & 1))) & 0xffffu;
+        if (m) {
+          const int pb = row[lb];
+          const bool ok = pb >= 0 && pb < a.num_blocks;
+          ent[pos++] = ok ? make_int2(pb, static_cast<int>(m)) : make_int2(0, 0);
+        }
+      }
+    }
+  }
+  if (t == 0) a.counts[p] = n_list;
+}
+
+// ---------------------------------------------------------------------------
 // The pair kernel: one 256-thread workgroup per pair p = b * Hkv + g.
 // ---------------------------------------------------------------------------
 // STH: the thought spans are staged in LDS (a template flag, so that the
@@ -488,45 +552,155 @@ pair_kernel(PairArgs a) {
       atomicOr(&L.bmask[lb >> 1], m << (16 * (lb & 1)));
     }
     __syncthreads();
-    // non-empty blocks in logical order -> (physical block, slot mask)
-    const int bl0 = t * a.bt_per;
-    int nz = 0;
-    for (int j = 0; j < a.bt_per; ++j) {
-      const int lb = bl0 + j;
-      if (lb < nb) nz += ((L.bmask[lb >> 1] >> (16 * (lb & 1))) & 0xffffu) != 0u;
-    }
-    int n_list;
-    int pos = pair_exclusive_scan(nz, wtmp, &n_list);
-    int2* ent = a.entries + static_cast<size_t>(p) * a.max_blocks;
-    const int32_t* row = a.block_table + static_cast<size_t>(b) * a.max_blocks;
-    if (bt_pref) {
-#pragma unroll
-      for (int j = 0; j < kBtRegs; ++j) {
-        const int lb = bl0 + j;
-        if (j < a.bt_per && lb < nb) {
-          const uint32_t m = (L.bmask[lb >> 1] >> (16 * (lb & 1))) & 0xffffu;
-          if (m) {
-            const int pb = btr[j];
-            const bool ok = pb >= 0 && pb < a.num_blocks;
-            ent[pos++] = ok ? make_int2(pb, static_cast<int>(m)) : make_int2(0, 0);
-          }
-        }
-      }
-    } else {
-      for (int j = 0; j < a.bt_per; ++j) {
-        const int lb = bl0 + j;
-        if (lb < nb) {
-          const uint32_t m = (L.bmask[lb >> 1] >> (16 * (lb & 1))) & 0xffffu;
-          if (m) {
-            const int pb = row[lb];
-            const bool ok = pb >= 0 && pb < a.num_blocks;
-            ent[pos++] = ok ? make_int2(pb, static_cast<int>(m)) : make_int2(0, 0);
-          }
-        }
-      }
-    }
-    if (t == 0) a.counts[p] = n_list;
+    emit_list(a, L, p, b, nb, bt_pref, btr, wtmp);
   }
+}
+
+// ---------------------------------------------------------------------------
+// Consensus (ZoomR Sec. 3.3, "Global Aggregation and Consensus"): one
+// workgroup per sequence. Votes v_i = the number of (layer, KV head) top-k
+// rows holding thought i (LDS atomics; rows hold distinct indices, as the
+// selector writes them); the consensus set is the c thoughts with the most
+// votes among those with any, ties to the lower index, in ascending index;
+// agreement = votes of the consensus set over all votes (ZoomR Sec. 4).
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(kPairThreads)
+consensus_kernel(ConsArgs a) {
+  extern __shared__ __align__(16) int32_t dyn[];
+  __shared__ int wtmp[kPairWaves];
+  __shared__ uint32_t hist[kPairThreads];
+  __shared__ uint32_t sh[2];
+  __shared__ uint64_t comp[kPairThreads];
+  __shared__ int tot_tmp[kPairWaves];
+  const int b = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  PairLds L{};
+  L.keys = reinterpret_cast<uint32_t*>(dyn);
+  L.sel_l = dyn + up4(a.max_per_seq);
+  int lo = a.seq_ptr[b], hi = a.seq_ptr[b + 1];
+  lo = lo < 0 ? 0 : (lo > a.n_total ? a.n_total : lo);
+  hi = hi < lo ? lo : (hi > a.n_total ? a.n_total : hi);
+  const int n = hi - lo < a.max_per_seq ? hi - lo : a.max_per_seq;
+  for (int i = t; i < up4(n); i += kPairThreads) L.keys[i] = 0u;
+  __syncthreads();
+  const int rows = a.n_layers * a.Hkv;
+  for (int e = t; e < rows * a.k; e += kPairThreads) {
+    const int r = e / a.k, j = e - r * a.k;
+    const int l = r / a.Hkv, g = r - l * a.Hkv;
+    const int i = a.sel[((static_cast<size_t>(l) * a.B + b) * a.Hkv + g) * a.k + j];
+    if (i >= 0 && i < n) atomicAdd(&L.keys[i], 1u);
+  }
+  __syncthreads();
+  int mine = 0;
+  for (int i = t; i < n; i += kPairThreads) {
+    a.votes[lo + i] = static_cast<int32_t>(L.keys[i]);
+    mine += static_cast<int>(L.keys[i]);
+  }
+  const int wsum = wave_sum(mine);
+  if (lane == 0) tot_tmp[wave] = wsum;
+  int nsel = 0;
+  if (a.c > 0) {
+    if (n <= a.c) {
+      for (int j = t; j < n; j += kPairThreads) L.sel_l[j] = j;
+      nsel = n;
+    } else if (n <= kRankMax) {
+      select_by_rank<false>(L, n, a.c, L.sel_l, wtmp, comp);
+      nsel = a.c;
+    } else {
+      select_by_radix<false>(L, n, a.c, L.sel_l, hist, wtmp, sh);
+      nsel = a.c;
+    }
+  }
+  __syncthreads();
+  int total = 0;
+#pragma unroll
+  for (int v = 0; v < kPairWaves; ++v) total += tot_tmp[v];
+  // keep the chosen thoughts that have votes (thread t owns a contiguous run)
+  const int per = (nsel + kPairThreads - 1) / kPairThreads;
+  const int j0 = t * per, j1 = j0 + per < nsel ? j0 + per : nsel;
+  int keep = 0, kvotes = 0;
+  for (int j = j0; j < j1; ++j) {
+    const uint32_t v = L.keys[L.sel_l[j]];
+    keep += v > 0u;
+    kvotes += static_cast<int>(v);
+  }
+  int n_keep;
+  int pos = pair_exclusive_scan(keep, wtmp, &n_keep);
+  int32_t* out = a.cons + static_cast<size_t>(b) * a.c;
+  for (int j = j0; j < j1; ++j) {
+    const int i = L.sel_l[j];
+    if (L.keys[i] > 0u) out[pos++] = i;
+  }
+  for (int j = n_keep + t; j < a.c; j += kPairThreads) out[j] = -1;
+  int kv_all;
+  pair_exclusive_scan(kvotes, wtmp, &kv_all);
+  if (t == 0) a.agree[b] = total > 0 ? static_cast<float>(kv_all) / static_cast<float>(total) : 0.f;
+}
+
+// ---------------------------------------------------------------------------
+// Block lists of the multi-granularity set (ZoomR Sec. 3.3, "Constructing the
+// Final Multi-Granularity Context"): the prompt [0, N_p), the regular segment
+// R_i of every consensus thought and the summary segment S_i of every other
+// thought with a vote, clipped below the window start (the attention kernel
+// adds the window). One workgroup per (sequence, KV head); the list is the
+// same for every head of a sequence.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(kPairThreads)
+zoom_plan_kernel(PairArgs a) {
+  extern __shared__ __align__(16) int32_t dyn[];
+  __shared__ int wtmp[kPairWaves];
+  const int p = blockIdx.x, t = threadIdx.x;
+  const int b = p / a.Hkv;
+  int* flag = dyn;  // [up4(max_per_seq)]: 1 = consensus thought
+  PairLds L{};
+  L.bmask = reinterpret_cast<uint32_t*>(dyn + up4(a.max_per_seq));
+  int lo = a.seq_ptr[b], hi = a.seq_ptr[b + 1];
+  int T = a.seq_lens[b];
+  int btr[kBtRegs];
+  const bool bt_pref = a.bt_per <= kBtRegs;
+  if (bt_pref) {
+    const int32_t* row = a.block_table + static_cast<size_t>(b) * a.max_blocks;
+#pragma unroll
+    for (int j = 0; j < kBtRegs; ++j) {
+      const int lb = t * a.bt_per + j;
+      btr[j] = (j < a.bt_per && lb < a.max_blocks) ? row[lb] : 0;
+    }
+  }
+  lo = lo < 0 ? 0 : (lo > a.n_total ? a.n_total : lo);
+  hi = hi < lo ? lo : (hi > a.n_total ? a.n_total : hi);
+  const int n = hi - lo < a.max_per_seq ? hi - lo : a.max_per_seq;
+  const int cap = a.max_blocks * kBlock;
+  T = T < 0 ? 0 : (T > cap ? cap : T);
+  const int tw = T - a.window > 0 ? T - a.window : 0;
+  const int nb = (T + kBlock - 1) / kBlock;
+  for (int i = t; i < (nb + 1) / 2; i += kPairThreads) L.bmask[i] = 0u;
+  for (int i = t; i < n; i += kPairThreads) flag[i] = 0;
+  __syncthreads();
+  for (int j = t; j < a.c; j += kPairThreads) {
+    const int i = a.cons[static_cast<size_t>(b) * a.c + j];
+    if (i >= 0 && i < n) flag[i] = 1;
+  }
+  __syncthreads();
+  // prompt: its blocks shared by the whole workgroup
+  const int pe = a.n_prompt < tw ? a.n_prompt : tw;
+  if (pe > 0) or_span(L.bmask, 0, pe, t, kPairThreads);
+  // thoughts with votes: one thread per thought walks its segment's blocks
+  for (int i = t; i < n; i += kPairThreads) {
+    if (a.votes[lo + i] <= 0) continue;
+    int s, ln;
+    if (flag[i]) {
+      s = a.th_start[lo + i];
+      ln = a.th_len[lo + i];
+    } else {
+      s = a.sum_start[lo + i];
+      ln = a.sum_len[lo + i];
+    }
+    s = s > 0 ? s : 0;
+    int e = ln > 0 ? s + ln : s;
+    e = e < tw ? e : tw;
+    if (e > s) or_span(L.bmask, s, e, 0, 1);
+  }
+  __syncthreads();
+  emit_list(a, L, p, b, nb, bt_pref, btr, wtmp);
 }
 
 // ---------------------------------------------------------------------------
@@ -589,6 +763,43 @@ hipError_t launch_pair(const zr_geom& gm, const PairArgs& a, int mode, hipStream
     case kModeStep: return launch_pair_mode<true, true, true>(gm, a, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+}  // namespace zr
+
+namespace zr {
+
+static size_t consensus_lds(int max_per_seq, int c) {
+  return (static_cast<size_t>(up4(max_per_seq)) + up4(c)) * sizeof(int32_t);
+}
+
+bool consensus_lds_ok(int max_per_seq, int c) {
+  return kPairStaticLds + consensus_lds(max_per_seq, c) + 64 <= kPairLdsLimit;
+}
+
+hipError_t launch_consensus(const ConsArgs& a, hipStream_t s) {
+  if (a.B == 0) return hipSuccess;
+  hipLaunchKernelGGL(consensus_kernel, dim3(a.B), dim3(kPairThreads),
+                     consensus_lds(a.max_per_seq, a.c), s, a);
+  return hipGetLastError();
+}
+
+static size_t zoom_lds(const zr_geom& gm, int max_per_seq) {
+  return (static_cast<size_t>(up4(max_per_seq)) + up4((gm.max_blocks_per_seq + 1) / 2)) *
+         sizeof(int32_t);
+}
+
+bool zoom_lds_ok(const zr_geom& gm, int max_per_seq) {
+  return zoom_lds(gm, max_per_seq) + 1024 <= kPairLdsLimit;
+}
+
+hipError_t launch_zoom_plan(const zr_geom& gm, const PairArgs& a0, hipStream_t s) {
+  if (gm.batch == 0) return hipSuccess;
+  PairArgs a = a0;
+  a.bt_per = (gm.max_blocks_per_seq + kPairThreads - 1) / kPairThreads;
+  hipLaunchKernelGGL(zoom_plan_kernel, dim3(gm.batch * gm.n_kv_heads), dim3(kPairThreads),
+                     zoom_lds(gm, a.max_per_seq), s, a);
+  return hipGetLastError();
 }
 
 }  // namespace zr

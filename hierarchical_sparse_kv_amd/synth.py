@@ -24,6 +24,12 @@ hundred tokens as in ZoomR Sec. 3.5's worked example):
 * Paging: "permuted" = one seeded permutation of every physical block id;
   "interleaved" = sequences allocate blocks in lockstep, one block per
   sequence per round, so consecutive blocks of a sequence are far apart.
+* Multi-granularity layout (``summary`` spec set): ``prompt`` tokens first,
+  then each thought's regular segment R_i followed by its summary segment S_i
+  (lengths drawn from ``thought`` and ``summary``), until the next pair would
+  pass the sequence end; the remaining tokens are the thought still being
+  written (no summary yet, not a candidate). Summary keys then average the
+  summary segment's keys (ZoomR's mean summary key) plus the same noise.
 * Room to grow (append tests): ``extra_tokens`` widens the block table by that
   many tokens per sequence and ``spare_blocks`` adds unused physical blocks,
   returned as a free stack (``free_blocks``, top = last entry).
@@ -60,6 +66,13 @@ CONFIGS = {
     4: dict(name="long-64k-b4", B=4, Hq=32, Hkv=8, d=128, dtype="bf16",
             seq_len=("fixed", 65536), thought=("loguniform", 32, 2048), k=16, window=256,
             planted=3, q_scale=3.0, q_noise=1.0, kbar_noise=0.1, paging="permuted"),
+    # multi-granularity workload: prompt, regular + summary segments, sizes of
+    # ZoomR Sec. 3.5's worked example (N_p 512, N_w 512, c 2, mean L_R 250,
+    # mean L_S 20) on config 1's shapes
+    5: dict(name="zoomr-16k-b8", B=8, Hq=32, Hkv=8, d=128, dtype="bf16",
+            seq_len=("fixed", 16384), prompt=512, thought=("uniform", 100, 400),
+            summary=("uniform", 10, 30), k=8, c=2, window=512,
+            planted=2, q_scale=1.0, q_noise=0.5, kbar_noise=0.1, paging="permuted"),
 }
 
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
@@ -113,22 +126,25 @@ class Workload:
         return float(np.float32(1.0 / math.sqrt(self.d)))
 
 
+def _draw_one(rng, spec):
+    """One integer length from a length spec."""
+    kind = spec[0]
+    if kind == "fixed":
+        return int(spec[1])
+    if kind == "uniform":
+        return int(rng.integers(spec[1], spec[2] + 1))
+    if kind == "loguniform":
+        ln = int(math.floor(math.exp(rng.uniform(math.log(spec[1]), math.log(spec[2] + 1)))))
+        return min(max(ln, spec[1]), spec[2])
+    raise ValueError(kind)
+
+
 def _draw_lengths(rng, spec, total):
     """Integer thought lengths covering ``total`` tokens; the last one is cut."""
     out = []
     acc = 0
     while acc < total:
-        kind = spec[0]
-        if kind == "fixed":
-            ln = spec[1]
-        elif kind == "uniform":
-            ln = int(rng.integers(spec[1], spec[2] + 1))
-        elif kind == "loguniform":
-            ln = int(math.floor(math.exp(rng.uniform(math.log(spec[1]), math.log(spec[2] + 1)))))
-            ln = min(max(ln, spec[1]), spec[2])
-        else:
-            raise ValueError(kind)
-        ln = min(ln, total - acc)
+        ln = min(_draw_one(rng, spec), total - acc)
         out.append(ln)
         acc += ln
     return out
@@ -147,13 +163,28 @@ def make_structure(cfg: dict, seed: int, seq_lens=None):
             seq_lens = rng.integers(kind[1], kind[2] + 1, size=B).astype(np.int32)
     seq_lens = np.asarray(seq_lens, dtype=np.int32)
     starts, lens, ptr = [], [], [0]
+    sstarts, slens = [], []
     for b in range(B):
-        ls = _draw_lengths(rng, cfg["thought"], int(seq_lens[b])) if seq_lens[b] > 0 else []
-        s = 0
-        for ln in ls:
-            starts.append(s)
-            lens.append(ln)
-            s += ln
+        if cfg.get("summary") is None:
+            ls = _draw_lengths(rng, cfg["thought"], int(seq_lens[b])) if seq_lens[b] > 0 else []
+            s = 0
+            for ln in ls:
+                starts.append(s)
+                lens.append(ln)
+                s += ln
+        else:
+            T = int(seq_lens[b])
+            s = min(int(cfg.get("prompt", 0)), T)
+            while True:
+                lr = _draw_one(rng, cfg["thought"])
+                ls_ = _draw_one(rng, cfg["summary"])
+                if s + lr + ls_ > T:
+                    break
+                starts.append(s)
+                lens.append(lr)
+                sstarts.append(s + lr)
+                slens.append(ls_)
+                s += lr + ls_
         ptr.append(len(starts))
     nblk = [(int(t) + BLOCK_SIZE - 1) // BLOCK_SIZE for t in seq_lens]
     extra = int(cfg.get("extra_tokens", 0))
@@ -188,8 +219,12 @@ def make_structure(cfg: dict, seed: int, seq_lens=None):
             if n_b > 0:
                 m = min(n_pl, n_b)
                 planted[b, g, :m] = np.sort(rng.choice(n_b, size=m, replace=False))
+    if not sstarts:
+        sstarts, slens = list(starts), list(lens)
     return dict(seq_lens=seq_lens, block_table=table, num_blocks=num_blocks,
                 free_blocks=free_blocks.astype(np.int32),
+                sum_start=np.array(sstarts, dtype=np.int32),
+                sum_len=np.array(slens, dtype=np.int32),
                 seq_ptr=np.array(ptr, dtype=np.int32),
                 th_start=np.array(starts, dtype=np.int32),
                 th_len=np.array(lens, dtype=np.int32), planted=planted)
@@ -210,8 +245,8 @@ def _summary_keys(k_pool, st, cfg, gen, device):
         rows = k_pool[table[b, j // BLOCK_SIZE], :, j % BLOCK_SIZE, :].to(torch.float64)
         csum = torch.cat([torch.zeros((1, Hkv, d), dtype=torch.float64, device=device),
                           rows.cumsum(0)])
-        s = torch.as_tensor(st["th_start"][lo:hi], device=device, dtype=torch.int64)
-        ln = torch.as_tensor(st["th_len"][lo:hi], device=device, dtype=torch.int64)
+        s = torch.as_tensor(st["sum_start"][lo:hi], device=device, dtype=torch.int64)
+        ln = torch.as_tensor(st["sum_len"][lo:hi], device=device, dtype=torch.int64)
         out[lo:hi] = (csum[s + ln] - csum[s]) / ln.to(torch.float64)[:, None, None]
         del rows, csum
     noise = torch.randn((n_total, Hkv, d), generator=gen, device=device, dtype=torch.float32)
@@ -258,12 +293,15 @@ def make_workload(cfg_id, seed=None, device="cpu", overrides=None, seq_lens=None
     q = q.to(dt)
     n_max = int(np.max(np.diff(st["seq_ptr"]))) if B > 0 else 0
     k = cfg["k"] if cfg["k"] is not None else max(1, n_max)
+    extra = {"cfg": cfg, "free_blocks": st["free_blocks"], "sum_start": st["sum_start"],
+             "sum_len": st["sum_len"], "prompt": int(cfg.get("prompt", 0)),
+             "c": int(cfg.get("c", 0))}
     return Workload(name=cfg["name"], seed=int(seed), dtype=cfg["dtype"], B=B, Hq=Hq, Hkv=Hkv,
                     d=d, k=int(k), window=int(cfg["window"]), seq_lens=st["seq_lens"],
                     block_table=st["block_table"], num_blocks=st["num_blocks"],
                     seq_ptr=st["seq_ptr"], th_start=st["th_start"], th_len=st["th_len"],
                     planted=st["planted"], k_pool=k_pool, v_pool=v_pool, summary_keys=kbar,
-                    q=q, extra={"cfg": cfg, "free_blocks": st["free_blocks"]})
+                    q=q, extra=extra)
 
 
 def to_numpy_f32(t: torch.Tensor) -> np.ndarray:

@@ -59,6 +59,12 @@ _SIGS = {
     "zr_sparse_decode_attn_cached": (ctypes.c_int, [_G, _P, _P, _P, _P, _P, ctypes.c_int32,
                                                     ctypes.c_float, ctypes.c_int32, _P, _P,
                                                     ctypes.c_size_t, _P]),
+    "zr_consensus": (ctypes.c_int, [_G, _T, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                    _P, _P, _P, _P]),
+    "zr_zoom_decode_attn": (ctypes.c_int, [_G, _P, _P, _P, _P, _P, _T, _P, _P, _P, _P,
+                                           ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.c_float, ctypes.c_int32, _P, _P,
+                                           ctypes.c_size_t, _P]),
     "zr_append_kv": (ctypes.c_int, [_G, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "zr_summary_keys": (ctypes.c_int, [_G, _P, _P, _T, _P, ctypes.c_int32, _P, _P]),
     "zr_dense_paged_decode_attn": (ctypes.c_int, [_G, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P,
@@ -132,6 +138,20 @@ def zr_sparse_decode_attn_cached(geom, q, k_pool, v_pool, block_table, seq_lens,
                                               seq_lens, int(window), float(scale),
                                               int(max_attended), out, workspace, int(ws_bytes),
                                               stream)
+
+
+def zr_consensus(geom, th, sel, n_layers, k, c, votes, cons, agree, stream=None) -> int:
+    return lib().zr_consensus(ctypes.byref(geom), ctypes.byref(th), sel, int(n_layers), int(k),
+                              int(c), votes, cons, agree, stream)
+
+
+def zr_zoom_decode_attn(geom, q, k_pool, v_pool, block_table, seq_lens, th, sum_start, sum_len,
+                        votes, cons, c, n_prompt, window, scale, max_attended, out, workspace,
+                        ws_bytes, stream=None) -> int:
+    return lib().zr_zoom_decode_attn(ctypes.byref(geom), q, k_pool, v_pool, block_table,
+                                     seq_lens, ctypes.byref(th), sum_start, sum_len, votes, cons,
+                                     int(c), int(n_prompt), int(window), float(scale),
+                                     int(max_attended), out, workspace, int(ws_bytes), stream)
 
 
 def zr_append_kv(geom, k_pool, v_pool, block_table, seq_lens, k_new, v_new, free_blocks,
@@ -253,6 +273,26 @@ class DeviceStep:
         check("zr_summary_keys", zr_summary_keys(
             self.geom, _ptr(self.k_pool), _ptr(self.block_table), self.th, _ptr(which),
             which.numel(), _ptr(out), _stream()))
+
+    def consensus(self, sel_stack, c, votes, cons, agree):
+        """Votes, consensus set and agreement over stacked selections
+        [n_layers][B][Hkv][k] (zr_consensus)."""
+        sel_stack = sel_stack.contiguous()
+        n_layers, k = sel_stack.shape[0], sel_stack.shape[-1]
+        check("zr_consensus", zr_consensus(
+            self.geom, self.th, _ptr(sel_stack), n_layers, k, int(c), _ptr(votes),
+            _ptr(cons) if c else None, _ptr(agree), _stream()))
+
+    def zoom_attn(self, sum_start, sum_len, votes, cons, c, n_prompt, window=None, out=None):
+        """Attention over the multi-granularity set (zr_zoom_decode_attn)."""
+        window = self.window if window is None else int(window)
+        out = self.out if out is None else out
+        check("zr_zoom_decode_attn", zr_zoom_decode_attn(
+            self.geom, _ptr(self.q), _ptr(self.k_pool), _ptr(self.v_pool),
+            _ptr(self.block_table), _ptr(self.seq_lens), self.th, _ptr(sum_start),
+            _ptr(sum_len), _ptr(votes), _ptr(cons) if c else None, int(c), int(n_prompt), window,
+            self.scale, self.max_attended, _ptr(out), _ptr(self.workspace),
+            self.workspace.numel(), _stream()))
 
     def dense_attn(self, out=None):
         out = self.out if out is None else out

@@ -22,6 +22,12 @@
  *   Sec. 3.4 and Appendix A.3; Algorithm 1 rebuilds it at boundaries only).
  *   zr_dense_paged_decode_attn is the dense baseline: attention over every
  *   cached token through the same block table (same page, eq. 4).
+ *   zr_consensus and zr_zoom_decode_attn are ZoomR's full multi-granularity
+ *   selection: votes over every (layer, KV head) top-k set, the consensus
+ *   set, and attention over prompt + window + consensus thoughts at full
+ *   resolution + the other voted thoughts' summaries (ZoomR Sec. 3.3,
+ *   "Global Aggregation and Consensus" and "Constructing the Final
+ *   Multi-Granularity Context").
  *   zr_append_kv and zr_summary_keys are the append path that precedes a
  *   step: the new token's K/V into the paged cache (with on-demand block
  *   allocation) and the mean summary key of a thought once it is complete.
@@ -182,8 +188,8 @@ zr_status zr_sparse_decode_attn(const zr_geom* geom, const void* q, const void* 
 
 /*
  * Sparse attention on a cached selection. `workspace` must hold the block
- * lists written by the last zr_sparse_decode_attn or zr_sparse_decode_step
- * that used it (same geom; the block-table rows of those spans unchanged):
+ * lists written by the last zr_sparse_decode_attn, zr_sparse_decode_step or
+ * zr_zoom_decode_attn that used it (same geom; the block-table rows of those spans unchanged):
  * the selected thoughts' spans, clipped below that call's window start
  * T0 - window0. This call attends those spans plus its own window
  * [T - window, T) of the current seq_lens. Between semantic boundaries pass
@@ -277,6 +283,50 @@ zr_status zr_append_kv(const zr_geom* geom, void* k_pool, void* v_pool, int32_t*
 zr_status zr_summary_keys(const zr_geom* geom, const void* k_pool, const int32_t* block_table,
                           const zr_thoughts* th, const int32_t* which, int32_t n_which,
                           void* summary_keys, void* stream);
+
+/*
+ * Votes and consensus (ZoomR, Sec. 3.3, eqs. for I_all and v_i; Sec. 4, the
+ * agreeability metric AG). sel holds n_layers stacked selections, [n_layers]
+ * [batch][n_kv_heads][k] as zr_select_topk writes them (local thought
+ * indices, distinct within a row, -1 = none). For every sequence b:
+ *   votes[i] = number of (layer, KV head) rows holding thought i  ([n_total]);
+ *   cons[b][0..) = the min(c, |I_all|) thoughts with the most votes among those
+ *                  with at least one, ties to the lower index, ascending, -1
+ *                  padded to c  ([batch][c]);
+ *   agree[b] = sum of the consensus thoughts' votes / sum of all votes (0 if
+ *              there are none)  ([batch] float32).
+ * Indices outside [0, N_b) in sel are ignored; a repeated index within one
+ * row is counted each time it appears. n_layers = 0 or k = 0 gives no votes.
+ * Errors: ZR_E_NULL, ZR_E_SHAPE (n_layers, k, c < 0; k, c > ZR_MAX_K),
+ * ZR_E_UNSUPPORTED (max_per_seq too large for on-chip memory), ZR_E_LAUNCH.
+ */
+zr_status zr_consensus(const zr_geom* geom, const zr_thoughts* th, const int32_t* sel,
+                       int32_t n_layers, int32_t k, int32_t c, int32_t* votes, int32_t* cons,
+                       float* agree, void* stream);
+
+/*
+ * Attention over ZoomR's multi-granularity set (ZoomR, Sec. 3.3, eq. for
+ * I_f), one set per sequence shared by all heads:
+ *   I_f = [0, n_prompt)  union  [T_b - window, T_b)
+ *         union  R_i = [start_i, start_i + len_i)          for i in cons[b]
+ *         union  S_i = [sum_start_i, sum_start_i + sum_len_i)  for the other
+ *                                                 thoughts with votes[i] > 0
+ * (th->start/len are the regular segments R_i; sum_start/sum_len [n_total]
+ * the summary segments S_i), each token once, clipped to [0, T_b). Every
+ * query head gets softmax(scale * q . K) V over I_f, float32 accumulation.
+ * Like zr_sparse_decode_attn it leaves the block lists in `workspace`, so
+ * zr_sparse_decode_attn_cached can repeat the attention between semantic
+ * boundaries. Workspace, alignment and errors as zr_sparse_decode_attn
+ * (ZR_E_SHAPE also for c or n_prompt < 0).
+ */
+zr_status zr_zoom_decode_attn(const zr_geom* geom, const void* q, const void* k_pool,
+                              const void* v_pool, const int32_t* block_table,
+                              const int32_t* seq_lens, const zr_thoughts* th,
+                              const int32_t* sum_start, const int32_t* sum_len,
+                              const int32_t* votes, const int32_t* cons, int32_t c,
+                              int32_t n_prompt, int32_t window, float scale,
+                              int32_t max_attended, float* out, void* workspace,
+                              size_t ws_bytes, void* stream);
 
 /* Workspace bytes the attention calls need for a grid sized for
  * `max_attended` tokens per (sequence, KV head): per-(b, g) block lists

@@ -44,6 +44,18 @@ The append path (before a step's attention):
    the thought's own cached keys, reading R11), float64, rounded to float32
    and then to the cache dtype (bf16: round to nearest even).
 
+The full multi-granularity set (ZoomR's consensus):
+
+8. ``consensus``       - votes v_i = number of (layer, KV head) top-k sets that
+   contain thought i, I_all = thoughts with a vote, consensus set I_c = the c
+   thoughts with the most votes (ties to the lower index, reading R25), the
+   agreement AG = sum of I_c's votes over all votes (ZoomR, Sec. 3.3 "Global
+   Aggregation and Consensus", eqs. for I_all and v_i; Sec. 4, the AG metric).
+9. ``zoom_attended_tokens`` - I_f = I_p U I_w U (R_i, i in I_c) U (S_i, i in
+   I_s), I_s = I_all minus I_c (ZoomR, Sec. 3.3 "Constructing the Final
+   Multi-Granularity Context", eq. for I_f), shared by every head.
+10. ``zoom_decode_step`` - attention of every query head over I_f.
+
 Accounting helpers pinned to printed figures:
 ``memory_savings`` (ZoomR, Sec. 3.5, eq. MS) and ``dense_kv_bytes`` (the
 dense-cache sizing formula on the KV-cache management page, "Sizing the dense
@@ -244,6 +256,83 @@ def sparse_decode_step(q, k_pool, v_pool, block_table, seq_lens, seq_ptr, starts
         n_att[b, g] = len(toks)
         out[b, g * G:(g + 1) * G] = attend(q[b, g * G:(g + 1) * G], K[toks, g], V[toks, g], scale)
     return {"scores": scores, "sel": own_sel, "out": out, "n_attended": n_att}
+
+
+def consensus(sel_layers, seq_ptr, c):
+    """Votes, consensus set and agreement per sequence.
+
+    ``sel_layers`` [n_layers][B][Hkv][k] holds every (layer, KV head) top-k
+    set (local thought indices, -1 = none). v_i counts the sets containing
+    thought i (an indicator per set: a repeated index counts once); I_all is
+    the thoughts with v_i > 0; I_c the min(c, |I_all|) of them with the most
+    votes, ties to the lower index; AG = sum_{I_c} v_i / sum_{I_all} v_i (0
+    with no votes). Returns votes [n_total] int32, cons [B][c] int32 (ascending,
+    -1 padded) and agree [B] float64.
+    """
+    sel_layers = np.asarray(sel_layers)
+    seq_ptr = np.asarray(seq_ptr)
+    B = len(seq_ptr) - 1
+    n_total = int(seq_ptr[-1])
+    votes = np.zeros(n_total, dtype=np.int32)
+    cons = np.full((B, max(c, 0)), -1, dtype=np.int32)
+    agree = np.zeros(B, dtype=np.float64)
+    for b in range(B):
+        lo, hi = int(seq_ptr[b]), int(seq_ptr[b + 1])
+        n = hi - lo
+        for row in sel_layers[:, b].reshape(-1, sel_layers.shape[-1]):
+            for i in set(int(x) for x in row if 0 <= x < n):
+                votes[lo + i] += 1
+        members = [i for i in range(n) if votes[lo + i] > 0]
+        ranked = sorted(members, key=lambda i: (-int(votes[lo + i]), i))
+        chosen = sorted(ranked[:max(c, 0)])
+        cons[b, :len(chosen)] = chosen
+        total = sum(int(votes[lo + i]) for i in members)
+        agree[b] = sum(int(votes[lo + i]) for i in chosen) / total if total else 0.0
+    return votes, cons, agree
+
+
+def zoom_attended_tokens(votes_b, cons_row, starts, lens, sum_starts, sum_lens, n_prompt,
+                         n_cached, window):
+    """Ascending token indices of I_f for one sequence: the prompt [0, N_p),
+    the window [T - W, T), the regular segment R_i of every consensus thought
+    and the summary segment S_i of every other voted thought, as a set union
+    inside [0, T). ``votes_b`` and the spans are indexed by local thought."""
+    T = int(n_cached)
+    tokens = set(range(0, min(int(n_prompt), T))) | set(range(max(0, T - window), T))
+    cons = set(int(i) for i in cons_row if i >= 0)
+    for i, v in enumerate(np.asarray(votes_b).tolist()):
+        if v <= 0:
+            continue
+        if i in cons:
+            s, ln = int(starts[i]), int(lens[i])
+        else:
+            s, ln = int(sum_starts[i]), int(sum_lens[i])
+        tokens |= set(range(s, s + ln))
+    return np.array(sorted(t for t in tokens if 0 <= t < T), dtype=np.int64)
+
+
+def zoom_decode_step(q, k_pool, v_pool, block_table, seq_lens, seq_ptr, starts, lens,
+                     sum_starts, sum_lens, votes, cons, n_prompt, window, scale):
+    """Attention of every query head over its sequence's I_f (shared by all
+    heads). Returns dict with ``out`` [B][Hq][d] f64 and ``n_attended`` [B]."""
+    q = np.asarray(q)
+    B, Hq, d = q.shape
+    Hkv = k_pool.shape[1]
+    G = Hq // Hkv
+    out = np.zeros((B, Hq, d))
+    n_att = np.zeros(B, dtype=np.int64)
+    for b in range(B):
+        T = int(seq_lens[b])
+        K = gather_keys(k_pool, block_table[b], T)
+        V = gather_values(v_pool, block_table[b], T)
+        lo, hi = int(seq_ptr[b]), int(seq_ptr[b + 1])
+        toks = zoom_attended_tokens(votes[lo:hi], cons[b], starts[lo:hi], lens[lo:hi],
+                                    sum_starts[lo:hi], sum_lens[lo:hi], n_prompt, T, window)
+        n_att[b] = len(toks)
+        for g in range(Hkv):
+            out[b, g * G:(g + 1) * G] = attend(q[b, g * G:(g + 1) * G], K[toks, g], V[toks, g],
+                                               scale)
+    return {"out": out, "n_attended": n_att}
 
 
 def dense_decode_step(q, k_pool, v_pool, block_table, seq_lens, scale, pairs=None):

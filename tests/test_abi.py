@@ -25,6 +25,7 @@ def test_exports_every_declared_symbol(L):
     assert declared == sorted(["zr_coarse_score", "zr_select_topk", "zr_sparse_decode_attn",
                                "zr_sparse_decode_attn_cached", "zr_sparse_decode_step",
                                "zr_dense_paged_decode_attn", "zr_append_kv", "zr_summary_keys",
+                               "zr_consensus", "zr_zoom_decode_attn",
                                "zr_workspace_bytes", "zr_status_string"])
     out = subprocess.run(["nm", "-D", "--defined-only", zr.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
@@ -178,3 +179,27 @@ def test_append_and_summary_errors(L):
     assert sk(summary_keys=FAKE + 8) == zr.ZR_E_ALIGN
     assert sk(th=_th(len=None)) == zr.ZR_E_NULL
     assert sk(n_which=0, which=None) == zr.ZR_OK
+
+
+def test_consensus_and_zoom_errors(L):
+    g = _geom()
+    cs = lambda **kw: zr.zr_consensus(**dict(dict(
+        geom=g, th=_th(), sel=FAKE, n_layers=2, k=4, c=2, votes=FAKE, cons=FAKE, agree=FAKE),
+        **kw))
+    assert cs(c=-1) == zr.ZR_E_SHAPE
+    assert cs(k=2000) == zr.ZR_E_SHAPE
+    assert cs(n_layers=-1) == zr.ZR_E_SHAPE
+    assert cs(votes=None) == zr.ZR_E_NULL
+    assert cs(cons=None) == zr.ZR_E_NULL
+    assert cs(sel=None) == zr.ZR_E_NULL
+    assert cs(th=_th(max_per_seq=9000)) == zr.ZR_E_UNSUPPORTED
+    zm = lambda **kw: zr.zr_zoom_decode_attn(**dict(dict(
+        geom=g, q=FAKE, k_pool=FAKE, v_pool=FAKE, block_table=FAKE, seq_lens=FAKE, th=_th(),
+        sum_start=FAKE, sum_len=FAKE, votes=FAKE, cons=FAKE, c=2, n_prompt=16, window=16,
+        scale=0.1, max_attended=100, out=FAKE, workspace=FAKE, ws_bytes=1 << 20), **kw))
+    assert zm(n_prompt=-1) == zr.ZR_E_SHAPE
+    assert zm(c=-2) == zr.ZR_E_SHAPE
+    assert zm(sum_len=None) == zr.ZR_E_NULL
+    assert zm(cons=None) == zr.ZR_E_NULL
+    assert zm(out=FAKE + 4) == zr.ZR_E_ALIGN
+    assert zm(ws_bytes=8) == zr.ZR_E_WORKSPACE

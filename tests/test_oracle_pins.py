@@ -424,3 +424,95 @@ def test_summary_keys_closed_forms():
     a = O.summary_keys(k, table, seq_ptr, starts, lens, range(5), "bf16")
     b = O.summary_keys(k2, perm[table], seq_ptr, starts, lens, range(5), "bf16")
     assert np.array_equal(a, b)
+
+
+# --------------------------------------------------------------------------
+# Consensus and the multi-granularity set
+# --------------------------------------------------------------------------
+def test_consensus_hand_example():
+    """2 layers x 2 KV heads, k = 2 over 5 thoughts: votes are counted per
+    set (a repeated index counts once), the consensus set takes the most
+    voted thoughts with ties to the lower index, AG is the consensus share of
+    all votes."""
+    sel = np.array([[[[0, 1], [1, 2]]], [[[1, 3], [3, 4]]]], np.int32)   # [L][B][Hkv][k]
+    ptr = np.array([0, 5], np.int32)
+    votes, cons, ag = O.consensus(sel, ptr, 2)
+    assert votes.tolist() == [1, 3, 1, 2, 1]
+    assert cons.tolist() == [[1, 3]] and ag[0] == 5 / 8
+    votes, cons, ag = O.consensus(sel, ptr, 3)
+    assert cons.tolist() == [[0, 1, 3]] and ag[0] == 6 / 8
+    dup = sel.copy()
+    dup[0, 0, 0] = [1, 1]
+    votes, _, _ = O.consensus(dup, ptr, 2)
+    assert votes.tolist() == [0, 3, 1, 2, 1]
+    # every voted thought in the consensus set: AG = 1; no votes: AG = 0
+    assert O.consensus(sel, ptr, 8)[2][0] == 1.0
+    v, c, a = O.consensus(np.full_like(sel, -1), ptr, 2)
+    assert v.sum() == 0 and c.tolist() == [[-1, -1]] and a[0] == 0.0
+
+
+def test_consensus_votes_are_row_memberships():
+    """Random rows: votes sum to the number of distinct valid entries per
+    row, and each thought's votes equal the number of rows holding it."""
+    rng = np.random.default_rng(4)
+    L_, B, Hkv, k = 3, 2, 4, 5
+    ptr = np.array([0, 9, 12], np.int32)
+    sel = np.full((L_, B, Hkv, k), -1, np.int32)
+    for l in range(L_):
+        for b in range(B):
+            n = ptr[b + 1] - ptr[b]
+            for g in range(Hkv):
+                m = min(k, n)
+                sel[l, b, g, :m] = np.sort(rng.choice(n, size=m, replace=False))
+    votes, cons, ag = O.consensus(sel, ptr, 2)
+    for b in range(B):
+        rows = sel[:, b].reshape(-1, k)
+        assert votes[ptr[b]:ptr[b + 1]].sum() == (rows >= 0).sum()
+        for i in range(ptr[b + 1] - ptr[b]):
+            assert votes[ptr[b] + i] == sum(int(i in r) for r in rows.tolist())
+
+
+def test_zoom_set_size_matches_memory_formula():
+    """A layout of prompt + 100 thoughts (regular 250 tokens, summary 20) and
+    an 80-thought candidate set with c = 2 consensus thoughts, away from the
+    512-token window: |I_f| equals the denominator of ZoomR Sec. 3.5's memory
+    savings, and N/|I_f| equals the savings helper pinned to the printed 5.48x."""
+    n_p, n_w, L_R, L_S, n_th = 512, 512, 250, 20, 100
+    starts = n_p + (L_R + L_S) * np.arange(n_th)
+    lens = np.full(n_th, L_R)
+    sstarts = starts + L_R
+    slens = np.full(n_th, L_S)
+    T = n_p + n_th * (L_R + L_S)
+    votes = np.zeros(n_th, np.int32)
+    votes[:80] = 1
+    votes[[7, 40]] = 5
+    cons = np.array([7, 40], np.int32)
+    toks = O.zoom_attended_tokens(votes, cons, starts, lens, sstarts, slens, n_p, T, n_w)
+    assert len(toks) == n_p + 2 * L_R + (80 - 2) * L_S + n_w
+    ms = O.memory_savings(n_p, T - n_p, n_w, 2, L_R, L_S, 80)
+    assert abs(ms - T / len(toks)) < 1e-12
+
+
+def test_zoom_equals_per_head_path_when_heads_agree():
+    """With summary segments equal to the regular ones, no prompt, and every
+    KV head selecting the same thoughts, the multi-granularity set is the
+    window plus those thoughts' spans whatever c is, so the zoom attention
+    equals the per-head sparse step on that selection."""
+    rng = np.random.default_rng(11)
+    B, Hq, Hkv, d, nb = 2, 4, 2, 8, 12
+    k_pool = rng.normal(size=(nb, Hkv, 16, d))
+    v_pool = rng.normal(size=(nb, Hkv, d, 16))
+    table = np.array([[3, 0, 7, 9, 1, 11], [2, 4, 5, 6, 8, 10]], np.int32)
+    lens_seq = np.array([90, 77], np.int32)
+    seq_ptr = np.array([0, 4, 7], np.int32)
+    starts = np.array([0, 20, 45, 60, 0, 30, 50], np.int32)
+    lens = np.array([20, 25, 15, 30, 30, 20, 27], np.int32)
+    q = rng.normal(size=(B, Hq, d))
+    kbar = rng.normal(size=(7, Hkv, d))
+    sel = np.array([[[0, 2], [0, 2]], [[1, -1], [1, -1]]], np.int32)
+    ref = O.sparse_decode_step(q, k_pool, v_pool, table, lens_seq, seq_ptr, starts, lens, kbar,
+                               2, 16, 0.3, sel=sel)
+    votes, cons, _ = O.consensus(sel[None], seq_ptr, 1)
+    got = O.zoom_decode_step(q, k_pool, v_pool, table, lens_seq, seq_ptr, starts, lens, starts,
+                             lens, votes, cons, 0, 16, 0.3)
+    assert np.allclose(got["out"], ref["out"], rtol=0, atol=1e-12)
