@@ -85,6 +85,8 @@ def main():
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-offload", action="store_true",
+                    help="skip the host-memory (PCIe) figure")
     ap.add_argument("--no-zoom", action="store_true",
                     help="skip the multi-granularity (consensus) figure")
     ap.add_argument("--period", type=int, default=35,
@@ -130,6 +132,7 @@ def main():
     att = [zr.attended_counts(st.sel.cpu().numpy(), w.seq_lens, w.seq_ptr, w.th_start, w.th_len,
                               w.window) for st, w in zip(steps, layers)]
     kv_bytes = [int(a.sum()) * 2 * d * s_bytes for a in att]
+    dense_bytes = int(w0.seq_lens.sum()) * w0.Hkv * 2 * d * s_bytes
     q_out_bytes = w0.B * w0.Hq * d * (s_bytes + 4)
 
     # Steps are captured into HIP graphs (one node per kernel, no host work
@@ -281,9 +284,32 @@ def main():
                 "between_us_per_layer": round(between_us, 3),
                 "between_gbs": round(zbytes / (between_us * 1e-6) / 1e9, 1)}
 
+    # host-offloaded cache (ZoomR Sec. 3.4): layer 0's pools in pinned host
+    # memory; the kernels read only the attended blocks over PCIe
+    offload = None
+    if not args.no_offload:
+        kp_h, vp_h = w0.k_pool.cpu().pin_memory(), w0.v_pool.cpu().pin_memory()
+        hs = zr.DeviceStep(w0.q, kp_h, vp_h, w0.block_table, w0.seq_lens, w0.seq_ptr,
+                           w0.th_start, w0.th_len, w0.summary_keys, w0.max_per_seq, w0.k,
+                           w0.window, w0.scale, steps[0].max_attended)
+        hs.step()
+        torch.cuda.synchronize()
+        n_off = 10
+        g_off = capture(lambda i: hs.sparse_attn(sel=steps[0].sel), n_off)
+        g_off.replay()
+        off_us = timed(g_off, n_off)
+        g_offd = capture(lambda i: hs.dense_attn(), 2)
+        g_offd.replay()
+        offd_us = timed(g_offd, 2)
+        offload = {"pools": "pinned host memory, read by the kernels over PCIe (layer 0)",
+                   "sparse_attn_us": round(off_us, 1),
+                   "sparse_h2d_gbs": round(kv_bytes[0] / (off_us * 1e-6) / 1e9, 2),
+                   "dense_attn_us": round(offd_us, 1),
+                   "dense_h2d_gbs": round(dense_bytes / (offd_us * 1e-6) / 1e9, 2)}
+        del hs, kp_h, vp_h
+
     # dense baseline (same caches, every token) for context
     dense_us = timed(g_dense, L)
-    dense_bytes = int(w0.seq_lens.sum()) * w0.Hkv * 2 * d * s_bytes
 
     cpu = None
     if not args.no_cpu:
@@ -325,6 +351,7 @@ def main():
                             "steps_per_s": round(1e6 / period_us, 1)},
         "speedup_vs_dense_attention": round(dense_us / attn_us, 3),
         "zoomr_consensus": zoom,
+        "host_offload": offload,
         "append_path": {"append_kv_us": round(append_us, 3),
                         "summary_keys_us": round(summary_us, 3),
                         "summary_thoughts_per_call": int(w0.B),

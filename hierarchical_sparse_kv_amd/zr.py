@@ -184,6 +184,33 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+_hip = None
+
+
+def pinned_device_ptr(t: torch.Tensor) -> int:
+    """Device address of a pinned host tensor (hipHostGetDevicePointer), for
+    pools kept in host memory and read by the kernels over PCIe. Raises if
+    the tensor is not pinned or the runtime reports no device mapping."""
+    global _hip
+    if not (t.device.type == "cpu" and t.is_pinned()):
+        raise ValueError("expected a pinned host tensor")
+    if _hip is None:
+        _hip = ctypes.CDLL("libamdhip64.so")
+        _hip.hipHostGetDevicePointer.restype = ctypes.c_int
+        _hip.hipHostGetDevicePointer.argtypes = [ctypes.POINTER(ctypes.c_void_p),
+                                                 ctypes.c_void_p, ctypes.c_uint]
+    dev = ctypes.c_void_p()
+    err = _hip.hipHostGetDevicePointer(ctypes.byref(dev), ctypes.c_void_p(t.data_ptr()), 0)
+    if err != 0 or not dev.value:
+        raise RuntimeError(f"hipHostGetDevicePointer failed ({err})")
+    return int(dev.value)
+
+
+def _pool_ptr(t):
+    """Device address of a K/V pool: device memory, or pinned host memory."""
+    return pinned_device_ptr(t) if t.device.type == "cpu" else t.data_ptr()
+
+
 def _stream():
     return torch.cuda.current_stream().cuda_stream
 
@@ -204,6 +231,8 @@ class DeviceStep:
                                         dtype=torch.int32, device=dev).contiguous()
         self.q = q.contiguous()
         self.k_pool, self.v_pool = k_pool.contiguous(), v_pool.contiguous()
+        # pools may live in pinned host memory (read over PCIe)
+        self.kp, self.vp = _pool_ptr(self.k_pool), _pool_ptr(self.v_pool)
         self.block_table = i32(block_table)
         self.seq_lens = i32(seq_lens)
         n_total = int(np.asarray(seq_ptr)[-1]) if not torch.is_tensor(seq_ptr) else int(seq_ptr[-1])
@@ -242,7 +271,7 @@ class DeviceStep:
         sel = self.sel if sel is None else sel
         out = self.out if out is None else out
         check("zr_sparse_decode_attn", zr_sparse_decode_attn(
-            self.geom, _ptr(self.q), _ptr(self.k_pool), _ptr(self.v_pool),
+            self.geom, _ptr(self.q), self.kp, self.vp,
             _ptr(self.block_table), _ptr(self.seq_lens), self.th,
             _ptr(sel) if self.k else None, self.k, self.window, self.scale, self.max_attended,
             _ptr(out), _ptr(self.workspace), self.workspace.numel(), _stream()))
@@ -254,7 +283,7 @@ class DeviceStep:
         q = self.q if q is None else q
         out = self.out if out is None else out
         check("zr_sparse_decode_attn_cached", zr_sparse_decode_attn_cached(
-            self.geom, _ptr(q), _ptr(self.k_pool), _ptr(self.v_pool), _ptr(self.block_table),
+            self.geom, _ptr(q), self.kp, self.vp, _ptr(self.block_table),
             _ptr(seq_lens), int(window), self.scale, self.max_attended, _ptr(out),
             _ptr(self.workspace), self.workspace.numel(), _stream()))
 
@@ -262,7 +291,7 @@ class DeviceStep:
         """Append one token per sequence (zr_append_kv); updates this step's
         block table and sequence lengths in place."""
         check("zr_append_kv", zr_append_kv(
-            self.geom, _ptr(self.k_pool), _ptr(self.v_pool), _ptr(self.block_table),
+            self.geom, self.kp, self.vp, _ptr(self.block_table),
             _ptr(self.seq_lens), _ptr(k_new.contiguous()), _ptr(v_new.contiguous()),
             _ptr(free_blocks), _ptr(free_count), _ptr(status), _stream()))
 
@@ -271,7 +300,7 @@ class DeviceStep:
         into `out` (default: this step's summary keys)."""
         out = self.summary_keys if out is None else out
         check("zr_summary_keys", zr_summary_keys(
-            self.geom, _ptr(self.k_pool), _ptr(self.block_table), self.th, _ptr(which),
+            self.geom, self.kp, _ptr(self.block_table), self.th, _ptr(which),
             which.numel(), _ptr(out), _stream()))
 
     def consensus(self, sel_stack, c, votes, cons, agree):
@@ -288,7 +317,7 @@ class DeviceStep:
         window = self.window if window is None else int(window)
         out = self.out if out is None else out
         check("zr_zoom_decode_attn", zr_zoom_decode_attn(
-            self.geom, _ptr(self.q), _ptr(self.k_pool), _ptr(self.v_pool),
+            self.geom, _ptr(self.q), self.kp, self.vp,
             _ptr(self.block_table), _ptr(self.seq_lens), self.th, _ptr(sum_start),
             _ptr(sum_len), _ptr(votes), _ptr(cons) if c else None, int(c), int(n_prompt), window,
             self.scale, self.max_attended, _ptr(out), _ptr(self.workspace),
@@ -297,7 +326,7 @@ class DeviceStep:
     def dense_attn(self, out=None):
         out = self.out if out is None else out
         check("zr_dense_paged_decode_attn", zr_dense_paged_decode_attn(
-            self.geom, _ptr(self.q), _ptr(self.k_pool), _ptr(self.v_pool),
+            self.geom, _ptr(self.q), self.kp, self.vp,
             _ptr(self.block_table), _ptr(self.seq_lens), self.scale, _ptr(out),
             _ptr(self.workspace), self.workspace.numel(), _stream()))
 
@@ -308,7 +337,7 @@ class DeviceStep:
         sel = self.sel if sel is None else sel
         out = self.out if out is None else out
         check("zr_sparse_decode_step", zr_sparse_decode_step(
-            self.geom, _ptr(self.q), _ptr(self.k_pool), _ptr(self.v_pool),
+            self.geom, _ptr(self.q), self.kp, self.vp,
             _ptr(self.block_table), _ptr(seq_lens), self.th, self.k, self.window,
             self.scale, self.max_attended, _ptr(scores), _ptr(sel) if self.k else None,
             _ptr(out), _ptr(self.workspace), self.workspace.numel(), _stream()))

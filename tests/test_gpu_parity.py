@@ -290,3 +290,27 @@ def test_cached_selection_between_boundaries():
         st2.sparse_attn(sel=sel)
         torch.cuda.synchronize()
         assert torch.equal(st2.out, got), i
+
+
+def test_pools_in_pinned_host_memory():
+    """The K/V pools kept in pinned host memory (ZoomR Sec. 3.4: the full
+    cache lives in CPU memory and each step moves the selected part to the
+    GPU): the kernels read only the listed blocks over PCIe, and every output
+    equals the run on device-resident pools bit for bit."""
+    w = _small(1, k=5)
+    st = zr.step_from_workload(w)
+    st.step()
+    torch.cuda.synchronize()
+    ref = (st.scores.clone(), st.sel.clone(), st.out.clone())
+    kp, vp = w.k_pool.cpu().pin_memory(), w.v_pool.cpu().pin_memory()
+    hs = zr.DeviceStep(w.q, kp, vp, w.block_table, w.seq_lens, w.seq_ptr, w.th_start, w.th_len,
+                       w.summary_keys, w.max_per_seq, w.k, w.window, w.scale, st.max_attended)
+    say(f"[gpu] pinned pools: host {kp.data_ptr():#x} -> device {hs.kp:#x}")
+    hs.step()
+    torch.cuda.synchronize()
+    assert torch.equal(hs.scores, ref[0]) and torch.equal(hs.sel, ref[1])
+    assert torch.equal(hs.out, ref[2])
+    st.dense_attn()
+    hs.dense_attn()
+    torch.cuda.synchronize()
+    assert torch.equal(hs.out, st.out)
