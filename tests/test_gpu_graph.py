@@ -45,3 +45,48 @@ def test_graph_replays_match_eager(fused):
         assert torch.equal(st.scores, ref[0]), rep
         assert torch.equal(st.sel, ref[1]), rep
         assert torch.equal(st.out, ref[2]), rep
+
+
+
+def test_graph_replays_of_cached_and_zoom_calls():
+    """Cached-selection and multi-granularity attention captured in one graph:
+    every replay equals the eager result."""
+    import numpy as np
+    w = synth.make_workload(5, device="cuda", overrides=dict(B=2, seq_len=("fixed", 3000)))
+    st = zr.step_from_workload(w)
+    ss = torch.as_tensor(w.extra["sum_start"], device="cuda")
+    sl = torch.as_tensor(w.extra["sum_len"], device="cuda")
+    st.coarse_score()
+    st.select_topk()
+    c = w.extra["c"]
+    votes = torch.empty(w.n_total, dtype=torch.int32, device="cuda")
+    cons = torch.empty((w.B, c), dtype=torch.int32, device="cuda")
+    agree = torch.empty(w.B, dtype=torch.float32, device="cuda")
+    outz = torch.empty_like(st.out)
+    outc = torch.empty_like(st.out)
+
+    def work():
+        st.consensus(st.sel[None], c, votes, cons, agree)
+        st.zoom_attn(ss, sl, votes, cons, c, w.extra["prompt"], out=outz)
+        st.cached_attn(w.window + 3, out=outc)
+
+    work()
+    torch.cuda.synchronize()
+    ref = (votes.clone(), cons.clone(), agree.clone(), outz.clone(), outc.clone())
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            work()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in (votes, cons, outz, outc):
+            t.fill_(-3)
+        st.step()                # eager work between replays, same workspace
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((votes, cons, agree, outz, outc), ref):
+            assert torch.equal(a, b), rep

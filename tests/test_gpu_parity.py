@@ -154,7 +154,9 @@ def _small(cfg, **over):
 
 @pytest.mark.parametrize("dtype,d,Hq,Hkv", [("bf16", 128, 32, 8), ("bf16", 64, 8, 8),
                                              ("bf16", 128, 16, 8), ("f32", 128, 8, 1),
-                                             ("f32", 64, 16, 2), ("bf16", 64, 4, 2)])
+                                             ("f32", 64, 16, 2), ("bf16", 64, 4, 2),
+                                             ("bf16", 128, 32, 2), ("bf16", 64, 16, 1),
+                                             ("f32", 128, 16, 4)])
 def test_shapes_and_dtypes(dtype, d, Hq, Hkv):
     w = _small(1, dtype=dtype, d=d, Hq=Hq, Hkv=Hkv)
     run_and_check(w, f"shape-{dtype}-d{d}-G{Hq // Hkv}", check_dense=True)
@@ -314,3 +316,15 @@ def test_pools_in_pinned_host_memory():
     hs.dense_attn()
     torch.cuda.synchronize()
     assert torch.equal(hs.out, st.out)
+
+
+def test_many_pairs_and_largest_k():
+    """320 (sequence, KV head) pairs (each workgroup's threads own two pairs in
+    the work assignment) and k = 1024 (the built maximum; radix select over
+    more than 256 thoughts)."""
+    w = synth.make_workload(1, device="cuda", overrides=dict(
+        B=40, seq_len=("uniform", 16, 400), thought=("uniform", 2, 40)))
+    run_and_check(w, "pairs-320")
+    w = synth.make_workload(1, device="cuda", overrides=dict(
+        B=2, Hq=8, Hkv=2, seq_len=("fixed", 9000), thought=("uniform", 1, 5), k=1024))
+    run_and_check(w, "k-1024")
