@@ -86,6 +86,8 @@ def main():
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the attention figures on the ragged and 64K-token workloads")
     ap.add_argument("--no-offload", action="store_true",
                     help="skip the host-memory (PCIe) figure")
     ap.add_argument("--no-zoom", action="store_true",
@@ -298,6 +300,38 @@ def main():
                 "between_us_per_layer": round(between_us, 3),
                 "between_gbs": round(zbytes / (between_us * 1e-6) / 1e9, 1)}
 
+    # the same attention + combine kernels on the other scope workloads (4
+    # layer caches each, rotated): ragged batch 32 and 64K tokens x batch 4
+    others = None
+    if not args.no_others:
+        others = {}
+        for cid, label in ((3, "ragged-b32: batch 32, T ~ U[4096, 32768], thoughts U[32, 1024], "
+                               "top-8 + 128 window, interleaved blocks"),
+                           (4, "long-64k-b4: batch 4, 65536 tokens, thoughts log-U[32, 2048], "
+                               "top-16 + 256 window")):
+            ws_ = [synth.make_workload(cid, value_seed=3000 + l, device=dev) for l in range(4)]
+            ss_ = [zr.step_from_workload(w) for w in ws_]
+            byts = []
+            for w, st in zip(ws_, ss_):
+                st.step()
+                torch.cuda.synchronize()
+                a_ = zr.attended_counts(st.sel.cpu().numpy(), w.seq_lens, w.seq_ptr, w.th_start,
+                                        w.th_len, w.window)
+                byts.append(int(a_.sum()) * 2 * w.d * synth.ELEM_BYTES[w.dtype])
+            g_o = capture(lambda i: ss_[i % 4].cached_attn(ws_[i % 4].window), 40)
+            g_o.replay()
+            us_o = timed(g_o, 40)
+            g_s = capture(lambda i: ss_[i % 4].step(), 40)
+            g_s.replay()
+            us_s = timed(g_s, 40)
+            gbs = float(np.mean(byts)) / (us_o * 1e-6) / 1e9
+            others[ws_[0].name] = {"workload": label, "gathered_bytes": int(np.mean(byts)),
+                                   "attn_combine_us": round(us_o, 2), "gbs": round(gbs, 1),
+                                   "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                   "step_us": round(us_s, 2)}
+            del ws_, ss_, g_o, g_s
+            torch.cuda.empty_cache()
+
     # host-offloaded cache (ZoomR Sec. 3.4): layer 0's pools in pinned host
     # memory; the kernels read only the attended blocks over PCIe
     offload = None
@@ -367,6 +401,7 @@ def main():
         "selection_reuse": {"period_steps": R, "us_per_step": round(period_us, 3),
                             "steps_per_s": round(1e6 / period_us, 1)},
         "speedup_vs_dense_attention": round(dense_us / attn_us, 3),
+        "other_workloads": others,
         "zoomr_consensus": zoom,
         "host_offload": offload,
         "append_path": {"append_kv_us": round(append_us, 3),
