@@ -54,7 +54,9 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 
 // Exclusive prefix sum of one value per thread across the workgroup; *total
 // gets the sum. `tmp` holds kPairWaves ints. Contains barriers: every thread
-// must call it.
+// must call it. REUSE = false drops the closing barrier that lets `tmp` be
+// written again (for the workgroup's last scan).
+template <bool REUSE = true>
 __device__ int pair_exclusive_scan(int v, int* tmp, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int incl = wave_incl_sum(v);
@@ -67,7 +69,7 @@ __device__ int pair_exclusive_scan(int v, int* tmp, int* total) {
     before += w < wave ? x : 0;
     all += x;
   }
-  __syncthreads();
+  if (REUSE) __syncthreads();
   *total = all;
   return before + incl - v;
 }
@@ -77,32 +79,52 @@ __device__ __forceinline__ int blocks_of_span(int s, int e) {
 }
 
 // Dynamic LDS (int32 units), each region 4-int aligned:
-//   keys[max_per_seq]                 SELECT (order keys, zero padded)
+//   keys[max(max_per_seq, kRankMax)]  SELECT (order keys, zero padded)
 //   th_s[max_per_seq] th_l[...]       PLAN with staged thought spans
 //   sel_l[k]                          PLAN
-//   sp_s[k+1] sp_e[k+1] sp_pref[k+2]  PLAN
 //   bmask[ceil(max_blocks / 2)]       PLAN (two 16-bit slot masks per int)
 __host__ __device__ inline int up4(int x) { return (x + 3) & ~3; }
+
+// Size of the keys region: ranking reads up to kRankMax padded entries.
+__host__ __device__ inline int keys_ints(int max_per_seq) {
+  return up4(max_per_seq) > kRankMax ? up4(max_per_seq) : kRankMax;
+}
+
+// Block-table entries (and 16-bit bitmap slots) owned by each thread: up to
+// kBtRegs per thread they are prefetched into registers, and the count is
+// rounded up to a power of two from 2 so that a thread owns whole bitmap
+// words (bt_per / 2 of them, read and cleared with one vector access).
+__host__ __device__ inline int pair_bt_per(int max_blocks) {
+  int bt = (max_blocks + kPairThreads - 1) / kPairThreads;
+  if (bt > kBtRegs) return bt;
+  int r = 2;
+  while (r < bt) r <<= 1;
+  return r;
+}
+
+// Size of the bitmap region: every thread's whole words when prefetching,
+// else one word per two blocks.
+__host__ __device__ inline int bmask_ints(int max_blocks) {
+  const int bt = pair_bt_per(max_blocks);
+  return bt <= kBtRegs ? kPairThreads * bt / 2 : up4((max_blocks + 1) / 2);
+}
 
 struct PairLds {
   uint32_t* keys;
   int32_t* th_s;
   int32_t* th_l;
   int32_t* sel_l;
-  int32_t* sp_s;
-  int32_t* sp_e;
-  int32_t* sp_pref;
   uint32_t* bmask;
 };
 
 __host__ __device__ inline size_t pair_lds_ints(int max_per_seq, int k, int max_blocks,
                                                 bool select, bool plan, bool stage_th) {
   size_t n = 0;
-  if (select) n += up4(max_per_seq);
+  if (select) n += keys_ints(max_per_seq);
   if (plan) {
     if (stage_th) n += 2 * static_cast<size_t>(up4(max_per_seq));
-    n += up4(k) + 2 * static_cast<size_t>(up4(k + 1)) + up4(k + 2);
-    n += up4((max_blocks + 1) / 2);
+    n += up4(k);
+    n += bmask_ints(max_blocks);
   }
   return n;
 }
@@ -113,7 +135,7 @@ __device__ inline PairLds pair_lds(int32_t* dyn, int max_per_seq, int k, int max
   int32_t* c = dyn;
   if (select) {
     L.keys = reinterpret_cast<uint32_t*>(c);
-    c += up4(max_per_seq);
+    c += keys_ints(max_per_seq);
   }
   if (plan) {
     if (stage_th) {
@@ -124,12 +146,6 @@ __device__ inline PairLds pair_lds(int32_t* dyn, int max_per_seq, int k, int max
     }
     L.sel_l = c;
     c += up4(k);
-    L.sp_s = c;
-    c += up4(k + 1);
-    L.sp_e = c;
-    c += up4(k + 1);
-    L.sp_pref = c;
-    c += up4(k + 2);
     L.bmask = reinterpret_cast<uint32_t*>(c);
   }
   return L;
@@ -140,29 +156,47 @@ __device__ inline PairLds pair_lds(int32_t* dyn, int max_per_seq, int k, int max
 // L.sel_l (when PLAN) and to `out` (k ints).
 // ---------------------------------------------------------------------------
 
-// n <= kPairThreads: thread t ranks thought t by counting the thoughts
-// ahead of it. The order (larger key, then lower index) is the order of the
-// 64-bit composite key << 32 | ~index, so one unsigned compare per thought.
+// n <= kRankMax: thought i is ranked by counting the thoughts ahead of it
+// (a larger key, or the same key and a lower index); the k of rank < k win.
+// The keys are padded with zeros to np, a power of two from 32 to kRankMax
+// (a zero key at an index past n is never ahead of a real thought), and
+// S = kRankMax / np consecutive lanes share thought i, each counting over
+// np / S keys with 16-byte LDS reads, so that few reads are in flight per
+// lane before the counts are summed across the S lanes with DPP.
+__device__ __forceinline__ int rank_pad(int n) {
+  int np = 32;
+  while (np < n) np <<= 1;
+  return np;
+}
+
+// Entries of L.keys that must hold a key or a zero before a selection.
+__device__ __forceinline__ int keys_fill(int n) { return n <= kRankMax ? rank_pad(n) : up4(n); }
+
 template <bool PLAN>
-__device__ void select_by_rank(const PairLds& L, int n, int k, int32_t* out, int* wtmp,
-                               uint64_t* comp) {
+__device__ void select_by_rank(const PairLds& L, int n, int k, int32_t* out, int* wtmp) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const uint64_t mine =
-      t < n ? (static_cast<uint64_t>(L.keys[t]) << 32) | static_cast<uint32_t>(~t) : 0ull;
-  comp[t] = mine;  // entries past n are 0: never ahead of a real thought
-  __syncthreads();
-  bool take = false;
-  if (t < n) {
-    int rank = 0;
-    const ulonglong2* c2 = reinterpret_cast<const ulonglong2*>(comp);
+  const int np = rank_pad(n);
+  const int lgS = 8 - (31 - __builtin_clz(np));  // kRankMax = 256 = 2^8
+  const int S = 1 << lgS;
+  const int i = t >> lgS, q = t & (S - 1);
+  const int per4 = np >> (2 + lgS);  // 16-byte reads per lane
+  const uint32_t ki = L.keys[i];
+  const uint32_t ki1 = ki + 1u;      // keys at or after i must beat ki (no wrap: NaN -> 0, +inf < 2^32 - 1)
+  const uint4* k4 = reinterpret_cast<const uint4*>(L.keys) + q * per4;
+  int j = q * per4 * 4;
+  int cnt = 0;
 #pragma unroll 4
-    for (int j2 = 0; j2 < (n + 1) / 2; ++j2) {
-      const ulonglong2 v = c2[j2];
-      rank += v.x > mine ? 1 : 0;
-      rank += v.y > mine ? 1 : 0;
-    }
-    take = rank < k;
+  for (int r = 0; r < per4; ++r, j += 4) {
+    const uint4 v = k4[r];
+    cnt += v.x >= (j < i ? ki : ki1) ? 1 : 0;
+    cnt += v.y >= (j + 1 < i ? ki : ki1) ? 1 : 0;
+    cnt += v.z >= (j + 2 < i ? ki : ki1) ? 1 : 0;
+    cnt += v.w >= (j + 3 < i ? ki : ki1) ? 1 : 0;
   }
+  if (S >= 2) cnt += dpp_move<0xb1>(cnt);   // quad_perm [1,0,3,2]
+  if (S >= 4) cnt += dpp_move<0x4e>(cnt);   // quad_perm [2,3,0,1]
+  if (S >= 8) cnt += dpp_move<0x141>(cnt);  // half-row mirror: the other quad
+  const bool take = q == 0 && i < n && cnt < k;
   const uint64_t bal = __ballot(take);
   if (lane == 0) wtmp[wave] = __popcll(bal);
   __syncthreads();
@@ -171,8 +205,8 @@ __device__ void select_by_rank(const PairLds& L, int n, int k, int32_t* out, int
   for (int w = 0; w < kPairWaves; ++w) before += w < wave ? wtmp[w] : 0;
   if (take) {
     const int pos = before + __popcll(bal & ((1ull << lane) - 1ull));
-    out[pos] = t;
-    if (PLAN) L.sel_l[pos] = t;
+    out[pos] = i;
+    if (PLAN) L.sel_l[pos] = i;
   }
 }
 
@@ -287,12 +321,88 @@ __device__ __forceinline__ void or_span(uint32_t* bmask, int s, int e, int j0, i
   }
 }
 
+// Bitmap words owned by this thread (bt_per <= kBtRegs): W of them from
+// word threadIdx.x * W, as 4-, 8- or 16-byte LDS accesses.
+template <int W>
+__device__ __forceinline__ void own_words_load(const uint32_t* bmask, uint32_t (&w)[W]) {
+  const uint32_t* src = bmask + threadIdx.x * W;
+  if constexpr (W == 1) {
+    w[0] = src[0];
+  } else if constexpr (W == 2) {
+    const uint2 v = *reinterpret_cast<const uint2*>(src);
+    w[0] = v.x;
+    w[1] = v.y;
+  } else {
+#pragma unroll
+    for (int c = 0; c < W; c += 4) {
+      const uint4 v = *reinterpret_cast<const uint4*>(src + c);
+      w[c] = v.x;
+      w[c + 1] = v.y;
+      w[c + 2] = v.z;
+      w[c + 3] = v.w;
+    }
+  }
+}
+
+template <int W>
+__device__ __forceinline__ void own_words_clear(uint32_t* bmask) {
+  uint32_t* dst = bmask + threadIdx.x * W;
+  if constexpr (W == 1) {
+    dst[0] = 0u;
+  } else if constexpr (W == 2) {
+    *reinterpret_cast<uint2*>(dst) = make_uint2(0u, 0u);
+  } else {
+#pragma unroll
+    for (int c = 0; c < W; c += 4) *reinterpret_cast<uint4*>(dst + c) = make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
+// Zero the bitmap before the spans are ORed in: each thread its own words
+// when bt_per <= kBtRegs (the whole region), else the words of nb blocks.
+__device__ __forceinline__ void clear_bitmap(uint32_t* bmask, int bt_per, int nb) {
+  switch (bt_per) {
+    case 2: own_words_clear<1>(bmask); break;
+    case 4: own_words_clear<2>(bmask); break;
+    case 8: own_words_clear<4>(bmask); break;
+    case 16: own_words_clear<8>(bmask); break;
+    default:
+      for (int i = threadIdx.x; i < (nb + 1) / 2; i += kPairThreads) bmask[i] = 0u;
+  }
+}
+
 // The non-empty blocks of the bitmap in logical order -> the pair's list of
-// (physical block, slot mask) entries and its length. Block ids come from
-// the registers prefetched at kernel start (bt_pref) or from the table.
-// Contains barriers: every thread must call it.
-__device__ void emit_list(const PairArgs& a, const PairLds& L, int p, int b, int nb,
-                          bool bt_pref, const int (&btr)[kBtRegs], int* wtmp) {
+// (physical block, slot mask) entries and its length, with the block ids
+// prefetched into registers: thread t owns blocks [2Wt, 2W(t + 1)), whose
+// masks stay in registers between the count and the writes. Blocks past the
+// sequence have empty masks (the region is cleared whole).
+template <int W>
+__device__ void emit_list_regs(const PairArgs& a, int p, const uint32_t* bmask,
+                               const int (&btr)[kBtRegs], int* wtmp) {
+  uint32_t w[W];
+  own_words_load<W>(bmask, w);
+  int nz = 0;
+#pragma unroll
+  for (int j = 0; j < W; ++j) nz += ((w[j] & 0xffffu) != 0u ? 1 : 0) + ((w[j] >> 16) != 0u ? 1 : 0);
+  int n_list;
+  int pos = pair_exclusive_scan<false>(nz, wtmp, &n_list);
+  int2* ent = a.entries + static_cast<size_t>(p) * a.max_blocks;
+#pragma unroll
+  for (int j = 0; j < 2 * W; ++j) {
+    const uint32_t m = (w[j >> 1] >> (16 * (j & 1))) & 0xffffu;
+    if (m) {
+      const int pb = btr[j];
+      const bool ok = pb >= 0 && pb < a.num_blocks;
+      ent[pos++] = ok ? make_int2(pb, static_cast<int>(m)) : make_int2(0, 0);
+    }
+  }
+  if (threadIdx.x == 0) a.counts[p] = n_list;
+}
+
+// The same list for bt_per > kBtRegs: thread t owns blocks [t bt_per,
+// (t + 1) bt_per) and reads their ids from the table. Contains barriers:
+// every thread must call it (as must every thread call emit_list).
+__device__ void emit_list_table(const PairArgs& a, const PairLds& L, int p, int b, int nb,
+                                int* wtmp) {
   const int t = threadIdx.x;
   const int bl0 = t * a.bt_per;
   int nz = 0;
@@ -301,36 +411,32 @@ __device__ void emit_list(const PairArgs& a, const PairLds& L, int p, int b, int
     if (lb < nb) nz += ((L.bmask[lb >> 1] >> (16 * (lb & 1))) & 0xffffu) != 0u;
   }
   int n_list;
-  int pos = pair_exclusive_scan(nz, wtmp, &n_list);
+  int pos = pair_exclusive_scan<false>(nz, wtmp, &n_list);
   int2* ent = a.entries + static_cast<size_t>(p) * a.max_blocks;
   const int32_t* row = a.block_table + static_cast<size_t>(b) * a.max_blocks;
-  if (bt_pref) {
-#pragma unroll
-    for (int j = 0; j < kBtRegs; ++j) {
-      const int lb = bl0 + j;
-      if (j < a.bt_per && lb < nb) {
-        const uint32_t m = (L.bmask[lb >> 1] >> (16 * (lb & 1))) & 0xffffu;
-        if (m) {
-          const int pb = btr[j];
-          const bool ok = pb >= 0 && pb < a.num_blocks;
-          ent[pos++] = ok ? make_int2(pb, static_cast<int>(m)) : make_int2(0, 0);
-        }
-      }
-    }
-  } else {
-    for (int j = 0; j < a.bt_per; ++j) {
-      const int lb = bl0 + j;
-      if (lb < nb) {
-        const uint32_t m = (L.bmask[lb >> 1] >> (16 * (lb & 1))) & 0xffffu;
-        if (m) {
-          const int pb = row[lb];
-          const bool ok = pb >= 0 && pb < a.num_blocks;
-          ent[pos++] = ok ? make_int2(pb, static_cast<int>(m)) : make_int2(0, 0);
-        }
+  for (int j = 0; j < a.bt_per; ++j) {
+    const int lb = bl0 + j;
+    if (lb < nb) {
+      const uint32_t m = (L.bmask[lb >> 1] >> (16 * (lb & 1))) & 0xffffu;
+      if (m) {
+        const int pb = row[lb];
+        const bool ok = pb >= 0 && pb < a.num_blocks;
+        ent[pos++] = ok ? make_int2(pb, static_cast<int>(m)) : make_int2(0, 0);
       }
     }
   }
   if (t == 0) a.counts[p] = n_list;
+}
+
+__device__ void emit_list(const PairArgs& a, const PairLds& L, int p, int b, int nb,
+                          const int (&btr)[kBtRegs], int* wtmp) {
+  switch (a.bt_per) {
+    case 2: emit_list_regs<1>(a, p, L.bmask, btr, wtmp); break;
+    case 4: emit_list_regs<2>(a, p, L.bmask, btr, wtmp); break;
+    case 8: emit_list_regs<4>(a, p, L.bmask, btr, wtmp); break;
+    case 16: emit_list_regs<8>(a, p, L.bmask, btr, wtmp); break;
+    default: emit_list_table(a, L, p, b, nb, wtmp);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -349,7 +455,6 @@ pair_kernel(PairArgs a) {
   __shared__ int wtmp[kPairWaves];
   __shared__ uint32_t hist[kPairThreads];
   __shared__ uint32_t sh[2];
-  __shared__ uint64_t comp[kPairThreads];
 
   const int p = blockIdx.x, t = threadIdx.x;
   const int b = p / a.Hkv, g = p - b * a.Hkv;
@@ -419,7 +524,7 @@ pair_kernel(PairArgs a) {
     T = T < 0 ? 0 : (T > cap ? cap : T);
     tw = T - a.window > 0 ? T - a.window : 0;
     nb = (T + kBlock - 1) / kBlock;
-    for (int i = t; i < (nb + 1) / 2; i += kPairThreads) L.bmask[i] = 0u;
+    clear_bitmap(L.bmask, a.bt_per, nb);
     if (!SELECT) {
 #pragma unroll
       for (int j = 0; j < kSelRegs; ++j) {
@@ -479,7 +584,7 @@ pair_kernel(PairArgs a) {
       L.keys[i] = order_key(a.scores[static_cast<size_t>(lo + i) * a.Hkv + g]);
   }
   if (SELECT)
-    for (int i = n + t; i < up4(n); i += kPairThreads) L.keys[i] = 0u;
+    for (int i = n + t; i < keys_fill(n); i += kPairThreads) L.keys[i] = 0u;
   __syncthreads();
 
   if (SELECT && a.k > 0) {
@@ -491,7 +596,7 @@ pair_kernel(PairArgs a) {
         if (PLAN) L.sel_l[j] = v;
       }
     } else if (n <= kRankMax) {
-      select_by_rank<PLAN>(L, n, a.k, out, wtmp, comp);
+      select_by_rank<PLAN>(L, n, a.k, out, wtmp);
     } else {
       select_by_radix<PLAN>(L, n, a.k, out, hist, wtmp, sh);
     }
@@ -499,60 +604,30 @@ pair_kernel(PairArgs a) {
   }
 
   if (PLAN) {
-    // spans: the selected thoughts, clipped below the window start (the
-    // attention kernel adds the window itself); thread t owns a contiguous
-    // run of spans so the block-count scan follows span order
-    const int nsp = a.k;
-    const int per_s = (nsp + kPairThreads - 1) / kPairThreads;
-    const int s0 = t * per_s, s1 = s0 + per_s < nsp ? s0 + per_s : nsp;
-    int cnt = 0;
-    for (int i = s0; i < s1; ++i) {
-      int s = 0, e = 0;
+    // the selected thoughts' tokens below the window start (the attention
+    // kernel adds the window itself) into the slot bitmap: tps threads share
+    // one selected thought, each ORing every tps-th block of its span
+    int tps = kPairThreads;
+    while (tps > 1 && tps * a.k > kPairThreads) tps >>= 1;
+    const int lgt = __builtin_ctz(tps);
+    for (int i = t >> lgt; i < a.k; i += kPairThreads >> lgt) {
       const int th = L.sel_l[i];
-      if (th >= 0 && th < n) {
-        int ts, tl;
-        if (STH) {
-          ts = L.th_s[th];
-          tl = L.th_l[th];
-        } else {
-          ts = a.th_start[lo + th];
-          tl = a.th_len[lo + th];
-        }
-        s = ts > 0 ? ts : 0;
-        e = tl > 0 ? ts + tl : s;
-        e = e < tw ? e : tw;
-        e = e > s ? e : s;
+      if (th < 0 || th >= n) continue;
+      int ts, tl;
+      if (STH) {
+        ts = L.th_s[th];
+        tl = L.th_l[th];
+      } else {
+        ts = a.th_start[lo + th];
+        tl = a.th_len[lo + th];
       }
-      L.sp_s[i] = s;
-      L.sp_e[i] = e;
-      cnt += blocks_of_span(s, e);
-    }
-    int total;
-    int run = pair_exclusive_scan(cnt, wtmp, &total);
-    for (int i = s0; i < s1; ++i) {
-      L.sp_pref[i] = run;
-      run += blocks_of_span(L.sp_s[i], L.sp_e[i]);
-    }
-    if (t == 0) L.sp_pref[nsp] = total;
-    __syncthreads();
-    // every (span, block) item ORs its slots into the block's mask
-    for (int f = t; f < total; f += kPairThreads) {
-      int l = 0, h = nsp - 1;  // last span with sp_pref <= f (it holds item f)
-      while (l < h) {
-        const int mid = (l + h + 1) >> 1;
-        if (L.sp_pref[mid] <= f) l = mid;
-        else h = mid - 1;
-      }
-      const int s = L.sp_s[l], e = L.sp_e[l];
-      const int lb = (s >> 4) + (f - L.sp_pref[l]);
-      const int b0 = lb << 4;
-      const int from = (s > b0 ? s : b0) - b0;
-      const int to = (e < b0 + kBlock ? e : b0 + kBlock) - b0;
-      const uint32_t m = ((1u << to) - 1u) & ~((1u << from) - 1u);
-      atomicOr(&L.bmask[lb >> 1], m << (16 * (lb & 1)));
+      const int s = ts > 0 ? ts : 0;
+      int e = tl > 0 ? ts + tl : s;
+      e = e < tw ? e : tw;
+      if (e > s) or_span(L.bmask, s, e, t & (tps - 1), tps);
     }
     __syncthreads();
-    emit_list(a, L, p, b, nb, bt_pref, btr, wtmp);
+    emit_list(a, L, p, b, nb, btr, wtmp);
   }
 }
 
@@ -570,17 +645,16 @@ consensus_kernel(ConsArgs a) {
   __shared__ int wtmp[kPairWaves];
   __shared__ uint32_t hist[kPairThreads];
   __shared__ uint32_t sh[2];
-  __shared__ uint64_t comp[kPairThreads];
   __shared__ int tot_tmp[kPairWaves];
   const int b = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
   PairLds L{};
   L.keys = reinterpret_cast<uint32_t*>(dyn);
-  L.sel_l = dyn + up4(a.max_per_seq);
+  L.sel_l = dyn + keys_ints(a.max_per_seq);
   int lo = a.seq_ptr[b], hi = a.seq_ptr[b + 1];
   lo = lo < 0 ? 0 : (lo > a.n_total ? a.n_total : lo);
   hi = hi < lo ? lo : (hi > a.n_total ? a.n_total : hi);
   const int n = hi - lo < a.max_per_seq ? hi - lo : a.max_per_seq;
-  for (int i = t; i < up4(n); i += kPairThreads) L.keys[i] = 0u;
+  for (int i = t; i < keys_fill(n); i += kPairThreads) L.keys[i] = 0u;
   __syncthreads();
   const int rows = a.n_layers * a.Hkv;
   for (int e = t; e < rows * a.k; e += kPairThreads) {
@@ -603,7 +677,7 @@ consensus_kernel(ConsArgs a) {
       for (int j = t; j < n; j += kPairThreads) L.sel_l[j] = j;
       nsel = n;
     } else if (n <= kRankMax) {
-      select_by_rank<false>(L, n, a.c, L.sel_l, wtmp, comp);
+      select_by_rank<false>(L, n, a.c, L.sel_l, wtmp);
       nsel = a.c;
     } else {
       select_by_radix<false>(L, n, a.c, L.sel_l, hist, wtmp, sh);
@@ -672,7 +746,7 @@ zoom_plan_kernel(PairArgs a) {
   T = T < 0 ? 0 : (T > cap ? cap : T);
   const int tw = T - a.window > 0 ? T - a.window : 0;
   const int nb = (T + kBlock - 1) / kBlock;
-  for (int i = t; i < (nb + 1) / 2; i += kPairThreads) L.bmask[i] = 0u;
+  clear_bitmap(L.bmask, a.bt_per, nb);
   for (int i = t; i < n; i += kPairThreads) flag[i] = 0;
   __syncthreads();
   for (int j = t; j < a.c; j += kPairThreads) {
@@ -700,14 +774,14 @@ zoom_plan_kernel(PairArgs a) {
     if (e > s) or_span(L.bmask, s, e, 0, 1);
   }
   __syncthreads();
-  emit_list(a, L, p, b, nb, bt_pref, btr, wtmp);
+  emit_list(a, L, p, b, nb, btr, wtmp);
 }
 
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
 constexpr size_t kPairLdsLimit = 64 * 1024;
-constexpr size_t kPairStaticLds = (kPairWaves + kPairThreads + 2) * sizeof(int32_t) + kPairThreads * sizeof(uint64_t);
+constexpr size_t kPairStaticLds = (kPairWaves + kPairThreads + 2) * sizeof(int32_t);
 
 static size_t pair_dyn_lds(const PairArgs& a, bool select, bool plan) {
   return pair_lds_ints(a.max_per_seq, a.k, a.max_blocks, select, plan, a.stage_th != 0) *
@@ -722,7 +796,7 @@ bool pair_lds_ok(const zr_geom& gm, int max_per_seq, int k, bool select, bool pl
 
 template <typename E, int D, bool SCORE, bool SELECT, bool PLAN>
 static hipError_t launch_pair_t(const zr_geom& gm, PairArgs a, hipStream_t s) {
-  a.bt_per = (gm.max_blocks_per_seq + kPairThreads - 1) / kPairThreads;
+  a.bt_per = pair_bt_per(gm.max_blocks_per_seq);
   a.stage_th = 0;
   if (PLAN) {
     PairArgs b2 = a;
@@ -770,7 +844,7 @@ hipError_t launch_pair(const zr_geom& gm, const PairArgs& a, int mode, hipStream
 namespace zr {
 
 static size_t consensus_lds(int max_per_seq, int c) {
-  return (static_cast<size_t>(up4(max_per_seq)) + up4(c)) * sizeof(int32_t);
+  return (static_cast<size_t>(keys_ints(max_per_seq)) + up4(c)) * sizeof(int32_t);
 }
 
 bool consensus_lds_ok(int max_per_seq, int c) {
@@ -785,7 +859,7 @@ hipError_t launch_consensus(const ConsArgs& a, hipStream_t s) {
 }
 
 static size_t zoom_lds(const zr_geom& gm, int max_per_seq) {
-  return (static_cast<size_t>(up4(max_per_seq)) + up4((gm.max_blocks_per_seq + 1) / 2)) *
+  return (static_cast<size_t>(up4(max_per_seq)) + bmask_ints(gm.max_blocks_per_seq)) *
          sizeof(int32_t);
 }
 
@@ -796,7 +870,7 @@ bool zoom_lds_ok(const zr_geom& gm, int max_per_seq) {
 hipError_t launch_zoom_plan(const zr_geom& gm, const PairArgs& a0, hipStream_t s) {
   if (gm.batch == 0) return hipSuccess;
   PairArgs a = a0;
-  a.bt_per = (gm.max_blocks_per_seq + kPairThreads - 1) / kPairThreads;
+  a.bt_per = pair_bt_per(gm.max_blocks_per_seq);
   hipLaunchKernelGGL(zoom_plan_kernel, dim3(gm.batch * gm.n_kv_heads), dim3(kPairThreads),
                      zoom_lds(gm, a.max_per_seq), s, a);
   return hipGetLastError();
