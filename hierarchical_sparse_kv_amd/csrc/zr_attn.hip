@@ -9,17 +9,19 @@
 // attended slots enter the softmax; the gather reads the listed blocks, it
 // does not mask a full read.
 //
-// Work split. The grid is sized once for the whole GPU (about `nwg`
-// workgroups). Every workgroup reads all pairs' list lengths n_p and gives
-// pair p a number of workgroups proportional to its length,
-// S_p = max(1, round(n_p / per)), per = ceil(total / nwg), so each workgroup
-// serves one pair with about `per` blocks however ragged the pairs are. Its
-// 4 waves take chunks of NBW blocks in turn: a wave loads all its entries at
-// once (one lane per entry), then streams its chunks with the next chunk's
-// K/V loads in flight while the current one is computed, keeping a running
-// (max, sum, weighted V) per query head (online softmax across chunks,
-// two-pass inside one). The waves merge in LDS into one partial per
-// workgroup; a combine kernel merges each pair's partials by log-sum-exp.
+// Work split. The grid is sized once for the whole GPU (`nwg` workgroups).
+// Every workgroup reads all pairs' list lengths n_p and takes an equal range
+// (total / nwg entries, rounded down or up) of the pairs' lists laid end to
+// end, so every workgroup streams the same number of blocks however ragged
+// the pairs are; a range that crosses pairs is processed as one segment per
+// pair. For
+// each segment the 4 waves take chunks of NBW blocks in turn: a wave loads
+// all its entries at once (one lane per entry), then streams its chunks with
+// the next chunk's K/V loads in flight while the current one is computed,
+// keeping a running (max, sum, weighted V) per query head (online softmax
+// across chunks, two-pass inside one). The waves merge in LDS into one
+// partial per segment; a combine kernel merges each pair's partials by
+// log-sum-exp.
 // (Merging inside the attention kernel would need a device-scope
 // release/acquire per workgroup, which on this GPU writes back and
 // invalidates the whole L2; the kernel boundary is far cheaper.)
@@ -41,6 +43,8 @@
 //
 // Exponentials are base 2 with the scale folded in (exp(x) = 2^(x log2 e)).
 #include <math.h>
+
+#include <type_traits>
 
 #include "zr_internal.h"
 
@@ -68,12 +72,26 @@ __device__ __forceinline__ int cached_len(const AttnArgs& a, int b) {
   return T < 0 ? 0 : (T > cap ? cap : T);
 }
 
+// The pairs' lists, concatenated in pair order (total entries), are cut into
+// nr = min(nwg, total) ranges: workgroup w takes entries [R(w), R(w + 1)) of
+// the concatenation, R(w) = floor(w total / nr), so the workgroups' block
+// counts differ by at most one however ragged the pairs are (and no range is
+// empty). A range that crosses
+// the end of a pair is split into segments, one per pair met, each merged
+// into a partial of its own. Pair p (entries [start_p, start_p + n_p) of the
+// concatenation) is met by the workgroups w0_p = W(start_p) ..
+// W(start_p + n_p - 1), W(x) = the range holding entry x; its partials take
+// slots [base_p, base_p + S_p) (base = exclusive prefix of the S_p), segment
+// (p, w) the slot base_p + w - w0_p. Workgroup 0 publishes
+// base_p (ws_pref) for the combine kernel. Every workgroup computes the
+// whole plan itself from the lists' lengths.
 struct Assign {
   int p;       // pair
   int T;       // cached tokens of the pair's sequence
   int tw;      // first window token (dense: 0)
   int ncache;  // leading list entries read from the block lists (dense: 0)
   int lo, hi;  // entries [lo, hi) of the pair's list
+  int slot;    // partial slot
 };
 
 // A pair's list: its ncache span entries (sparse), then the blocks of the
@@ -97,119 +115,298 @@ __device__ __forceinline__ PairList pair_list(const AttnArgs& a, int p) {
   return r;
 }
 
-// Workgroups per pair and this workgroup's share. With per = ceil(total /
-// nwg), pair p gets S_p = max(1, round(n_p / per)) workgroups (0 when
-// n_p = 0), each an equal slice of its list. Workgroup 0 publishes the first
-// workgroup of every pair for the combine kernel. Returns false when this
-// workgroup has no work (uniform over the workgroup).
-//
-// Up to 64 pairs every wave computes the whole assignment by itself (one
-// pair per lane, DPP scans), with no LDS and no workgroup barrier.
-template <bool DENSE>
-__device__ bool assign_work_wave(const AttnArgs& a, Assign* as) {
-  const int P = a.B * a.Hkv;
-  const int lane = threadIdx.x & 63, w = blockIdx.x;
-  PairList pl{0, 0, 0, 0};
-  if (lane < P) pl = pair_list<DENSE>(a, lane);
-  const int n = pl.n;
-  const int total = wave_sum(n);
-  const int per = total > 0 ? (total + a.nwg - 1) / a.nwg : 1;
-  const int S = n > 0 ? max(1, (n + per / 2) / per) : 0;
-  const int incl = wave_incl_sum(S);
-  const int total_s = __builtin_amdgcn_readlane(incl, 63);
-  const int run = incl - S;
-  if (w == 0 && threadIdx.x < 64) {
-    if (lane < P) a.ws_pref[lane] = run;
-    if (lane == 0) a.ws_pref[P] = total_s;
-  }
-  if (w >= total_s) return false;  // uniform over the workgroup
-  const uint64_t own = __ballot(lane < P && w >= run && w < run + S);
-  const int p = __ffsll(static_cast<unsigned long long>(own)) - 1;
-  const int r = w - __builtin_amdgcn_readlane(run, p);
-  const int Sp = __builtin_amdgcn_readlane(S, p);
-  const int64_t np = __builtin_amdgcn_readlane(n, p);
-  as->p = p;
-  as->T = __builtin_amdgcn_readlane(pl.T, p);
-  as->tw = __builtin_amdgcn_readlane(pl.tw, p);
-  as->ncache = __builtin_amdgcn_readlane(pl.ncache, p);
-  as->lo = static_cast<int>(r * np / Sp);
-  as->hi = static_cast<int>((r + 1) * np / Sp);
-  return true;
+// First entry of range w, R(w) = floor(w total / nr), and the range W(x)
+// holding entry x (the largest w with R(w) <= x), for nr <= total ranges.
+// The quotients are taken in float64: numerator and denominator are exact
+// integers below 2^52, so the rounded quotient never crosses the integer
+// above the exact one (they differ by at least 1 / denominator, more than an
+// ulp), and the floor is exact; integer 64-bit division is a long sequence.
+__device__ __forceinline__ int floor_div(int64_t n, int d) {
+  return static_cast<int>(floor(static_cast<double>(n) / static_cast<double>(d)));
+}
+__device__ __forceinline__ int range_start(int w, int total, int nr) {
+  return floor_div(static_cast<int64_t>(w) * total, nr);
+}
+__device__ __forceinline__ int range_of(int x, int total, int nr) {
+  return floor_div((static_cast<int64_t>(x) + 1) * nr - 1, total);
 }
 
-// More pairs: thread t owns a contiguous run of pairs; workgroup sums and
-// scans through LDS.
+// Partial slots of a pair whose entries are [s, s + n) of the concatenation.
+__device__ __forceinline__ int pair_slots(int s, int n, int total, int nr) {
+  return n > 0 ? range_of(s + n - 1, total, nr) - range_of(s, total, nr) + 1 : 0;
+}
+
+// The segments reach the kernel body as LDS records, up to kMaxSeg at a
+// time. A range can meet more than kMaxSeg pairs only when they are short
+// and more than 64; every segment between the first and the last of a range
+// is then a whole pair with one partial, so the next records follow from
+// where the last one ended (next pair, its position in the concatenation,
+// its slot).
+constexpr int kMaxSeg = 64;
+struct PlanLds {
+  int tmp[kWaves];
+  int nrec;                 // records in rec
+  int next_p, next_pos, next_slot, r1;
+  int4 rec[kMaxSeg][2];     // {p, T, tw, ncache}, {lo, hi, slot, -}
+};
+
+__device__ __forceinline__ void put_record(PlanLds& sm, int i, int p, int T, int tw, int ncache,
+                                           int lo, int hi, int slot) {
+  sm.rec[i][0] = make_int4(p, T, tw, ncache);
+  sm.rec[i][1] = make_int4(lo, hi, slot, 0);
+}
+
+// (The values are the same in every lane: readfirstlane keeps them, and all
+// that is derived from them, in scalar registers.)
+__device__ __forceinline__ void get_record(const PlanLds& sm, int i, Assign* as) {
+  const int4 r0 = sm.rec[i][0], r1 = sm.rec[i][1];
+  as->p = __builtin_amdgcn_readfirstlane(r0.x);
+  as->T = __builtin_amdgcn_readfirstlane(r0.y);
+  as->tw = __builtin_amdgcn_readfirstlane(r0.z);
+  as->ncache = __builtin_amdgcn_readfirstlane(r0.w);
+  as->lo = __builtin_amdgcn_readfirstlane(r1.x);
+  as->hi = __builtin_amdgcn_readfirstlane(r1.y);
+  as->slot = __builtin_amdgcn_readfirstlane(r1.z);
+}
+
+// Up to 64 pairs every wave computes the plan by itself (one pair per lane,
+// DPP scans) and takes its first two segments into scalar registers, with
+// no LDS and no barrier; the records are written to LDS (the same values by
+// every wave) only when asked for or when there are more than two segments.
+// Returns the number of segments.
+//
+// Where whole-pair slices are about as even, they are used instead of the
+// ranges: pair p gets S_p = max(1, round(n_p / per)) workgroups (per =
+// ceil(total / nwg)), each an equal slice of its list, one segment per
+// workgroup, slot = workgroup. That is chosen when it needs no more than nwg
+// workgroups and no slice is longer than the ranges' largest plus 1/8:
+// one segment per workgroup and fewer partials then beat the exact balance.
+__device__ __forceinline__ void lane_segment(int p, int T, int tw, int ncache, int lo, int hi,
+                                             int slot, Assign* as) {
+  as->p = p;
+  as->T = __builtin_amdgcn_readlane(T, p);
+  as->tw = __builtin_amdgcn_readlane(tw, p);
+  as->ncache = __builtin_amdgcn_readlane(ncache, p);
+  as->lo = __builtin_amdgcn_readlane(lo, p);
+  as->hi = __builtin_amdgcn_readlane(hi, p);
+  as->slot = __builtin_amdgcn_readlane(slot, p);
+}
+
 template <bool DENSE>
-__device__ bool assign_work(const AttnArgs& a, int* tmp_n, int* tmp_s, int* sh, Assign* as) {
+__device__ int plan_wave(const AttnArgs& a, PlanLds& sm, bool records, Assign* sa, Assign* sb) {
   const int P = a.B * a.Hkv;
-  if (P <= 64) return assign_work_wave<DENSE>(a, as);
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, w = blockIdx.x;
+  const int lane = threadIdx.x & 63, w = blockIdx.x;
+  const bool publish = w == 0 && threadIdx.x < 64;
+  PairList L{0, 0, 0, 0};
+  if (lane < P) L = pair_list<DENSE>(a, lane);
+  const int incl = wave_incl_sum(L.n);
+  const int total = __builtin_amdgcn_readlane(incl, 63);
+  const int start = incl - L.n, end = incl;
+  const int nr = total < a.nwg ? total : a.nwg;  // ranges: none empty
+  // whole-pair slices
+  const int per = total > 0 ? (total + a.nwg - 1) / a.nwg : 1;
+  const int S = L.n > 0 ? max(1, (L.n + per / 2) / per) : 0;
+  const int sincl = wave_incl_sum(S);
+  const int total_s = __builtin_amdgcn_readlane(sincl, 63);
+  // every slice within 1/8 of the ranges' largest: n_p <= S_p * cap
+  const int range_max = nr > 0 ? (total + nr - 1) / nr : 0;
+  const int cap = range_max + range_max / 8;
+  const bool even = __ballot(L.n > S * cap) == 0ull;
+  if (total_s <= a.nwg && even) {  // uniform
+    const int run = sincl - S;
+    if (publish) {
+      if (lane < P) a.ws_pref[lane] = run;
+      if (lane == 0) a.ws_pref[P] = total_s;
+    }
+    if (w >= total_s) return 0;
+    const bool mine = lane < P && w >= run && w < run + S;
+    const int r = w - run;
+    const int lo = mine ? floor_div(static_cast<int64_t>(r) * L.n, S) : 0;
+    const int hi = mine ? floor_div(static_cast<int64_t>(r + 1) * L.n, S) : 0;
+    const int p = __ffsll(static_cast<unsigned long long>(__ballot(mine))) - 1;
+    lane_segment(p, L.T, L.tw, L.ncache, lo, hi, w, sa);
+    if (records && mine) put_record(sm, 0, lane, L.T, L.tw, L.ncache, lo, hi, w);
+    return 1;
+  }
+  // ranges
+  const int ns = pair_slots(start, L.n, total, nr);
+  const int rincl = wave_incl_sum(ns);
+  const int base = rincl - ns;
+  if (publish) {
+    if (lane < P) a.ws_pref[lane] = base;
+    if (lane == 0) a.ws_pref[P] = __builtin_amdgcn_readlane(rincl, 63);
+  }
+  const int R0 = w < nr ? range_start(w, total, nr) : total;
+  const int R1 = w < nr ? range_start(w + 1, total, nr) : total;
+  const bool mine = lane < P && L.n > 0 && start < R1 && end > R0;
+  const uint64_t mask = __ballot(mine);
+  const int nseg = __popcll(mask);
+  const int lo = (start > R0 ? start : R0) - start, hi = (end < R1 ? end : R1) - start;
+  const int slot = mine ? base + w - range_of(start, total, nr) : 0;
+  if (nseg >= 1) lane_segment(__ffsll(static_cast<unsigned long long>(mask)) - 1, L.T, L.tw,
+                              L.ncache, lo, hi, slot, sa);
+  if (nseg >= 2) lane_segment(__ffsll(static_cast<unsigned long long>(mask & (mask - 1))) - 1,
+                              L.T, L.tw, L.ncache, lo, hi, slot, sb);
+  if ((records || nseg > 2) && mine)
+    put_record(sm, __popcll(mask & ((1ull << lane) - 1ull)), lane, L.T, L.tw, L.ncache, lo, hi,
+               slot);
+  return nseg;
+}
+
+// More pairs: thread t owns a contiguous run of pairs, and the scans go
+// through LDS. Writes the first kMaxSeg records and the continuation state,
+// returns the number of segments (uniform). Contains barriers: every thread
+// must call it.
+template <bool DENSE>
+__device__ int plan_block(const AttnArgs& a, PlanLds& sm) {
+  const int P = a.B * a.Hkv;
+  const int t = threadIdx.x, w = blockIdx.x;
   const int per_t = (P + kThreads - 1) / kThreads;  // <= kPairsPerThread
   const int p0 = t * per_t;
-  int nreg[kPairsPerThread];
+  int nreg[kPairsPerThread], treg[kPairsPerThread], creg[kPairsPerThread];
   int mine = 0;
 #pragma unroll
   for (int j = 0; j < kPairsPerThread; ++j) {
     const int p = p0 + j;
-    int n = 0;
-    if (j < per_t && p < P) n = pair_list<DENSE>(a, p).n;
-    nreg[j] = n;
-    mine += n;
+    PairList L{0, 0, 0, 0};
+    if (j < per_t && p < P) L = pair_list<DENSE>(a, p);
+    nreg[j] = L.n;
+    treg[j] = L.T;
+    creg[j] = L.ncache;
+    mine += L.n;
   }
-  // total list length
-  const int wsum = wave_sum(mine);
-  if (lane == 0) tmp_n[wave] = wsum;
-  __syncthreads();
-  int total = 0;
-#pragma unroll
-  for (int v = 0; v < kWaves; ++v) total += tmp_n[v];
-  const int per = total > 0 ? (total + a.nwg - 1) / a.nwg : 1;
-  // workgroups per pair, prefix over pairs
+  int total;
+  const int run = wg_exclusive_scan<kWaves>(mine, sm.tmp, &total);
+  const int nr = total < a.nwg ? total : a.nwg;  // ranges: none empty
   int ms = 0;
+  {
+    int st = run;
 #pragma unroll
-  for (int j = 0; j < kPairsPerThread; ++j)
-    ms += nreg[j] > 0 ? max(1, (nreg[j] + per / 2) / per) : 0;
-  const int incl = wave_incl_sum(ms);
-  if (lane == 63) tmp_s[wave] = incl;
-  __syncthreads();
-  int run = incl - ms, total_s = 0;
-#pragma unroll
-  for (int v = 0; v < kWaves; ++v) {
-    run += v < wave ? tmp_s[v] : 0;
-    total_s += tmp_s[v];
-  }
-#pragma unroll
-  for (int j = 0; j < kPairsPerThread; ++j) {
-    const int p = p0 + j;
-    if (j < per_t && p < P) {
-      const int n = nreg[j];
-      const int S = n > 0 ? max(1, (n + per / 2) / per) : 0;
-      if (w >= run && w < run + S) {
-        const PairList pl = pair_list<DENSE>(a, p);  // this thread read it a moment ago
-        sh[0] = p;
-        sh[1] = w - run;
-        sh[2] = S;
-        sh[3] = n;
-        sh[4] = pl.T;
-        sh[5] = pl.tw;
-        sh[6] = pl.ncache;
-      }
-      if (w == 0) a.ws_pref[p] = run;
-      run += S;
+    for (int j = 0; j < kPairsPerThread; ++j) {
+      ms += pair_slots(st, nreg[j], total, nr);
+      st += nreg[j];
     }
   }
-  if (w == 0 && t == 0) a.ws_pref[P] = total_s;
-  if (w >= total_s) return false;  // uniform: total_s is the same in every thread
+  int total_slots;
+  const int sbase = wg_exclusive_scan<kWaves>(ms, sm.tmp, &total_slots);
+  const int R0 = w < nr ? range_start(w, total, nr) : total;
+  const int R1 = w < nr ? range_start(w + 1, total, nr) : total;
+  int cnt = 0;
+  {
+    int st = run, bs = sbase;
+#pragma unroll
+    for (int j = 0; j < kPairsPerThread; ++j) {
+      const int p = p0 + j, n = nreg[j];
+      if (w == 0 && j < per_t && p < P) a.ws_pref[p] = bs;
+      cnt += n > 0 && st < R1 && st + n > R0 ? 1 : 0;
+      bs += pair_slots(st, n, total, nr);
+      st += n;
+    }
+  }
+  if (w == 0 && t == 0) a.ws_pref[P] = total_slots;
+  int nseg;
+  int ord = wg_exclusive_scan<kWaves>(cnt, sm.tmp, &nseg);
+  {
+    int st = run, bs = sbase;
+#pragma unroll
+    for (int j = 0; j < kPairsPerThread; ++j) {
+      const int n = nreg[j], e = st + n;
+      if (n > 0 && st < R1 && e > R0) {
+        const int slot = bs + w - range_of(st, total, nr);
+        if (ord < kMaxSeg)
+          put_record(sm, ord, p0 + j, treg[j],
+                     DENSE ? 0 : (treg[j] - a.window > 0 ? treg[j] - a.window : 0), creg[j],
+                     (st > R0 ? st : R0) - st, (e < R1 ? e : R1) - st, slot);
+        if (ord == kMaxSeg - 1) {  // more segments follow only if this one ends inside
+          sm.next_p = p0 + j + 1;
+          sm.next_pos = e;
+          sm.next_slot = slot + 1;
+        }
+        ++ord;
+      }
+      bs += pair_slots(st, n, total, nr);
+      st += n;
+    }
+  }
+  if (t == 0) {
+    sm.nrec = nseg < kMaxSeg ? nseg : kMaxSeg;
+    sm.r1 = R1;
+  }
   __syncthreads();
-  const int p = sh[0], r = sh[1], S = sh[2];
-  const int64_t n = sh[3];
-  as->p = p;
-  as->T = sh[4];
-  as->tw = sh[5];
-  as->ncache = sh[6];
-  as->lo = static_cast<int>(r * n / S);
-  as->hi = static_cast<int>((r + 1) * n / S);
-  return true;
+  return nseg;
+}
+
+// The next records after a full batch (workgroups of more than kMaxSeg
+// segments): wave 0 walks the pairs from next_p, 64 at a time, and every
+// non-empty pair whose start is below the range end gives a record (the
+// last one clipped at the range end). Contains barriers: every thread must
+// call it. Returns the number of records (uniform, > 0 while segments
+// remain).
+template <bool DENSE>
+__device__ int plan_next(const AttnArgs& a, PlanLds& sm) {
+  __syncthreads();  // every thread has read the previous records
+  if (threadIdx.x < 64) {
+    const int P = a.B * a.Hkv, lane = threadIdx.x;
+    int p = sm.next_p, pos = sm.next_pos, slot = sm.next_slot;
+    const int r1 = sm.r1;
+    int cnt = 0;
+    while (cnt < kMaxSeg && pos < r1 && p < P) {
+      const int q = p + lane;
+      PairList L{0, 0, 0, 0};
+      if (q < P) L = pair_list<DENSE>(a, q);
+      const int incl = wave_incl_sum(L.n);
+      const int st = pos + incl - L.n, e = st + L.n;
+      const bool take = q < P && L.n > 0 && st < r1;
+      const uint64_t bal = __ballot(take);
+      const int ord = cnt + __popcll(bal & ((1ull << lane) - 1ull));
+      const bool put = take && ord < kMaxSeg;
+      if (put)
+        put_record(sm, ord, q, L.T, L.tw, L.ncache, 0, (e < r1 ? e : r1) - st,
+                   slot + ord - cnt);
+      // go on after the last pair put when the record cap cut the batch,
+      // else after all 64
+      const uint64_t bput = __ballot(put);
+      const int nput = __popcll(bput);
+      if (nput < __popcll(bal)) {
+        const int last = 63 - __builtin_clzll(bput);
+        p = p + last + 1;
+        pos = __builtin_amdgcn_readlane(e, last);
+      } else {
+        p += 64;
+        pos += __builtin_amdgcn_readlane(incl, 63);
+      }
+      slot += nput;
+      cnt += nput;
+    }
+    if (lane == 0) {
+      sm.nrec = cnt;
+      sm.next_p = p;
+      sm.next_pos = pos;
+      sm.next_slot = slot;
+    }
+  }
+  __syncthreads();
+  return sm.nrec;
+}
+
+// This workgroup's number of segments (uniform) and its first two segments
+// (*sa, *sb, scalar). The records [0, kMaxSeg) are in sm.rec, behind a
+// barrier, when `records` is set or there are more than two segments.
+// Contains barriers: every thread must call it.
+template <bool DENSE>
+__device__ int plan_work(const AttnArgs& a, PlanLds& sm, bool records, Assign* sa, Assign* sb) {
+  if (a.B * a.Hkv > 64) {
+    const int nseg = plan_block<DENSE>(a, sm);
+    if (nseg >= 1) get_record(sm, 0, sa);
+    if (nseg >= 2) get_record(sm, 1, sb);
+    return nseg;
+  }
+  const int nseg = plan_wave<DENSE>(a, sm, records, sa, sb);
+  if (records || nseg > 2) {  // uniform
+    if (threadIdx.x == 0) sm.nrec = nseg;
+    __syncthreads();
+  }
+  return nseg;
 }
 
 // Entry j of the pair's list -> physical block and slot mask ((0, 0) when j
@@ -258,9 +455,9 @@ __device__ __forceinline__ int wave_chunks(const Assign& as, int wave) {
 // Merge the waves' (m, l, acc) and write this workgroup's partial.
 // red_m / red_l: [kWaves][G]; red_o: [kWaves][G][D].
 template <int G, int D>
-__device__ void write_partial(const AttnArgs& a, const float (*red_m)[G],
+__device__ void write_partial(const AttnArgs& a, int slot_i, const float (*red_m)[G],
                               const float (*red_l)[G], const float (*red_o)[G][D]) {
-  const size_t slot = blockIdx.x;
+  const size_t slot = static_cast<size_t>(slot_i);
   for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
     const int h = idx / D, e = idx % D;
     float M = kNegInf;
@@ -425,60 +622,15 @@ __device__ __forceinline__ void compute_chunk(const AttnArgs& a, Chunk<D, NBW>& 
   }
 }
 
-template <int G, int D, int NBW, bool DENSE>
-__global__ void __launch_bounds__(kThreads, 2)
-attn_mfma_kernel(AttnArgs a) {
-  constexpr int KS = D / 32, NT = D / 16;
-  constexpr int EPB = 64;  // entries resolved per batch (one per lane)
-  __shared__ float red_m[kWaves][G];
-  __shared__ float red_l[kWaves][G];
-  __shared__ float red_o[kWaves][G][D];
-  __shared__ int tmp_n[kWaves], tmp_s[kWaves];
-  __shared__ int sh_as[8];
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// A wave's running state -> LDS slot (segment s, wave): m and l of head
+// h = l16; O rows are heads 4 lg + r.
+template <int G, int D>
+__device__ __forceinline__ void flush_state(const MfmaState& stt, const f32x4 (&o)[D / 16],
+                                            float (*red_m)[G], float (*red_l)[G],
+                                            float (*red_o)[G][D]) {
+  constexpr int NT = D / 16;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int l16 = lane & 15, lg = lane >> 4;
-  Assign as;
-  if (!assign_work<DENSE>(a, tmp_n, tmp_s, sh_as, &as)) return;
-  const int b = as.p / a.Hkv, g = as.p % a.Hkv;
-
-  // Q^T as the B operand: lane holds head l16, dims 32 kk + 8 lg .. +7
-  bf16x8 qop[KS];
-  {
-    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
-                           (static_cast<size_t>(b) * a.Hq + g * G + (l16 < G ? l16 : 0)) * D;
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      const bf16x8 qv = *reinterpret_cast<const bf16x8*>(qrow + 32 * kk + 8 * lg);
-      qop[kk] = l16 < G ? qv : bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
-    }
-  }
-  f32x4 o[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  MfmaState stt{kNegInf, 0.f, true};
-
-  const int nck_all = wave_chunks<NBW>(as, wave);
-  constexpr int CPB = EPB / NBW;  // chunks per batch
-  for (int c0 = 0; c0 < nck_all; c0 += CPB) {
-    // one lane per entry: resolve this batch's block-table entries at once
-    int pb_l;
-    uint32_t msk_l;
-    resolve_entry<DENSE>(a, as, b, wave_entry<NBW>(as, wave, c0 * NBW + lane), &pb_l, &msk_l);
-    const int nck = nck_all - c0 < CPB ? nck_all - c0 : CPB;
-    Chunk<D, NBW> cA, cB;
-    load_chunk<D, NBW>(a, g, 0, pb_l, msk_l, cA);
-    for (int c = 0; c < nck; c += 2) {
-      if (c + 1 < nck) load_chunk<D, NBW>(a, g, c + 1, pb_l, msk_l, cB);
-      compute_chunk<D, NBW>(a, cA, qop, o, stt);
-      if (c + 1 < nck) {
-        if (c + 2 < nck) load_chunk<D, NBW>(a, g, c + 2, pb_l, msk_l, cA);
-        compute_chunk<D, NBW>(a, cB, qop, o, stt);
-      }
-    }
-  }
-
-  // per-wave results -> LDS: head h = l16 for m and l; O rows are heads 4 lg + r
   float l_run = stt.l_run;
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
@@ -494,8 +646,165 @@ attn_mfma_kernel(AttnArgs a) {
       for (int nt = 0; nt < NT; ++nt) red_o[wave][h][16 * nt + l16] = o[nt][r];
     }
   }
-  __syncthreads();
-  write_partial<G, D>(a, red_m, red_l, red_o);
+}
+
+// Q^T of pair p as the B operand: lane holds head l16, dims 32 kk + 8 lg .. +7.
+template <int G, int D>
+__device__ __forceinline__ void load_q(const AttnArgs& a, int p, bf16x8 (&qop)[D / 32]) {
+  const int lane = threadIdx.x & 63, l16 = lane & 15, lg = lane >> 4;
+  const int b = p / a.Hkv, g = p - b * a.Hkv;
+  const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
+                         (static_cast<size_t>(b) * a.Hq + g * G + (l16 < G ? l16 : 0)) * D;
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk) {
+    const bf16x8 qv = *reinterpret_cast<const bf16x8*>(qrow + 32 * kk + 8 * lg);
+    qop[kk] = l16 < G ? qv : bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+}
+
+// One or two segments (A, then B) streamed as one sequence of chunks: the
+// chunks of A, then those of B, dealt round-robin to the waves, so both
+// segments share one pipeline and the waves stay balanced. A wave that
+// crosses from A to B stores its A state to LDS slot 0 and starts B with
+// B's query (kept in LDS: each lane reads back what it wrote itself). Three
+// or more segments (short pairs) are taken one after the other.
+template <int G, int D, int NBW, bool DENSE>
+__global__ void __launch_bounds__(kThreads, 2)
+attn_mfma_kernel(AttnArgs a) {
+  constexpr int KS = D / 32, NT = D / 16;
+  constexpr int EPB = 64;         // entries resolved per batch (one per lane)
+  constexpr int CPB = EPB / NBW;  // chunks per batch
+  __shared__ float red_m[2][kWaves][G];
+  __shared__ float red_l[2][kWaves][G];
+  __shared__ float red_o[2][kWaves][G][D];
+  __shared__ bf16x8 q_b[KS][64];
+  __shared__ PlanLds psm;
+
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int l16 = lane & 15;
+  Assign sa, sb;
+  const int nseg = plan_work<DENSE>(a, psm, false, &sa, &sb);
+  if (nseg == 0) return;  // uniform over the workgroup
+
+  if (nseg <= 2) {
+    if (nseg == 1) {
+      sb = sa;
+      sb.lo = sb.hi;
+    }
+    const int gA = sa.p % a.Hkv, gB = sb.p % a.Hkv;
+    const int nA = (sa.hi - sa.lo + NBW - 1) / NBW, nB = (sb.hi - sb.lo + NBW - 1) / NBW;
+    const int ntot = nA + nB;
+    const int nck_all = ntot > wave ? (ntot - wave + kWaves - 1) / kWaves : 0;
+    const int iB = nA > wave ? (nA - wave + kWaves - 1) / kWaves : 0;  // this wave's A chunks
+    // empty states for both segments (a wave may have chunks of one only)
+    if ((lane >> 4) == 0 && l16 < G) {
+      red_m[0][wave][l16] = kNegInf;
+      red_m[1][wave][l16] = kNegInf;
+      red_l[0][wave][l16] = 0.f;
+      red_l[1][wave][l16] = 0.f;
+    }
+    // this wave's first query in registers; B's query goes to LDS for a wave
+    // that crosses from A to B
+    bf16x8 qop[KS], qb[KS];
+    load_q<G, D>(a, iB > 0 ? sa.p : sb.p, qop);
+    const bool keep_b = iB > 0 && nck_all > iB;  // this wave crosses from A to B
+    if (keep_b) load_q<G, D>(a, sb.p, qb);
+    f32x4 o[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    MfmaState stt{kNegInf, 0.f, true};
+
+    // one lane per entry: resolve a batch of the wave's entries at once
+    int pb_l;
+    uint32_t msk_l;
+    auto resolve_batch = [&](int c0) {
+      const int e = c0 * NBW + lane;
+      const int k = (e / NBW) * kWaves + wave;  // chunk in the workgroup's sequence
+      const bool inB = k >= nA;
+      Assign al = inB ? sb : sa;
+      const int j = inB ? sb.lo + (k - nA) * NBW + e % NBW : sa.lo + k * NBW + e % NBW;
+      resolve_entry<DENSE>(a, al, al.p / a.Hkv, j < al.hi ? j : -1, &pb_l, &msk_l);
+    };
+    resolve_batch(0);
+    if (keep_b) {  // B's query was loaded before the entries: its wait overlaps theirs
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) q_b[kk][lane] = qb[kk];
+    }
+    for (int c0 = 0; c0 < nck_all; c0 += CPB) {
+      if (c0 > 0) resolve_batch(c0);
+      const int nck = nck_all - c0 < CPB ? nck_all - c0 : CPB;
+      // chunk c of the batch is this wave's chunk c0 + c: in A while < iB.
+      // Before computing the first chunk of B the wave stores its A state
+      // and starts over with B's query (checked ahead of the next chunk's
+      // loads, so that loads and matrix work stay in one block of code).
+      auto switch_at = [&](int c) {
+        if (c0 + c == iB && iB > 0) {
+          flush_state<G, D>(stt, o, red_m[0], red_l[0], red_o[0]);
+#pragma unroll
+          for (int kk = 0; kk < KS; ++kk) qop[kk] = q_b[kk][lane];
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+          stt = MfmaState{kNegInf, 0.f, true};
+        }
+      };
+      Chunk<D, NBW> cA, cB;
+      load_chunk<D, NBW>(a, c0 < iB ? gA : gB, 0, pb_l, msk_l, cA);
+      for (int c = 0; c < nck; c += 2) {
+        switch_at(c);
+        if (c + 1 < nck) load_chunk<D, NBW>(a, c0 + c + 1 < iB ? gA : gB, c + 1, pb_l, msk_l, cB);
+        compute_chunk<D, NBW>(a, cA, qop, o, stt);
+        if (c + 1 < nck) {
+          switch_at(c + 1);
+          if (c + 2 < nck)
+            load_chunk<D, NBW>(a, c0 + c + 2 < iB ? gA : gB, c + 2, pb_l, msk_l, cA);
+          compute_chunk<D, NBW>(a, cB, qop, o, stt);
+        }
+      }
+    }
+    if (nck_all > 0) {
+      const int s = nck_all > iB ? 1 : 0;  // the segment of this wave's last chunk
+      flush_state<G, D>(stt, o, red_m[s], red_l[s], red_o[s]);
+    }
+    __syncthreads();
+    write_partial<G, D>(a, sa.slot, red_m[0], red_l[0], red_o[0]);
+    if (nseg == 2) write_partial<G, D>(a, sb.slot, red_m[1], red_l[1], red_o[1]);
+    return;
+  }
+
+  // three or more segments: one after the other, one chunk in flight
+  int nrec = psm.nrec, ri = 0;
+  for (int si = 0; si < nseg; ++si) {
+    if (si > 0) __syncthreads();  // the previous segment's LDS results have been read
+    if (ri == nrec) {             // uniform
+      nrec = plan_next<DENSE>(a, psm);
+      ri = 0;
+    }
+    Assign as;
+    get_record(psm, ri++, &as);
+    const int g = as.p % a.Hkv;
+    bf16x8 qop[KS];
+    load_q<G, D>(a, as.p, qop);
+    f32x4 o[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    MfmaState stt{kNegInf, 0.f, true};
+    const int nck_all = wave_chunks<NBW>(as, wave);
+    for (int c0 = 0; c0 < nck_all; c0 += CPB) {
+      int pb_l;
+      uint32_t msk_l;
+      resolve_entry<DENSE>(a, as, as.p / a.Hkv, wave_entry<NBW>(as, wave, c0 * NBW + lane),
+                           &pb_l, &msk_l);
+      const int nck = nck_all - c0 < CPB ? nck_all - c0 : CPB;
+      for (int c = 0; c < nck; ++c) {
+        Chunk<D, NBW> ch;
+        load_chunk<D, NBW>(a, g, c, pb_l, msk_l, ch);
+        compute_chunk<D, NBW>(a, ch, qop, o, stt);
+      }
+    }
+    flush_state<G, D>(stt, o, red_m[0], red_l[0], red_o[0]);
+    __syncthreads();
+    write_partial<G, D>(a, as.slot, red_m[0], red_l[0], red_o[0]);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -524,148 +833,162 @@ attn_valu_kernel(AttnArgs a) {
   __shared__ float red_l[kWaves][G];
   __shared__ float red_o[kWaves][G][D];
   __shared__ float p_lds[kWaves][NBW * kBlock][G];
-  __shared__ int tmp_n[kWaves], tmp_s[kWaves];
-  __shared__ int sh_as[8];
+  __shared__ PlanLds psm;
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  Assign as;
-  if (!assign_work<DENSE>(a, tmp_n, tmp_s, sh_as, &as)) return;
-  const int b = as.p / a.Hkv, g = as.p % a.Hkv;
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  auto segment = [&](const Assign& as) {
+    const int b = as.p / a.Hkv, g = as.p % a.Hkv;
 
-  const St* kpool = static_cast<const St*>(a.k_pool);
-  const St* vpool = static_cast<const St*>(a.v_pool);
-  const int cl = lane % LPR, rs = lane / LPR;
-  float qf[G][VPL];
-  {
-    const St* qb = static_cast<const St*>(a.q) + (static_cast<size_t>(b) * a.Hq + g * G) * D;
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      unpack16<E>(*reinterpret_cast<const uint4*>(qb + h * D + cl * VPL), qf[h]);
-#pragma unroll
-      for (int v = 0; v < VPL; ++v) qf[h][v] *= a.scale_log2;
-    }
-  }
-  float m_run[G], l_part[G], acc[G][DPL];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m_run[h] = kNegInf;
-    l_part[h] = 0.f;
-#pragma unroll
-    for (int dd = 0; dd < DPL; ++dd) acc[h][dd] = 0.f;
-  }
-
-  const int nck_all = wave_chunks<NBW>(as, wave);
-  for (int c0 = 0; c0 < nck_all; c0 += CPB) {
-    int pb_l;
-    uint32_t msk_l;
-    resolve_entry<DENSE>(a, as, b, wave_entry<NBW>(as, wave, c0 * NBW + lane), &pb_l, &msk_l);
-    const int nck = nck_all - c0 < CPB ? nck_all - c0 : CPB;
-    for (int c = 0; c < nck; ++c) {
-      int pb[NBW];
-      uint32_t msk[NBW];
-#pragma unroll
-      for (int i = 0; i < NBW; ++i) {
-        pb[i] = __shfl(pb_l, c * NBW + i);
-        msk[i] = __shfl(msk_l, c * NBW + i);
-      }
-      float z[NBW][NL][G];
-      float mc[G];
-#pragma unroll
-      for (int h = 0; h < G; ++h) mc[h] = kNegInf;
-#pragma unroll
-      for (int i = 0; i < NBW; ++i) {
-        const size_t tile = static_cast<size_t>(pb[i]) * a.Hkv + g;
-#pragma unroll
-        for (int t = 0; t < NL; ++t) {
-          const int slot = rs + RPW * t;
-          const bool on = (msk[i] >> slot) & 1u;
-          uint4 u = make_uint4(0, 0, 0, 0);
-          if (on)
-            u = *reinterpret_cast<const uint4*>(kpool + (tile * kBlock + slot) * D + cl * VPL);
-          float x[VPL];
-          unpack16<E>(u, x);
-#pragma unroll
-          for (int h = 0; h < G; ++h) {
-            float s = 0.f;
-#pragma unroll
-            for (int v = 0; v < VPL; ++v) s = fmaf(qf[h][v], x[v], s);
-            s = row_sum<LPR>(s);
-            z[i][t][h] = on ? s : kNegInf;
-            mc[h] = fmaxf(mc[h], z[i][t][h]);
-          }
-        }
-      }
+    const St* kpool = static_cast<const St*>(a.k_pool);
+    const St* vpool = static_cast<const St*>(a.v_pool);
+    const int cl = lane % LPR, rs = lane / LPR;
+    float qf[G][VPL];
+    {
+      const St* qb = static_cast<const St*>(a.q) + (static_cast<size_t>(b) * a.Hq + g * G) * D;
 #pragma unroll
       for (int h = 0; h < G; ++h) {
+        unpack16<E>(*reinterpret_cast<const uint4*>(qb + h * D + cl * VPL), qf[h]);
 #pragma unroll
-        for (int o = LPR; o < 64; o <<= 1) mc[h] = fmaxf(mc[h], __shfl_xor(mc[h], o));
-        const float mn = fmaxf(m_run[h], mc[h]);
-        const float alpha = mn == kNegInf ? 1.f : exp2f(m_run[h] - mn);
-        l_part[h] *= alpha;
-#pragma unroll
-        for (int dd = 0; dd < DPL; ++dd) acc[h][dd] *= alpha;
-        m_run[h] = mn;
+        for (int v = 0; v < VPL; ++v) qf[h][v] *= a.scale_log2;
       }
-      // probabilities of the wave's slots -> LDS (one writer lane per row)
+    }
+    float m_run[G], l_part[G], acc[G][DPL];
 #pragma unroll
-      for (int i = 0; i < NBW; ++i)
+    for (int h = 0; h < G; ++h) {
+      m_run[h] = kNegInf;
+      l_part[h] = 0.f;
 #pragma unroll
-        for (int t = 0; t < NL; ++t)
+      for (int dd = 0; dd < DPL; ++dd) acc[h][dd] = 0.f;
+    }
+
+    const int nck_all = wave_chunks<NBW>(as, wave);
+    for (int c0 = 0; c0 < nck_all; c0 += CPB) {
+      int pb_l;
+      uint32_t msk_l;
+      resolve_entry<DENSE>(a, as, b, wave_entry<NBW>(as, wave, c0 * NBW + lane), &pb_l, &msk_l);
+      const int nck = nck_all - c0 < CPB ? nck_all - c0 : CPB;
+      for (int c = 0; c < nck; ++c) {
+        int pb[NBW];
+        uint32_t msk[NBW];
 #pragma unroll
-          for (int h = 0; h < G; ++h) {
-            const float pv = z[i][t][h] != kNegInf ? exp2f(z[i][t][h] - m_run[h]) : 0.f;
-            if (cl == 0) {
-              p_lds[wave][i * kBlock + rs + RPW * t][h] = pv;
-              l_part[h] += pv;
+        for (int i = 0; i < NBW; ++i) {
+          pb[i] = __shfl(pb_l, c * NBW + i);
+          msk[i] = __shfl(msk_l, c * NBW + i);
+        }
+        float z[NBW][NL][G];
+        float mc[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) mc[h] = kNegInf;
+#pragma unroll
+        for (int i = 0; i < NBW; ++i) {
+          const size_t tile = static_cast<size_t>(pb[i]) * a.Hkv + g;
+#pragma unroll
+          for (int t = 0; t < NL; ++t) {
+            const int slot = rs + RPW * t;
+            const bool on = (msk[i] >> slot) & 1u;
+            uint4 u = make_uint4(0, 0, 0, 0);
+            if (on)
+              u = *reinterpret_cast<const uint4*>(kpool + (tile * kBlock + slot) * D + cl * VPL);
+            float x[VPL];
+            unpack16<E>(u, x);
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+              float s = 0.f;
+#pragma unroll
+              for (int v = 0; v < VPL; ++v) s = fmaf(qf[h][v], x[v], s);
+              s = row_sum<LPR>(s);
+              z[i][t][h] = on ? s : kNegInf;
+              mc[h] = fmaxf(mc[h], z[i][t][h]);
             }
           }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-      // values: lane owns dims lane + 64 dd; a value column holds 16 slots
+        }
 #pragma unroll
-      for (int i = 0; i < NBW; ++i) {
-        if (msk[i] == 0u) continue;
-        const size_t tile = static_cast<size_t>(pb[i]) * a.Hkv + g;
+        for (int h = 0; h < G; ++h) {
 #pragma unroll
-        for (int dd = 0; dd < DPL; ++dd) {
-          const St* col = vpool + (tile * D + lane + 64 * dd) * kBlock;
+          for (int o = LPR; o < 64; o <<= 1) mc[h] = fmaxf(mc[h], __shfl_xor(mc[h], o));
+          const float mn = fmaxf(m_run[h], mc[h]);
+          const float alpha = mn == kNegInf ? 1.f : exp2f(m_run[h] - mn);
+          l_part[h] *= alpha;
 #pragma unroll
-          for (int c2 = 0; c2 < VCH; ++c2) {
-            float x[VPL];
-            unpack16<E>(*reinterpret_cast<const uint4*>(col + c2 * VPL), x);
+          for (int dd = 0; dd < DPL; ++dd) acc[h][dd] *= alpha;
+          m_run[h] = mn;
+        }
+        // probabilities of the wave's slots -> LDS (one writer lane per row)
 #pragma unroll
-            for (int v = 0; v < VPL; ++v) {
-              const int slot = c2 * VPL + v;
-              if ((msk[i] >> slot) & 1u) {
+        for (int i = 0; i < NBW; ++i)
 #pragma unroll
-                for (int h = 0; h < G; ++h)
-                  acc[h][dd] = fmaf(p_lds[wave][i * kBlock + slot][h], x[v], acc[h][dd]);
+          for (int t = 0; t < NL; ++t)
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+              const float pv = z[i][t][h] != kNegInf ? exp2f(z[i][t][h] - m_run[h]) : 0.f;
+              if (cl == 0) {
+                p_lds[wave][i * kBlock + rs + RPW * t][h] = pv;
+                l_part[h] += pv;
+              }
+            }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        // values: lane owns dims lane + 64 dd; a value column holds 16 slots
+#pragma unroll
+        for (int i = 0; i < NBW; ++i) {
+          if (msk[i] == 0u) continue;
+          const size_t tile = static_cast<size_t>(pb[i]) * a.Hkv + g;
+#pragma unroll
+          for (int dd = 0; dd < DPL; ++dd) {
+            const St* col = vpool + (tile * D + lane + 64 * dd) * kBlock;
+#pragma unroll
+            for (int c2 = 0; c2 < VCH; ++c2) {
+              float x[VPL];
+              unpack16<E>(*reinterpret_cast<const uint4*>(col + c2 * VPL), x);
+#pragma unroll
+              for (int v = 0; v < VPL; ++v) {
+                const int slot = c2 * VPL + v;
+                if ((msk[i] >> slot) & 1u) {
+#pragma unroll
+                  for (int h = 0; h < G; ++h)
+                    acc[h][dd] = fmaf(p_lds[wave][i * kBlock + slot][h], x[v], acc[h][dd]);
+                }
               }
             }
           }
         }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     }
-  }
 
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float l = l_part[h];
+    for (int h = 0; h < G; ++h) {
+      float l = l_part[h];
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) l += __shfl_xor(l, o);
-    if (lane == 0) {
-      red_m[wave][h] = m_run[h];
-      red_l[wave][h] = l;
+      for (int o = 1; o < 64; o <<= 1) l += __shfl_xor(l, o);
+      if (lane == 0) {
+        red_m[wave][h] = m_run[h];
+        red_l[wave][h] = l;
+      }
+#pragma unroll
+      for (int dd = 0; dd < DPL; ++dd) red_o[wave][h][lane + 64 * dd] = acc[h][dd];
     }
-#pragma unroll
-    for (int dd = 0; dd < DPL; ++dd) red_o[wave][h][lane + 64 * dd] = acc[h][dd];
+    __syncthreads();
+    write_partial<G, D>(a, as.slot, red_m, red_l, red_o);
+  };
+
+  Assign sa, sb;
+  const int nseg = plan_work<DENSE>(a, psm, true, &sa, &sb);
+  if (nseg == 0) return;  // uniform over the workgroup
+  int nrec = psm.nrec, ri = 0;
+  for (int si = 0; si < nseg; ++si) {
+    if (si > 0) __syncthreads();  // the previous segment's LDS results have been read
+    if (ri == nrec) {  // uniform
+      nrec = plan_next<DENSE>(a, psm);
+      ri = 0;
+    }
+    Assign as;
+    get_record(psm, ri++, &as);
+    segment(as);
   }
-  __syncthreads();
-  write_partial<G, D>(a, red_m, red_l, red_o);
 }
 
 // ---------------------------------------------------------------------------
@@ -776,7 +1099,7 @@ size_t attn_workspace(const zr_geom& gm, int nwg, void* ws, AttnArgs* a) {
 
 template <int G, int D>
 static hipError_t launch_mfma(const zr_geom& gm, const AttnArgs& a, bool dense, hipStream_t s) {
-  const dim3 grid(a.nwg + gm.batch * gm.n_kv_heads);
+  const dim3 grid(a.nwg);
   if (dense)
     hipLaunchKernelGGL((attn_mfma_kernel<G, D, kMfmaNBW, true>), grid, dim3(kThreads), 0, s, a);
   else
@@ -790,7 +1113,7 @@ static hipError_t launch_mfma(const zr_geom& gm, const AttnArgs& a, bool dense, 
 
 template <typename E, int G, int D>
 static hipError_t launch_valu(const zr_geom& gm, const AttnArgs& a, bool dense, hipStream_t s) {
-  const dim3 grid(a.nwg + gm.batch * gm.n_kv_heads);
+  const dim3 grid(a.nwg);
   if (dense)
     hipLaunchKernelGGL((attn_valu_kernel<E, G, D, true>), grid, dim3(kThreads), 0, s, a);
   else

@@ -74,9 +74,37 @@ __device__ __forceinline__ int wave_incl_sum(int v) {
   return v;
 }
 
+// Index of the calling wave in its workgroup, as a wave-uniform (scalar)
+// value, so that what is derived from it stays scalar.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+}
+
 // Sum of v over the wave, in every lane.
 __device__ __forceinline__ int wave_sum(int v) {
   return __builtin_amdgcn_readlane(wave_incl_sum(v), 63);
+}
+
+// Exclusive prefix sum of one value per thread across a workgroup of NW
+// waves; *total gets the sum. `tmp` holds NW ints. Contains barriers: every
+// thread must call it. REUSE = false drops the closing barrier that lets
+// `tmp` be written again (for a workgroup's last scan).
+template <int NW, bool REUSE = true>
+__device__ __forceinline__ int wg_exclusive_scan(int v, int* tmp, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int incl = wave_incl_sum(v);
+  if (lane == 63) tmp[wave] = incl;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int x = tmp[w];
+    before += w < wave ? x : 0;
+    all += x;
+  }
+  if (REUSE) __syncthreads();
+  *total = all;
+  return before + incl - v;
 }
 
 template <int CTRL>
@@ -154,8 +182,8 @@ struct ConsArgs {
 // Attention launch parameters (device pointers + sizes), passed by value.
 // Pair p = b * Hkv + g attends its counts[p] list entries entries[p][0..)
 // (sparse only) and then the blocks of its window [T - window, T) (dense:
-// [0, T)), read from the block table. Partial results are indexed by
-// workgroup; workgroups [ws_pref[p], ws_pref[p + 1]) hold pair p's.
+// [0, T)), read from the block table. Partial results are indexed by slot;
+// slots [ws_pref[p], ws_pref[p + 1]) hold pair p's.
 struct AttnArgs {
   const void* q;
   const void* k_pool;
@@ -164,14 +192,14 @@ struct AttnArgs {
   const int32_t* seq_lens;
   const int32_t* counts;     // [P] (sparse)
   const int2* entries;       // [P][max_blocks] (sparse)
-  int32_t* ws_pref;          // [P + 1]: first workgroup of each pair
+  int32_t* ws_pref;          // [P + 1]: first partial slot of each pair
   float* ws_m;               // [nwg + P][G]
   float* ws_l;               // [nwg + P][G]
   float* ws_acc;             // [nwg + P][G][D]
   float* out;                // [B][Hq][D]
   int32_t B, Hq, Hkv, max_blocks, num_blocks;
   int32_t window;            // sparse: window tokens appended after the cached entries
-  int32_t nwg;               // target workgroups; the grid has nwg + P
+  int32_t nwg;               // workgroups of the grid (at most nwg + P partial slots)
   float scale_log2;          // scale * log2(e)
 };
 

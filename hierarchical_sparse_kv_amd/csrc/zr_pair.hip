@@ -52,28 +52,6 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Exclusive prefix sum of one value per thread across the workgroup; *total
-// gets the sum. `tmp` holds kPairWaves ints. Contains barriers: every thread
-// must call it. REUSE = false drops the closing barrier that lets `tmp` be
-// written again (for the workgroup's last scan).
-template <bool REUSE = true>
-__device__ int pair_exclusive_scan(int v, int* tmp, int* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int incl = wave_incl_sum(v);
-  if (lane == 63) tmp[wave] = incl;
-  __syncthreads();
-  int before = 0, all = 0;
-#pragma unroll
-  for (int w = 0; w < kPairWaves; ++w) {
-    const int x = tmp[w];
-    before += w < wave ? x : 0;
-    all += x;
-  }
-  if (REUSE) __syncthreads();
-  *total = all;
-  return before + incl - v;
-}
-
 __device__ __forceinline__ int blocks_of_span(int s, int e) {
   return e > s ? ((e - 1) >> 4) - (s >> 4) + 1 : 0;
 }
@@ -268,7 +246,7 @@ __device__ void select_by_radix(const PairLds& L, int n, int k, int32_t* out, ui
   int n_eq = 0;
   for (int i = i0; i < i1; ++i) n_eq += L.keys[i] == kth;
   int tot;
-  const int eq_before = pair_exclusive_scan(n_eq, wtmp, &tot);
+  const int eq_before = wg_exclusive_scan<kPairWaves>(n_eq, wtmp, &tot);
   int n_sel = 0;
   {
     int r = eq_before;
@@ -282,7 +260,7 @@ __device__ void select_by_radix(const PairLds& L, int n, int k, int32_t* out, ui
       }
     }
   }
-  int pos = pair_exclusive_scan(n_sel, wtmp, &tot);
+  int pos = wg_exclusive_scan<kPairWaves>(n_sel, wtmp, &tot);
   {
     int r = eq_before;
     for (int i = i0; i < i1; ++i) {
@@ -384,7 +362,7 @@ __device__ void emit_list_regs(const PairArgs& a, int p, const uint32_t* bmask,
 #pragma unroll
   for (int j = 0; j < W; ++j) nz += ((w[j] & 0xffffu) != 0u ? 1 : 0) + ((w[j] >> 16) != 0u ? 1 : 0);
   int n_list;
-  int pos = pair_exclusive_scan<false>(nz, wtmp, &n_list);
+  int pos = wg_exclusive_scan<kPairWaves, false>(nz, wtmp, &n_list);
   int2* ent = a.entries + static_cast<size_t>(p) * a.max_blocks;
 #pragma unroll
   for (int j = 0; j < 2 * W; ++j) {
@@ -411,7 +389,7 @@ __device__ void emit_list_table(const PairArgs& a, const PairLds& L, int p, int 
     if (lb < nb) nz += ((L.bmask[lb >> 1] >> (16 * (lb & 1))) & 0xffffu) != 0u;
   }
   int n_list;
-  int pos = pair_exclusive_scan<false>(nz, wtmp, &n_list);
+  int pos = wg_exclusive_scan<kPairWaves, false>(nz, wtmp, &n_list);
   int2* ent = a.entries + static_cast<size_t>(p) * a.max_blocks;
   const int32_t* row = a.block_table + static_cast<size_t>(b) * a.max_blocks;
   for (int j = 0; j < a.bt_per; ++j) {
@@ -698,7 +676,7 @@ consensus_kernel(ConsArgs a) {
     kvotes += static_cast<int>(v);
   }
   int n_keep;
-  int pos = pair_exclusive_scan(keep, wtmp, &n_keep);
+  int pos = wg_exclusive_scan<kPairWaves>(keep, wtmp, &n_keep);
   int32_t* out = a.cons + static_cast<size_t>(b) * a.c;
   for (int j = j0; j < j1; ++j) {
     const int i = L.sel_l[j];
@@ -706,7 +684,7 @@ consensus_kernel(ConsArgs a) {
   }
   for (int j = n_keep + t; j < a.c; j += kPairThreads) out[j] = -1;
   int kv_all;
-  pair_exclusive_scan(kvotes, wtmp, &kv_all);
+  wg_exclusive_scan<kPairWaves>(kvotes, wtmp, &kv_all);
   if (t == 0) a.agree[b] = total > 0 ? static_cast<float>(kv_all) / static_cast<float>(total) : 0.f;
 }
 

@@ -328,3 +328,24 @@ def test_many_pairs_and_largest_k():
     w = synth.make_workload(1, device="cuda", overrides=dict(
         B=2, Hq=8, Hkv=2, seq_len=("fixed", 9000), thought=("uniform", 1, 5), k=1024))
     run_and_check(w, "k-1024")
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
+def test_ranges_crossing_many_short_pairs(dtype, d):
+    """One long sequence among very short ones (64 pairs): the attention
+    workgroups' equal ranges of the concatenated lists cut pairs apart, and a
+    range holds two, three or more pairs' pieces (one partial each)."""
+    w = synth.make_workload(1, device="cuda", seq_lens=[20000, 16, 40, 100, 17, 300, 33, 5000],
+                            overrides=dict(B=8, dtype=dtype, d=d, thought=("uniform", 4, 60),
+                                           k=12))
+    run_and_check(w, f"ranges-short-pairs-{dtype}", check_dense=True)
+
+
+def test_range_meeting_more_than_64_pairs():
+    """160 pairs, 144 of them one block long between two long sequences: in
+    dense attention a workgroup's range meets more pairs than one batch of
+    segment records holds, so the records are refilled."""
+    lens = [65536] + [16] * 18 + [16384]
+    w = synth.make_workload(1, device="cuda", seq_lens=lens,
+                            overrides=dict(B=len(lens), thought=("uniform", 8, 400), k=4))
+    run_and_check(w, "ranges-over-64-pairs", check_dense=True)
