@@ -169,27 +169,31 @@ __device__ __forceinline__ void get_record(const PlanLds& sm, int i, Assign* as)
   as->slot = __builtin_amdgcn_readfirstlane(r1.z);
 }
 
-// Up to 64 pairs every wave computes the plan by itself (one pair per lane,
-// DPP scans) and takes its first two segments into scalar registers, with
-// no LDS and no barrier; the records are written to LDS (the same values by
-// every wave) only when asked for or when there are more than two segments.
-// Returns the number of segments.
+// Up to kWavePairs pairs every wave computes the plan by itself (lane l owns
+// pairs [l K, (l + 1) K), K = ceil(P / 64) <= kLanePairs, DPP scans) and
+// takes its first two segments into scalar registers, with no LDS and no
+// barrier; the records are written to LDS (the same values by every wave)
+// only when asked for or when there are more than two segments. Returns the
+// number of segments.
 //
 // Where whole-pair slices are about as even, they are used instead of the
 // ranges: pair p gets S_p = max(1, round(n_p / per)) workgroups (per =
 // ceil(total / nwg)), each an equal slice of its list, one segment per
 // workgroup, slot = workgroup. That is chosen when it needs no more than nwg
-// workgroups and no slice is longer than the ranges' largest plus 1/8:
-// one segment per workgroup and fewer partials then beat the exact balance.
-__device__ __forceinline__ void lane_segment(int p, int T, int tw, int ncache, int lo, int hi,
-                                             int slot, Assign* as) {
-  as->p = p;
-  as->T = __builtin_amdgcn_readlane(T, p);
-  as->tw = __builtin_amdgcn_readlane(tw, p);
-  as->ncache = __builtin_amdgcn_readlane(ncache, p);
-  as->lo = __builtin_amdgcn_readlane(lo, p);
-  as->hi = __builtin_amdgcn_readlane(hi, p);
-  as->slot = __builtin_amdgcn_readlane(slot, p);
+// workgroups and no slice is longer than the ranges' largest plus 1/8: one
+// segment per workgroup and fewer partials then beat the exact balance.
+constexpr int kLanePairs = 4;
+constexpr int kWavePairs = 64 * kLanePairs;
+
+__device__ __forceinline__ void lane_segment(int src, int p, int T, int tw, int ncache, int lo,
+                                             int hi, int slot, Assign* as) {
+  as->p = __builtin_amdgcn_readlane(p, src);
+  as->T = __builtin_amdgcn_readlane(T, src);
+  as->tw = __builtin_amdgcn_readlane(tw, src);
+  as->ncache = __builtin_amdgcn_readlane(ncache, src);
+  as->lo = __builtin_amdgcn_readlane(lo, src);
+  as->hi = __builtin_amdgcn_readlane(hi, src);
+  as->slot = __builtin_amdgcn_readlane(slot, src);
 }
 
 template <bool DENSE>
@@ -197,59 +201,141 @@ __device__ int plan_wave(const AttnArgs& a, PlanLds& sm, bool records, Assign* s
   const int P = a.B * a.Hkv;
   const int lane = threadIdx.x & 63, w = blockIdx.x;
   const bool publish = w == 0 && threadIdx.x < 64;
-  PairList L{0, 0, 0, 0};
-  if (lane < P) L = pair_list<DENSE>(a, lane);
-  const int incl = wave_incl_sum(L.n);
+  const int K = (P + 63) / 64;
+  const int p0 = lane * K;
+  int n[kLanePairs], T[kLanePairs], nc[kLanePairs];
+  int nsum = 0;
+#pragma unroll
+  for (int j = 0; j < kLanePairs; ++j) {
+    PairList L{0, 0, 0, 0};
+    if (j < K && p0 + j < P) L = pair_list<DENSE>(a, p0 + j);
+    n[j] = L.n;
+    T[j] = L.T;
+    nc[j] = L.ncache;
+    nsum += L.n;
+  }
+  auto window_start = [&](int t) { return DENSE ? 0 : (t - a.window > 0 ? t - a.window : 0); };
+  const int incl = wave_incl_sum(nsum);
   const int total = __builtin_amdgcn_readlane(incl, 63);
-  const int start = incl - L.n, end = incl;
+  const int run = incl - nsum;  // first entry of this lane's pairs
   const int nr = total < a.nwg ? total : a.nwg;  // ranges: none empty
+
   // whole-pair slices
   const int per = total > 0 ? (total + a.nwg - 1) / a.nwg : 1;
-  const int S = L.n > 0 ? max(1, (L.n + per / 2) / per) : 0;
-  const int sincl = wave_incl_sum(S);
-  const int total_s = __builtin_amdgcn_readlane(sincl, 63);
-  // every slice within 1/8 of the ranges' largest: n_p <= S_p * cap
   const int range_max = nr > 0 ? (total + nr - 1) / nr : 0;
   const int cap = range_max + range_max / 8;
-  const bool even = __ballot(L.n > S * cap) == 0ull;
-  if (total_s <= a.nwg && even) {  // uniform
-    const int run = sincl - S;
+  int S[kLanePairs];
+  int ssum = 0;
+  bool uneven = false;
+#pragma unroll
+  for (int j = 0; j < kLanePairs; ++j) {
+    S[j] = n[j] > 0 ? max(1, (n[j] + per / 2) / per) : 0;
+    ssum += S[j];
+    uneven = uneven || n[j] > S[j] * cap;
+  }
+  const int sincl = wave_incl_sum(ssum);
+  const int total_s = __builtin_amdgcn_readlane(sincl, 63);
+  if (total_s <= a.nwg && __ballot(uneven) == 0ull) {  // uniform
+    const int srun = sincl - ssum;
     if (publish) {
-      if (lane < P) a.ws_pref[lane] = run;
+      int r = srun;
+#pragma unroll
+      for (int j = 0; j < kLanePairs; ++j) {
+        if (j < K && p0 + j < P) a.ws_pref[p0 + j] = r;
+        r += S[j];
+      }
       if (lane == 0) a.ws_pref[P] = total_s;
     }
     if (w >= total_s) return 0;
-    const bool mine = lane < P && w >= run && w < run + S;
-    const int r = w - run;
-    const int lo = mine ? floor_div(static_cast<int64_t>(r) * L.n, S) : 0;
-    const int hi = mine ? floor_div(static_cast<int64_t>(r + 1) * L.n, S) : 0;
-    const int p = __ffsll(static_cast<unsigned long long>(__ballot(mine))) - 1;
-    lane_segment(p, L.T, L.tw, L.ncache, lo, hi, w, sa);
-    if (records && mine) put_record(sm, 0, lane, L.T, L.tw, L.ncache, lo, hi, w);
+    const bool mine = w >= srun && w < srun + ssum;
+    int pj = 0, tj = 0, cj = 0, lo = 0, hi = 0;
+    if (mine) {
+      int r0 = srun;
+#pragma unroll
+      for (int j = 0; j < kLanePairs; ++j) {
+        if (w >= r0 && w < r0 + S[j]) {
+          const int r = w - r0;
+          pj = p0 + j;
+          tj = T[j];
+          cj = nc[j];
+          lo = floor_div(static_cast<int64_t>(r) * n[j], S[j]);
+          hi = floor_div(static_cast<int64_t>(r + 1) * n[j], S[j]);
+        }
+        r0 += S[j];
+      }
+    }
+    const int src = __ffsll(static_cast<unsigned long long>(__ballot(mine))) - 1;
+    lane_segment(src, pj, tj, window_start(tj), cj, lo, hi, w, sa);
+    if (records && mine) put_record(sm, 0, pj, tj, window_start(tj), cj, lo, hi, w);
     return 1;
   }
+
   // ranges
-  const int ns = pair_slots(start, L.n, total, nr);
-  const int rincl = wave_incl_sum(ns);
-  const int base = rincl - ns;
-  if (publish) {
-    if (lane < P) a.ws_pref[lane] = base;
-    if (lane == 0) a.ws_pref[P] = __builtin_amdgcn_readlane(rincl, 63);
+  int nssum = 0;
+  {
+    int st = run;
+#pragma unroll
+    for (int j = 0; j < kLanePairs; ++j) {
+      nssum += pair_slots(st, n[j], total, nr);
+      st += n[j];
+    }
   }
+  const int rincl = wave_incl_sum(nssum);
   const int R0 = w < nr ? range_start(w, total, nr) : total;
   const int R1 = w < nr ? range_start(w + 1, total, nr) : total;
-  const bool mine = lane < P && L.n > 0 && start < R1 && end > R0;
-  const uint64_t mask = __ballot(mine);
-  const int nseg = __popcll(mask);
-  const int lo = (start > R0 ? start : R0) - start, hi = (end < R1 ? end : R1) - start;
-  const int slot = mine ? base + w - range_of(start, total, nr) : 0;
-  if (nseg >= 1) lane_segment(__ffsll(static_cast<unsigned long long>(mask)) - 1, L.T, L.tw,
-                              L.ncache, lo, hi, slot, sa);
-  if (nseg >= 2) lane_segment(__ffsll(static_cast<unsigned long long>(mask & (mask - 1))) - 1,
-                              L.T, L.tw, L.ncache, lo, hi, slot, sb);
-  if ((records || nseg > 2) && mine)
-    put_record(sm, __popcll(mask & ((1ull << lane) - 1ull)), lane, L.T, L.tw, L.ncache, lo, hi,
-               slot);
+  int cnt = 0;
+  {
+    int st = run, bs = rincl - nssum;
+#pragma unroll
+    for (int j = 0; j < kLanePairs; ++j) {
+      if (publish && j < K && p0 + j < P) a.ws_pref[p0 + j] = bs;
+      cnt += n[j] > 0 && st < R1 && st + n[j] > R0 ? 1 : 0;
+      bs += pair_slots(st, n[j], total, nr);
+      st += n[j];
+    }
+  }
+  if (publish && lane == 0) a.ws_pref[P] = __builtin_amdgcn_readlane(rincl, 63);
+  const int cincl = wave_incl_sum(cnt);
+  const int nseg = __builtin_amdgcn_readlane(cincl, 63);
+  const bool put = records || nseg > 2;
+  // this lane's segments, ordinals from cincl - cnt on; keep ordinals 0 and 1
+  int v0[7] = {0, 0, 0, 0, 0, 0, 0}, v1[7] = {0, 0, 0, 0, 0, 0, 0};
+  {
+    int st = run, bs = rincl - nssum, ord = cincl - cnt;
+#pragma unroll
+    for (int j = 0; j < kLanePairs; ++j) {
+      const int e = st + n[j];
+      if (n[j] > 0 && st < R1 && e > R0) {
+        const int v[7] = {p0 + j, T[j], window_start(T[j]), nc[j], (st > R0 ? st : R0) - st,
+                          (e < R1 ? e : R1) - st, bs + w - range_of(st, total, nr)};
+        if (put && ord < kMaxSeg) put_record(sm, ord, v[0], v[1], v[2], v[3], v[4], v[5], v[6]);
+        if (put && ord == kMaxSeg - 1) {  // more segments follow only if this one ends inside
+          sm.next_p = v[0] + 1;
+          sm.next_pos = e;
+          sm.next_slot = v[6] + 1;
+        }
+#pragma unroll
+        for (int i = 0; i < 7; ++i) {
+          v0[i] = ord == 0 ? v[i] : v0[i];
+          v1[i] = ord == 1 ? v[i] : v1[i];
+        }
+        ++ord;
+      }
+      bs += pair_slots(st, n[j], total, nr);
+      st += n[j];
+    }
+  }
+  if (put && lane == 0) sm.r1 = R1;
+  const int before = cincl - cnt;
+  if (nseg >= 1) {
+    const int src = __ffsll(static_cast<unsigned long long>(__ballot(cnt > 0 && before == 0))) - 1;
+    lane_segment(src, v0[0], v0[1], v0[2], v0[3], v0[4], v0[5], v0[6], sa);
+  }
+  if (nseg >= 2) {
+    const int src =
+        __ffsll(static_cast<unsigned long long>(__ballot(before <= 1 && before + cnt > 1))) - 1;
+    lane_segment(src, v1[0], v1[1], v1[2], v1[3], v1[4], v1[5], v1[6], sb);
+  }
   return nseg;
 }
 
@@ -395,7 +481,7 @@ __device__ int plan_next(const AttnArgs& a, PlanLds& sm) {
 // Contains barriers: every thread must call it.
 template <bool DENSE>
 __device__ int plan_work(const AttnArgs& a, PlanLds& sm, bool records, Assign* sa, Assign* sb) {
-  if (a.B * a.Hkv > 64) {
+  if (a.B * a.Hkv > kWavePairs) {
     const int nseg = plan_block<DENSE>(a, sm);
     if (nseg >= 1) get_record(sm, 0, sa);
     if (nseg >= 2) get_record(sm, 1, sb);
@@ -403,7 +489,7 @@ __device__ int plan_work(const AttnArgs& a, PlanLds& sm, bool records, Assign* s
   }
   const int nseg = plan_wave<DENSE>(a, sm, records, sa, sb);
   if (records || nseg > 2) {  // uniform
-    if (threadIdx.x == 0) sm.nrec = nseg;
+    if (threadIdx.x == 0) sm.nrec = nseg < kMaxSeg ? nseg : kMaxSeg;
     __syncthreads();
   }
   return nseg;
