@@ -341,11 +341,13 @@ def test_ranges_crossing_many_short_pairs(dtype, d):
     run_and_check(w, f"ranges-short-pairs-{dtype}", check_dense=True)
 
 
-def test_range_meeting_more_than_64_pairs():
-    """160 pairs, 144 of them one block long between two long sequences: in
-    dense attention a workgroup's range meets more pairs than one batch of
-    segment records holds, so the records are refilled."""
-    lens = [65536] + [16] * 18 + [16384]
+@pytest.mark.parametrize("n_short", [18, 38])
+def test_range_meeting_more_than_64_pairs(n_short):
+    """160 or 320 pairs (planned by each wave alone, or by the whole
+    workgroup), all but 16 of them one block long between two long
+    sequences: in dense attention a workgroup's range meets more pairs than
+    one batch of segment records holds, so the records are refilled."""
+    lens = [65536] + [16] * n_short + [16384]
     w = synth.make_workload(1, device="cuda", seq_lens=lens,
                             overrides=dict(B=len(lens), thought=("uniform", 8, 400), k=4))
-    run_and_check(w, "ranges-over-64-pairs", check_dense=True)
+    run_and_check(w, f"ranges-over-64-pairs-{8 * len(lens)}", check_dense=True)
