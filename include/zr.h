@@ -330,8 +330,9 @@ zr_status zr_zoom_decode_attn(const zr_geom* geom, const void* q, const void* k_
 
 /* Workspace bytes the attention calls need for a grid sized for
  * `max_attended` tokens per (sequence, KV head): per-(b, g) block lists
- * (8 bytes per block-table column) and per-workgroup partial softmax
- * states. 0 if geom is invalid or batch * n_kv_heads > ZR_MAX_PAIRS. */
+ * (8 bytes per block-table column) and the partial softmax states (one per
+ * piece of a (b, g) list that one workgroup takes). 0 if geom is invalid or
+ * batch * n_kv_heads > ZR_MAX_PAIRS. */
 size_t zr_workspace_bytes(const zr_geom* geom, int32_t max_attended);
 
 /* Static, NUL-terminated description of a status code. */
