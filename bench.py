@@ -121,9 +121,11 @@ def main():
     log(f"[bench] generating {L} layer caches (config: llama8b-16k-b8)")
     layers, steps = [], []
     for l in range(L):
+        # one structure (lengths, thoughts, block table) shared by all layers, as
+        # in a model; every layer has its own K/V pools, summary keys and query
         w = synth.make_workload(1, seed=1, value_seed=1000 + l, device=dev)
         layers.append(w)
-        steps.append(zr.step_from_workload(w))
+        steps.append(zr.step_from_workload(w, meta=steps[0] if steps else None))
     torch.cuda.synchronize()
     w0 = layers[0]
     d, s_bytes = w0.d, synth.ELEM_BYTES[w0.dtype]
@@ -248,7 +250,9 @@ def main():
     if not args.no_zoom:
         zl = [synth.make_workload(5, value_seed=2000 + l, device=dev) for l in range(L)]
         wz = zl[0]
-        zs = [zr.step_from_workload(w) for w in zl]
+        zs = []
+        for w in zl:
+            zs.append(zr.step_from_workload(w, meta=zs[0] if zs else None))
         cz, npz = wz.extra["c"], wz.extra["prompt"]
         ss = torch.as_tensor(wz.extra["sum_start"], device=dev)
         sl = torch.as_tensor(wz.extra["sum_len"], device=dev)
@@ -310,7 +314,9 @@ def main():
                            (4, "long-64k-b4: batch 4, 65536 tokens, thoughts log-U[32, 2048], "
                                "top-16 + 256 window")):
             ws_ = [synth.make_workload(cid, value_seed=3000 + l, device=dev) for l in range(4)]
-            ss_ = [zr.step_from_workload(w) for w in ws_]
+            ss_ = []
+            for w in ws_:
+                ss_.append(zr.step_from_workload(w, meta=ss_[0] if ss_ else None))
             byts = []
             for w, st in zip(ws_, ss_):
                 st.step()

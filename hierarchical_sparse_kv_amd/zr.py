@@ -359,11 +359,21 @@ def max_attended_bound(seq_lens, seq_ptr, th_len, k, window):
     return best
 
 
-def step_from_workload(w, k=None):
-    """DeviceStep for a synth.Workload (tensors already on the GPU)."""
+def step_from_workload(w, k=None, meta=None):
+    """DeviceStep for a synth.Workload (tensors already on the GPU). `meta`: a
+    DeviceStep whose per-sequence tensors (block table, lengths, thought spans)
+    this one shares, as the layers of one model share them (each layer has
+    its own pools, summary keys and queries); the workload must have the same
+    structure."""
     k = w.k if k is None else k
-    return DeviceStep(w.q, w.k_pool, w.v_pool, w.block_table, w.seq_lens, w.seq_ptr, w.th_start,
-                      w.th_len, w.summary_keys, max(w.max_per_seq, 1), k, w.window, w.scale,
+    bt, lens, ptr, ts, tl = (w.block_table, w.seq_lens, w.seq_ptr, w.th_start, w.th_len)
+    if meta is not None:
+        assert np.array_equal(meta.block_table.cpu().numpy(), w.block_table)
+        assert np.array_equal(meta.seq_lens.cpu().numpy(), w.seq_lens)
+        bt, lens, ptr, ts, tl = (meta.block_table, meta.seq_lens, meta.seq_ptr, meta.th_start,
+                                 meta.th_len)
+    return DeviceStep(w.q, w.k_pool, w.v_pool, bt, lens, ptr, ts, tl, w.summary_keys,
+                      max(w.max_per_seq, 1), k, w.window, w.scale,
                       max_attended_bound(w.seq_lens, w.seq_ptr, w.th_len, k, w.window))
 
 
