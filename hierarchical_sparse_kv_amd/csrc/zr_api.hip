@@ -55,6 +55,10 @@ zr_status attention_common(const zr_geom* geom, const void* q, const void* k_poo
   if (!isfinite(scale)) return ZR_E_SHAPE;
   if (static_cast<int64_t>(geom->batch) * geom->n_kv_heads > ZR_MAX_PAIRS)
     return ZR_E_UNSUPPORTED;
+  // the work split counts all pairs' list entries (at most 2 max_blocks each) in int32
+  if (static_cast<int64_t>(geom->batch) * geom->n_kv_heads *
+          (2 * static_cast<int64_t>(geom->max_blocks_per_seq) + 1) > INT32_MAX)
+    return ZR_E_UNSUPPORTED;
   const int nwg = zr::attn_workgroups(*geom, max_attended);
   const size_t need = zr::attn_workspace(*geom, nwg, nullptr, nullptr);
   if (geom->batch > 0 && (!workspace || ws_bytes < need || !aligned16(workspace)))

@@ -166,18 +166,19 @@ zr_status zr_select_topk(const zr_geom* geom, const zr_thoughts* th, const float
  * any order, repeats count once); k = 0 means window only (sel may then be
  * NULL).
  * Work split: one pair kernel lists each (b, g)'s attended 16-token blocks
- * with slot masks; the attention kernel gives each (b, g) a number of
- * workgroups proportional to its block count (the grid is sized from
- * `max_attended`, the caller's bound on tokens per (b, g); a larger count is
- * still handled correctly, only with a coarser split); a combine kernel
- * merges the partial softmax states by log-sum-exp. `workspace` holds the
- * block lists and partial results (no state is kept between calls); it must
+ * with slot masks; the attention kernel's workgroups take equal ranges of
+ * all (b, g) lists laid end to end (the grid is sized from `max_attended`,
+ * the caller's bound on tokens per (b, g); a larger count is still handled
+ * correctly, only with a coarser split); a combine kernel merges the
+ * partial softmax states by log-sum-exp. `workspace` holds the block lists
+ * (kept for zr_sparse_decode_attn_cached) and the partial results; it must
  * be at least zr_workspace_bytes(geom, max_attended) bytes and 16-byte
  * aligned, and calls that share a workspace must not run concurrently.
  * Errors: ZR_E_NULL, ZR_E_SHAPE (k, window, max_attended < 0; k > ZR_MAX_K),
  * ZR_E_UNSUPPORTED (also: the per-(b, g) lists do not fit the kernel's
- * on-chip memory, roughly max_blocks_per_seq > 20000), ZR_E_WORKSPACE,
- * ZR_E_ALIGN, ZR_E_LAUNCH.
+ * on-chip memory, roughly max_blocks_per_seq > 20000, or batch * n_kv_heads
+ * * (2 max_blocks_per_seq + 1) > INT32_MAX, the list entries the work split
+ * counts), ZR_E_WORKSPACE, ZR_E_ALIGN, ZR_E_LAUNCH.
  */
 zr_status zr_sparse_decode_attn(const zr_geom* geom, const void* q, const void* k_pool,
                                 const void* v_pool, const int32_t* block_table,

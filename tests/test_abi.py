@@ -128,6 +128,10 @@ def test_null_and_range_errors(L):
     assert sp(ws_bytes=need - 1) == zr.ZR_E_WORKSPACE
     assert zr.zr_dense_paged_decode_attn(g, FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, FAKE, 64) \
         == zr.ZR_E_WORKSPACE
+    # all pairs' list entries must be countable in int32 (4096 pairs x 2 x 300000 blocks)
+    big = _geom(batch=512, n_kv_heads=8, n_q_heads=32, max_blocks_per_seq=300000)
+    assert zr.zr_dense_paged_decode_attn(big, FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, FAKE,
+                                         1 << 40) == zr.ZR_E_UNSUPPORTED
 
 
 def test_step_errors(L):
