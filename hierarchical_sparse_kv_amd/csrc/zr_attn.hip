@@ -1087,57 +1087,106 @@ attn_valu_kernel(AttnArgs a) {
 // ---------------------------------------------------------------------------
 constexpr int kCombineTile = 8;
 
+// Log-sum-exp merge state of one item (4 dims of one head).
+struct MergeState {
+  float M, L;
+  float4 A;
+};
+
+// Merge slots [c0, s1) of one item, tiles of kCombineTile taken `stride`
+// slots apart, into st.
+template <int G, int D>
+__device__ __forceinline__ void merge_slots(const AttnArgs& a, int h, int e4, int c0, int s1,
+                                            int stride, MergeState& st) {
+  constexpr int D4 = D / 4;
+  const float4* acc4 = reinterpret_cast<const float4*>(a.ws_acc);
+  for (; c0 < s1; c0 += stride) {
+    float ms[kCombineTile], ls[kCombineTile];
+    float4 vs[kCombineTile];
+#pragma unroll
+    for (int u = 0; u < kCombineTile; ++u) {
+      const size_t s = static_cast<size_t>(c0 + u < s1 ? c0 + u : s1 - 1);
+      ms[u] = a.ws_m[s * G + h];
+      ls[u] = a.ws_l[s * G + h];
+      vs[u] = acc4[(s * G + h) * D4 + e4];
+      if (c0 + u >= s1) ms[u] = kNegInf;
+    }
+    float mt = st.M;
+#pragma unroll
+    for (int u = 0; u < kCombineTile; ++u) mt = fmaxf(mt, ms[u]);
+    if (mt == kNegInf) continue;
+    const float alpha = st.M == kNegInf ? 0.f : exp2f(st.M - mt);
+    st.L *= alpha;
+    st.A.x *= alpha;
+    st.A.y *= alpha;
+    st.A.z *= alpha;
+    st.A.w *= alpha;
+#pragma unroll
+    for (int u = 0; u < kCombineTile; ++u) {
+      const float w = ms[u] != kNegInf ? exp2f(ms[u] - mt) : 0.f;
+      st.L = fmaf(ls[u], w, st.L);
+      st.A.x = fmaf(vs[u].x, w, st.A.x);
+      st.A.y = fmaf(vs[u].y, w, st.A.y);
+      st.A.z = fmaf(vs[u].z, w, st.A.z);
+      st.A.w = fmaf(vs[u].w, w, st.A.w);
+    }
+    st.M = mt;
+  }
+}
+
+// One workgroup per pair. When a pair's items (G heads x D/4) leave threads
+// over, NGRP groups of threads take the tiles of partials in turn (so up to
+// NGRP tiles are loaded at once) and merge their states through LDS.
 template <int G, int D>
 __global__ void __launch_bounds__(kThreads)
 attn_combine_kernel(AttnArgs a) {
   constexpr int D4 = D / 4, ITEMS = G * D4, PER = (ITEMS + kThreads - 1) / kThreads;
+  constexpr int NGRP = ITEMS < kThreads ? kThreads / ITEMS : 1;
+  __shared__ MergeState sh[NGRP > 1 ? (NGRP - 1) * ITEMS : 1];
   const int g = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
   const int p = b * a.Hkv + g;
   const int s0 = a.ws_pref[p], s1 = a.ws_pref[p + 1];
   float4* out4 = reinterpret_cast<float4*>(a.out + (static_cast<size_t>(b) * a.Hq + g * G) * D);
-  const float4* acc4 = reinterpret_cast<const float4*>(a.ws_acc);
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int idx = t + j * kThreads;
-    if (idx >= ITEMS) continue;
-    const int h = idx / D4, e4 = idx % D4;
-    float M = kNegInf, Lsum = 0.f;
-    float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int c0 = s0; c0 < s1; c0 += kCombineTile) {
-      float ms[kCombineTile], ls[kCombineTile];
-      float4 vs[kCombineTile];
-#pragma unroll
-      for (int u = 0; u < kCombineTile; ++u) {
-        const size_t s = static_cast<size_t>(c0 + u < s1 ? c0 + u : s1 - 1);
-        ms[u] = a.ws_m[s * G + h];
-        ls[u] = a.ws_l[s * G + h];
-        vs[u] = acc4[(s * G + h) * D4 + e4];
-        if (c0 + u >= s1) ms[u] = kNegInf;
-      }
-      float mt = M;
-#pragma unroll
-      for (int u = 0; u < kCombineTile; ++u) mt = fmaxf(mt, ms[u]);
-      if (mt == kNegInf) continue;
-      const float alpha = M == kNegInf ? 0.f : exp2f(M - mt);
-      Lsum *= alpha;
-      A.x *= alpha;
-      A.y *= alpha;
-      A.z *= alpha;
-      A.w *= alpha;
-#pragma unroll
-      for (int u = 0; u < kCombineTile; ++u) {
-        const float w = ms[u] != kNegInf ? exp2f(ms[u] - mt) : 0.f;
-        Lsum = fmaf(ls[u], w, Lsum);
-        A.x = fmaf(vs[u].x, w, A.x);
-        A.y = fmaf(vs[u].y, w, A.y);
-        A.z = fmaf(vs[u].z, w, A.z);
-        A.w = fmaf(vs[u].w, w, A.w);
-      }
-      M = mt;
-    }
-    const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
-    out4[idx] = Lsum > 0.f ? make_float4(A.x * inv, A.y * inv, A.z * inv, A.w * inv)
+  auto finish = [&](int idx, const MergeState& st) {
+    const float inv = st.L > 0.f ? 1.f / st.L : 0.f;
+    out4[idx] = st.L > 0.f ? make_float4(st.A.x * inv, st.A.y * inv, st.A.z * inv, st.A.w * inv)
                            : make_float4(0.f, 0.f, 0.f, 0.f);
+  };
+  if constexpr (NGRP > 1) {
+    const int grp = t / ITEMS, idx = t - grp * ITEMS;
+    const int h = idx / D4, e4 = idx % D4;
+    MergeState st{kNegInf, 0.f, make_float4(0.f, 0.f, 0.f, 0.f)};
+    merge_slots<G, D>(a, h, e4, s0 + grp * kCombineTile, s1, NGRP * kCombineTile, st);
+    if (s1 - s0 <= kCombineTile) {  // one tile: group 0 holds everything (uniform)
+      if (grp == 0) finish(idx, st);
+      return;
+    }
+    if (grp > 0) sh[(grp - 1) * ITEMS + idx] = st;
+    __syncthreads();
+    if (grp > 0) return;
+#pragma unroll
+    for (int k = 0; k < NGRP - 1; ++k) {
+      const MergeState o = sh[k * ITEMS + idx];
+      if (o.M == kNegInf) continue;
+      const float mt = fmaxf(st.M, o.M);
+      const float fa = st.M == kNegInf ? 0.f : exp2f(st.M - mt), fb = exp2f(o.M - mt);
+      st.L = st.L * fa + o.L * fb;
+      st.A.x = st.A.x * fa + o.A.x * fb;
+      st.A.y = st.A.y * fa + o.A.y * fb;
+      st.A.z = st.A.z * fa + o.A.z * fb;
+      st.A.w = st.A.w * fa + o.A.w * fb;
+      st.M = mt;
+    }
+    finish(idx, st);
+  } else {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int idx = t + j * kThreads;
+      if (idx >= ITEMS) continue;
+      MergeState st{kNegInf, 0.f, make_float4(0.f, 0.f, 0.f, 0.f)};
+      merge_slots<G, D>(a, idx / D4, idx % D4, s0, s1, kCombineTile, st);
+      finish(idx, st);
+    }
   }
 }
 
