@@ -351,3 +351,23 @@ def test_range_meeting_more_than_64_pairs(n_short):
     w = synth.make_workload(1, device="cuda", seq_lens=lens,
                             overrides=dict(B=len(lens), thought=("uniform", 8, 400), k=4))
     run_and_check(w, f"ranges-over-64-pairs-{8 * len(lens)}", check_dense=True)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_shapes(seed):
+    """Seeded random batches: 1-48 sequences of 0-6000 tokens, 1/2/8 KV heads,
+    grouped or not, bf16 or fp32, k and window from 0 up, so the attention
+    plan meets empty pairs, single-block pairs and long ones under both plan
+    paths (up to 256 pairs per wave, more per workgroup)."""
+    rng = np.random.default_rng(1000 + seed)
+    dtype = ["bf16", "f32"][seed % 2]
+    Hkv = [1, 2, 8][seed % 3]
+    G = [1, 2, 4, 8][rng.integers(0, 4)]
+    B = 40 if seed == 2 else int(rng.integers(1, 49))  # seed 2: 320 pairs
+    lens = rng.integers(0, 6001, B)
+    lens[rng.random(B) < 0.2] = rng.integers(0, 40)
+    w = synth.make_workload(1, device="cuda", seq_lens=lens.tolist(), overrides=dict(
+        B=B, dtype=dtype, d=[64, 128][(seed // 2) % 2], Hq=Hkv * G, Hkv=Hkv,
+        thought=("uniform", 1, int(rng.integers(2, 300))), k=int(rng.integers(0, 12)),
+        window=int(rng.integers(0, 300))))
+    run_and_check(w, f"random-{seed}", check_dense=True)
