@@ -453,7 +453,7 @@ __device__ int plan_next(const AttnArgs& a, PlanLds& sm) {
       // else after all 64
       const uint64_t bput = __ballot(put);
       const int nput = __popcll(bput);
-      if (nput < __popcll(bal)) {
+      if (nput < static_cast<int>(__popcll(bal))) {
         const int last = 63 - __builtin_clzll(bput);
         p = p + last + 1;
         pos = __builtin_amdgcn_readlane(e, last);

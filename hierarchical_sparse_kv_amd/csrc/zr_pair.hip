@@ -107,8 +107,8 @@ __host__ __device__ inline size_t pair_lds_ints(int max_per_seq, int k, int max_
   return n;
 }
 
-__device__ inline PairLds pair_lds(int32_t* dyn, int max_per_seq, int k, int max_blocks,
-                                   bool select, bool plan, bool stage_th) {
+__device__ inline PairLds pair_lds(int32_t* dyn, int max_per_seq, int k, bool select, bool plan,
+                                   bool stage_th) {
   PairLds L{};
   int32_t* c = dyn;
   if (select) {
@@ -436,7 +436,7 @@ pair_kernel(PairArgs a) {
 
   const int p = blockIdx.x, t = threadIdx.x;
   const int b = p / a.Hkv, g = p - b * a.Hkv;
-  const PairLds L = pair_lds(dyn, a.max_per_seq, a.k, a.max_blocks, SELECT, PLAN, STH);
+  const PairLds L = pair_lds(dyn, a.max_per_seq, a.k, SELECT, PLAN, STH);
 
   using St = typename E::storage;
   const int c = t % LPT, r0 = t / LPT;
