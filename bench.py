@@ -263,9 +263,7 @@ def main():
 
         def boundary(_):
             for l, st in enumerate(zs):
-                st.coarse_score()
-                st.select_topk()
-                sel_stack[l].copy_(st.sel)
+                st.score_topk(sel=sel_stack[l])  # each layer's top-k straight into the stack
             zs[0].consensus(sel_stack, cz, votes, cons, agree)
             for st in zs:
                 st.zoom_attn(ss, sl, votes, cons, cz, npz)

@@ -164,6 +164,31 @@ ZR_API zr_status zr_select_topk(const zr_geom* geom, const zr_thoughts* th, cons
   return ZR_OK;
 }
 
+ZR_API zr_status zr_score_topk(const zr_geom* geom, const void* q, const zr_thoughts* th,
+                               int32_t k, float* scores, int32_t* sel, void* stream) {
+  zr_status st = check_geom(geom);
+  if (st != ZR_OK) return st;
+  st = check_thoughts(th, true);
+  if (st != ZR_OK) return st;
+  if (k < 0 || k > ZR_MAX_K) return ZR_E_SHAPE;
+  if (!q || !scores) return ZR_E_NULL;
+  if (k > 0 && !sel) return ZR_E_NULL;
+  if (!aligned16(q)) return ZR_E_ALIGN;
+  if (k == 0) return zr_coarse_score(geom, q, th, scores, stream);
+  if (!zr::pair_lds_ok(*geom, th->max_per_seq, k, true, false)) return ZR_E_UNSUPPORTED;
+  zr::PairArgs a{};
+  a.q = q;
+  a.kbar = th->summary_keys;
+  a.seq_ptr = th->seq_ptr;
+  a.scores = scores;
+  a.sel = sel;
+  fill_pair_sizes(*geom, *th, k, 0, &a);
+  if (zr::launch_pair(*geom, a, zr::kModeScoreSelect, static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return ZR_E_LAUNCH;
+  return ZR_OK;
+}
+
 ZR_API zr_status zr_sparse_decode_attn(const zr_geom* geom, const void* q, const void* k_pool,
                                        const void* v_pool, const int32_t* block_table,
                                        const int32_t* seq_lens, const zr_thoughts* th,

@@ -144,7 +144,8 @@ __device__ __forceinline__ float load_elem<BF16>(const uint16_t* p, size_t i) {
 
 // Pre-attention work of one (sequence, KV head) pair (zr_pair.hip): scores,
 // top-k and the attended-block list, by mode.
-enum PairMode { kModeScore = 0, kModeSelect = 1, kModePlan = 2, kModeStep = 3 };
+enum PairMode { kModeScore = 0, kModeSelect = 1, kModePlan = 2, kModeStep = 3,
+                kModeScoreSelect = 4 };
 
 struct PairArgs {
   const void* q;              // [B][Hq][D]                      (score)

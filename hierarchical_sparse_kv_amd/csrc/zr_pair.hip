@@ -813,6 +813,7 @@ hipError_t launch_pair(const zr_geom& gm, const PairArgs& a, int mode, hipStream
     case kModeSelect: return launch_pair_mode<false, true, false>(gm, a, s);
     case kModePlan: return launch_pair_mode<false, false, true>(gm, a, s);
     case kModeStep: return launch_pair_mode<true, true, true>(gm, a, s);
+    case kModeScoreSelect: return launch_pair_mode<true, true, false>(gm, a, s);
     default: return hipErrorInvalidValue;
   }
 }

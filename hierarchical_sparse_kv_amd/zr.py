@@ -50,6 +50,7 @@ _T = ctypes.POINTER(zr_thoughts)
 _SIGS = {
     "zr_coarse_score": (ctypes.c_int, [_G, _P, _T, _P, _P]),
     "zr_select_topk": (ctypes.c_int, [_G, _T, _P, ctypes.c_int32, _P, _P]),
+    "zr_score_topk": (ctypes.c_int, [_G, _P, _T, ctypes.c_int32, _P, _P, _P]),
     "zr_sparse_decode_attn": (ctypes.c_int, [_G, _P, _P, _P, _P, _P, _T, _P, ctypes.c_int32,
                                              ctypes.c_int32, ctypes.c_float, ctypes.c_int32,
                                              _P, _P, ctypes.c_size_t, _P]),
@@ -114,6 +115,11 @@ def zr_coarse_score(geom, q, th, scores, stream=None) -> int:
 
 def zr_select_topk(geom, th, scores, k, sel, stream=None) -> int:
     return lib().zr_select_topk(ctypes.byref(geom), ctypes.byref(th), scores, int(k), sel, stream)
+
+
+def zr_score_topk(geom, q, th, k, scores, sel, stream=None) -> int:
+    return lib().zr_score_topk(ctypes.byref(geom), q, ctypes.byref(th), int(k), scores, sel,
+                               stream)
 
 
 def zr_sparse_decode_attn(geom, q, k_pool, v_pool, block_table, seq_lens, th, sel, k, window,
@@ -266,6 +272,13 @@ class DeviceStep:
     def select_topk(self):
         check("zr_select_topk", zr_select_topk(self.geom, self.th, _ptr(self.scores), self.k,
                                                _ptr(self.sel) if self.k else None, _stream()))
+
+    def score_topk(self, sel=None):
+        """Scores and top-k in one call (zr_score_topk); sel defaults to self.sel."""
+        sel = self.sel if sel is None else sel
+        check("zr_score_topk", zr_score_topk(self.geom, _ptr(self.q), self.th, self.k,
+                                             _ptr(self.scores), _ptr(sel) if self.k else None,
+                                             _stream()))
 
     def sparse_attn(self, sel=None, out=None):
         sel = self.sel if sel is None else sel

@@ -155,6 +155,17 @@ zr_status zr_select_topk(const zr_geom* geom, const zr_thoughts* th, const float
                          int32_t k, int32_t* sel, void* stream);
 
 /*
+ * zr_coarse_score then zr_select_topk in one call (one kernel; scores and
+ * sel bit-identical to the two calls): the per-layer work of a semantic
+ * boundary before the consensus step (ZoomR Algorithm 1, scores and top-k of
+ * every head; Sec. 3.3). k = 0 writes the scores only (sel may be NULL).
+ * Errors: those of zr_coarse_score and zr_select_topk, and ZR_E_UNSUPPORTED
+ * when max_per_seq and k do not fit the kernel's on-chip memory.
+ */
+zr_status zr_score_topk(const zr_geom* geom, const void* q, const zr_thoughts* th, int32_t k,
+                        float* scores, int32_t* sel, void* stream);
+
+/*
  * Zoomed-in sparse decode attention (ZoomR, Sec. 3.3 eq. I_f restricted to
  * the recent window and the selected thoughts' full-resolution spans; Sec. 2
  * eq. A). For sequence b, KV head g the attended tokens are

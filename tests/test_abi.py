@@ -22,7 +22,8 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     declared = zr.header_symbols()
-    assert declared == sorted(["zr_coarse_score", "zr_select_topk", "zr_sparse_decode_attn",
+    assert declared == sorted(["zr_coarse_score", "zr_select_topk", "zr_score_topk",
+                               "zr_sparse_decode_attn",
                                "zr_sparse_decode_attn_cached", "zr_sparse_decode_step",
                                "zr_dense_paged_decode_attn", "zr_append_kv", "zr_summary_keys",
                                "zr_consensus", "zr_zoom_decode_attn",
@@ -109,6 +110,16 @@ def test_null_and_range_errors(L):
     assert zr.zr_select_topk(g, _th(), FAKE, 1025, FAKE) == zr.ZR_E_SHAPE
     assert zr.zr_select_topk(g, _th(), FAKE, 3, None) == zr.ZR_E_NULL
     assert zr.zr_select_topk(g, _th(seq_ptr=None), FAKE, 3, FAKE) == zr.ZR_E_NULL
+    st = lambda **kw: zr.zr_score_topk(**dict(dict(geom=g, q=FAKE, th=_th(), k=3, scores=FAKE,
+                                                    sel=FAKE), **kw))
+    assert st(k=-1) == zr.ZR_E_SHAPE
+    assert st(k=1025) == zr.ZR_E_SHAPE
+    assert st(sel=None) == zr.ZR_E_NULL
+    assert st(scores=None) == zr.ZR_E_NULL
+    assert st(q=None) == zr.ZR_E_NULL
+    assert st(th=_th(summary_keys=None)) == zr.ZR_E_NULL
+    assert st(q=FAKE + 4) == zr.ZR_E_ALIGN
+    assert st(th=_th(max_per_seq=100000)) == zr.ZR_E_UNSUPPORTED
     args = lambda **kw: dict(dict(geom=g, q=FAKE, k_pool=FAKE, v_pool=FAKE, block_table=FAKE,
                                   seq_lens=FAKE, th=_th(), sel=FAKE, k=2, window=16, scale=0.1,
                                   max_attended=100, out=FAKE, workspace=FAKE,

@@ -64,6 +64,13 @@ def run_and_check(w, name, k=None, check_dense=False):
     assert torch.equal(fused[0][:w.n_total], st.scores[:w.n_total]), name
     assert torch.equal(fused[1], st.sel), name
     assert torch.equal(fused[2], st.out), name
+    # scores + top-k in one call: the same bits as the two calls
+    st.scores.fill_(float("nan"))
+    st.sel.fill_(-7)
+    st.score_topk()
+    torch.cuda.synchronize()
+    assert torch.equal(fused[0][:w.n_total], st.scores[:w.n_total]), name
+    assert torch.equal(fused[1], st.sel), name
     scores = st.scores.cpu().numpy()[:w.n_total]
     sel = st.sel.cpu().numpy()
     out = st.out.cpu().numpy()
