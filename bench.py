@@ -265,14 +265,18 @@ def main():
             for l, st in enumerate(zs):
                 st.score_topk(sel=sel_stack[l])  # each layer's top-k straight into the stack
             zs[0].consensus(sel_stack, cz, votes, cons, agree)
-            for st in zs:
-                st.zoom_attn(ss, sl, votes, cons, cz, npz)
+            # the set is shared by every layer and head: its block lists are built
+            # once (layer 0) and every other layer attends on them
+            zs[0].zoom_attn(ss, sl, votes, cons, cz, npz)
+            for st in zs[1:]:
+                st.cached_attn(wz.window, workspace=zs[0].workspace)
 
         g_bound = capture(boundary, 1)
         g_bound.replay()
         torch.cuda.synchronize()
         bound_us = timed(g_bound, L)
-        g_between = capture(lambda i: zs[i % L].cached_attn(wz.window), args.steps)
+        g_between = capture(lambda i: zs[i % L].cached_attn(wz.window, workspace=zs[0].workspace),
+                            args.steps)
         between_us = timed(g_between, args.steps)
         v_h, c_h = votes.cpu().numpy(), cons.cpu().numpy()
         n_att = []

@@ -289,16 +289,19 @@ class DeviceStep:
             _ptr(sel) if self.k else None, self.k, self.window, self.scale, self.max_attended,
             _ptr(out), _ptr(self.workspace), self.workspace.numel(), _stream()))
 
-    def cached_attn(self, window, seq_lens=None, q=None, out=None):
+    def cached_attn(self, window, seq_lens=None, q=None, out=None, workspace=None):
         """Attention on the selection cached in the workspace by the last
-        sparse_attn / step call, with window `window` over `seq_lens`."""
+        sparse_attn / step / zoom_attn call, with window `window` over
+        `seq_lens`. `workspace`: another step's (same geometry), e.g. the
+        multi-granularity set that every layer shares."""
         seq_lens = self.seq_lens if seq_lens is None else seq_lens
         q = self.q if q is None else q
         out = self.out if out is None else out
+        ws = self.workspace if workspace is None else workspace
         check("zr_sparse_decode_attn_cached", zr_sparse_decode_attn_cached(
             self.geom, _ptr(q), self.kp, self.vp, _ptr(self.block_table),
             _ptr(seq_lens), int(window), self.scale, self.max_attended, _ptr(out),
-            _ptr(self.workspace), self.workspace.numel(), _stream()))
+            _ptr(ws), ws.numel(), _stream()))
 
     def append(self, k_new, v_new, free_blocks, free_count, status):
         """Append one token per sequence (zr_append_kv); updates this step's

@@ -138,6 +138,11 @@ def test_zoom_pipeline_two_layers():
     assert np.array_equal(votes.cpu().numpy(), v_ref)
     assert np.array_equal(cons.cpu().numpy(), c_ref)
     assert np.max(np.abs(agree.cpu().numpy() - a_ref)) <= 1e-6
+    # the set is the same for every layer: layer 1 attending on layer 0's
+    # block lists gives layer 1's own result, bit for bit
+    steps[1].cached_attn(w0.window, workspace=steps[0].workspace)
+    torch.cuda.synchronize()
+    assert np.array_equal(steps[1].out.cpu().numpy(), outs[1])
     for w, h, got in zip(layers, hosts, outs):
         ref = O.zoom_decode_step(h["q"], h["k_pool"], h["v_pool"], w.block_table, w.seq_lens,
                                  w.seq_ptr, w.th_start, w.th_len, w.extra["sum_start"],
