@@ -142,11 +142,15 @@ def test_append_table_full():
     assert np.array_equal(st.seq_lens.cpu().numpy(), w.seq_lens)
 
 
-@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 128)])
-def test_summary_keys_parity(dtype, d):
+@pytest.mark.parametrize("dtype,d,seq_len,thought", [
+    ("bf16", 128, ("uniform", 100, 3000), ("uniform", 1, 700)),
+    ("bf16", 64, ("uniform", 100, 3000), ("uniform", 1, 700)),
+    ("f32", 128, ("uniform", 100, 3000), ("uniform", 1, 700)),
+    # thoughts longer than one LDS window of block ids (8176 tokens)
+    ("bf16", 128, ("fixed", 40000), ("uniform", 8000, 20000))])
+def test_summary_keys_parity(dtype, d, seq_len, thought):
     w = synth.make_workload(1, device="cuda", overrides=dict(
-        B=3, dtype=dtype, d=d, Hq=8, Hkv=2, seq_len=("uniform", 100, 3000),
-        thought=("uniform", 1, 700)))
+        B=3, dtype=dtype, d=d, Hq=8, Hkv=2, seq_len=seq_len, thought=thought))
     st = zr.step_from_workload(w)
     out = torch.full_like(st.summary_keys, 7.0)
     which_np = np.concatenate([np.arange(w.n_total), [-1, w.n_total, 0]]).astype(np.int32)
