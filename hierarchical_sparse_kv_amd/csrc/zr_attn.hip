@@ -103,7 +103,7 @@ struct PairList {
 template <bool DENSE>
 __device__ __forceinline__ PairList pair_list(const AttnArgs& a, int p) {
   PairList r;
-  r.T = cached_len(a, p / a.Hkv);
+  r.T = cached_len(a, div_small(p, a.Hkv));
   r.tw = DENSE ? 0 : (r.T - a.window > 0 ? r.T - a.window : 0);
   r.ncache = 0;
   if (!DENSE) {
@@ -221,17 +221,22 @@ __device__ int plan_wave(const AttnArgs& a, PlanLds& sm, bool records, Assign* s
   const int nr = total < a.nwg ? total : a.nwg;  // ranges: none empty
 
   // whole-pair slices
-  const int per = total > 0 ? (total + a.nwg - 1) / a.nwg : 1;
-  const int range_max = nr > 0 ? (total + nr - 1) / nr : 0;
+  const int per = total > 0 ? floor_div(total - 1, a.nwg) + 1 : 1;
+  const int range_max = nr > 0 ? floor_div(total - 1, nr) + 1 : 0;
   const int cap = range_max + range_max / 8;
   int S[kLanePairs];
   int ssum = 0;
   bool uneven = false;
 #pragma unroll
   for (int j = 0; j < kLanePairs; ++j) {
-    S[j] = n[j] > 0 ? max(1, (n[j] + per / 2) / per) : 0;
-    ssum += S[j];
-    uneven = uneven || n[j] > S[j] * cap;
+    S[j] = 0;
+    if (j < K) {  // uniform: pair slots past K hold nothing and cost no division
+      // round(n / per), halves up, without forming n + per / 2
+      const int q = floor_div(n[j], per), r = n[j] - q * per;
+      S[j] = n[j] > 0 ? max(1, q + (r >= per - per / 2 ? 1 : 0)) : 0;
+      ssum += S[j];
+      uneven = uneven || n[j] > S[j] * cap;
+    }
   }
   const int sincl = wave_incl_sum(ssum);
   const int total_s = __builtin_amdgcn_readlane(sincl, 63);
@@ -248,22 +253,25 @@ __device__ int plan_wave(const AttnArgs& a, PlanLds& sm, bool records, Assign* s
     }
     if (w >= total_s) return 0;
     const bool mine = w >= srun && w < srun + ssum;
-    int pj = 0, tj = 0, cj = 0, lo = 0, hi = 0;
+    int pj = 0, tj = 0, cj = 0, nj = 0, sj = 1, r = 0;
     if (mine) {
       int r0 = srun;
 #pragma unroll
       for (int j = 0; j < kLanePairs; ++j) {
         if (w >= r0 && w < r0 + S[j]) {
-          const int r = w - r0;
+          r = w - r0;
           pj = p0 + j;
           tj = T[j];
           cj = nc[j];
-          lo = floor_div(static_cast<int64_t>(r) * n[j], S[j]);
-          hi = floor_div(static_cast<int64_t>(r + 1) * n[j], S[j]);
+          nj = n[j];
+          sj = S[j];
         }
         r0 += S[j];
       }
     }
+    // the slice bounds of the owning lane's pair only (one division pair)
+    const int lo = floor_div(static_cast<int64_t>(r) * nj, sj);
+    const int hi = floor_div(static_cast<int64_t>(r + 1) * nj, sj);
     const int src = __ffsll(static_cast<unsigned long long>(__ballot(mine))) - 1;
     lane_segment(src, pj, tj, window_start(tj), cj, lo, hi, w, sa);
     if (records && mine) put_record(sm, 0, pj, tj, window_start(tj), cj, lo, hi, w);
@@ -276,7 +284,7 @@ __device__ int plan_wave(const AttnArgs& a, PlanLds& sm, bool records, Assign* s
     int st = run;
 #pragma unroll
     for (int j = 0; j < kLanePairs; ++j) {
-      nssum += pair_slots(st, n[j], total, nr);
+      if (j < K) nssum += pair_slots(st, n[j], total, nr);
       st += n[j];
     }
   }
@@ -290,7 +298,7 @@ __device__ int plan_wave(const AttnArgs& a, PlanLds& sm, bool records, Assign* s
     for (int j = 0; j < kLanePairs; ++j) {
       if (publish && j < K && p0 + j < P) a.ws_pref[p0 + j] = bs;
       cnt += n[j] > 0 && st < R1 && st + n[j] > R0 ? 1 : 0;
-      bs += pair_slots(st, n[j], total, nr);
+      if (j < K) bs += pair_slots(st, n[j], total, nr);
       st += n[j];
     }
   }
@@ -321,7 +329,7 @@ __device__ int plan_wave(const AttnArgs& a, PlanLds& sm, bool records, Assign* s
         }
         ++ord;
       }
-      bs += pair_slots(st, n[j], total, nr);
+      if (j < K) bs += pair_slots(st, n[j], total, nr);
       st += n[j];
     }
   }
@@ -738,13 +746,15 @@ __device__ __forceinline__ void flush_state(const MfmaState& stt, const f32x4 (&
 template <int G, int D>
 __device__ __forceinline__ void load_q(const AttnArgs& a, int p, bf16x8 (&qop)[D / 32]) {
   const int lane = threadIdx.x & 63, l16 = lane & 15, lg = lane >> 4;
-  const int b = p / a.Hkv, g = p - b * a.Hkv;
+  const int b = div_small(p, a.Hkv), g = p - b * a.Hkv;
   const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
                          (static_cast<size_t>(b) * a.Hq + g * G + (l16 < G ? l16 : 0)) * D;
 #pragma unroll
-  for (int kk = 0; kk < D / 32; ++kk) {
-    const bf16x8 qv = *reinterpret_cast<const bf16x8*>(qrow + 32 * kk + 8 * lg);
-    qop[kk] = l16 < G ? qv : bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
+  for (int kk = 0; kk < D / 32; ++kk) qop[kk] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
+  if (l16 < G) {  // padding heads load nothing (fewer lanes through the address unit)
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk)
+      qop[kk] = *reinterpret_cast<const bf16x8*>(qrow + 32 * kk + 8 * lg);
   }
 }
 
@@ -777,7 +787,8 @@ attn_mfma_kernel(AttnArgs a) {
       sb = sa;
       sb.lo = sb.hi;
     }
-    const int gA = sa.p % a.Hkv, gB = sb.p % a.Hkv;
+    const int gA = sa.p - div_small(sa.p, a.Hkv) * a.Hkv;
+    const int gB = sb.p - div_small(sb.p, a.Hkv) * a.Hkv;
     const int nA = (sa.hi - sa.lo + NBW - 1) / NBW, nB = (sb.hi - sb.lo + NBW - 1) / NBW;
     const int ntot = nA + nB;
     const int nck_all = ntot > wave ? (ntot - wave + kWaves - 1) / kWaves : 0;
@@ -791,15 +802,6 @@ attn_mfma_kernel(AttnArgs a) {
     }
     // this wave's first query in registers; B's query goes to LDS for a wave
     // that crosses from A to B
-    bf16x8 qop[KS], qb[KS];
-    load_q<G, D>(a, iB > 0 ? sa.p : sb.p, qop);
-    const bool keep_b = iB > 0 && nck_all > iB;  // this wave crosses from A to B
-    if (keep_b) load_q<G, D>(a, sb.p, qb);
-    f32x4 o[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    MfmaState stt{kNegInf, 0.f, true};
-
     // one lane per entry: resolve a batch of the wave's entries at once
     int pb_l;
     uint32_t msk_l;
@@ -809,13 +811,20 @@ attn_mfma_kernel(AttnArgs a) {
       const bool inB = k >= nA;
       Assign al = inB ? sb : sa;
       const int j = inB ? sb.lo + (k - nA) * NBW + e % NBW : sa.lo + k * NBW + e % NBW;
-      resolve_entry<DENSE>(a, al, al.p / a.Hkv, j < al.hi ? j : -1, &pb_l, &msk_l);
+      resolve_entry<DENSE>(a, al, div_small(al.p, a.Hkv), j < al.hi ? j : -1, &pb_l, &msk_l);
     };
+    // the entries first: the first K/V loads wait for them, the queries are
+    // needed only once those loads have returned
     resolve_batch(0);
-    if (keep_b) {  // B's query was loaded before the entries: its wait overlaps theirs
+    bf16x8 qop[KS], qb[KS];
+    load_q<G, D>(a, iB > 0 ? sa.p : sb.p, qop);
+    const bool keep_b = iB > 0 && nck_all > iB;  // this wave crosses from A to B
+    if (keep_b) load_q<G, D>(a, sb.p, qb);
+    f32x4 o[NT];
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk) q_b[kk][lane] = qb[kk];
-    }
+    for (int nt = 0; nt < NT; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    MfmaState stt{kNegInf, 0.f, true};
+
     for (int c0 = 0; c0 < nck_all; c0 += CPB) {
       if (c0 > 0) resolve_batch(c0);
       const int nck = nck_all - c0 < CPB ? nck_all - c0 : CPB;
@@ -835,6 +844,10 @@ attn_mfma_kernel(AttnArgs a) {
       };
       Chunk<D, NBW> cA, cB;
       load_chunk<D, NBW>(a, c0 < iB ? gA : gB, 0, pb_l, msk_l, cA);
+      if (c0 == 0 && keep_b) {  // B's query to LDS once the first loads are out
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) q_b[kk][lane] = qb[kk];
+      }
       for (int c = 0; c < nck; c += 2) {
         switch_at(c);
         if (c + 1 < nck) load_chunk<D, NBW>(a, c0 + c + 1 < iB ? gA : gB, c + 1, pb_l, msk_l, cB);
@@ -867,19 +880,22 @@ attn_mfma_kernel(AttnArgs a) {
     }
     Assign as;
     get_record(psm, ri++, &as);
-    const int g = as.p % a.Hkv;
+    const int b = div_small(as.p, a.Hkv), g = as.p - b * a.Hkv;
+    const int nck_all = wave_chunks<NBW>(as, wave);
+    int pb_l;
+    uint32_t msk_l;
+    auto resolve_batch = [&](int c0) {
+      resolve_entry<DENSE>(a, as, b, wave_entry<NBW>(as, wave, c0 * NBW + lane), &pb_l, &msk_l);
+    };
+    resolve_batch(0);  // the entries before the query, as in the streamed path
     bf16x8 qop[KS];
     load_q<G, D>(a, as.p, qop);
     f32x4 o[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     MfmaState stt{kNegInf, 0.f, true};
-    const int nck_all = wave_chunks<NBW>(as, wave);
     for (int c0 = 0; c0 < nck_all; c0 += CPB) {
-      int pb_l;
-      uint32_t msk_l;
-      resolve_entry<DENSE>(a, as, as.p / a.Hkv, wave_entry<NBW>(as, wave, c0 * NBW + lane),
-                           &pb_l, &msk_l);
+      if (c0 > 0) resolve_batch(c0);
       const int nck = nck_all - c0 < CPB ? nck_all - c0 : CPB;
       for (int c = 0; c < nck; ++c) {
         Chunk<D, NBW> ch;

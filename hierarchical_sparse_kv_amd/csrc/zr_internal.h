@@ -44,6 +44,20 @@ __device__ __forceinline__ void unpack16<BF16>(const uint4& u, float* out) {
 }
 
 // ---------------------------------------------------------------------------
+// n / d for 0 <= n < 2^16, d >= 1, in a few instructions (the general 32-bit
+// integer division is about 30). The float32 estimate n * rcp(d) is within 1
+// of n / d whenever rcp(d) is accurate to 2^-16 relative (the hardware
+// reciprocal is accurate to about 1 ulp), and one correction step each way
+// makes it exact.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int div_small(int n, int d) {
+  int q = static_cast<int>(static_cast<float>(n) * __builtin_amdgcn_rcpf(static_cast<float>(d)));
+  q += (q + 1) * d <= n ? 1 : 0;
+  q -= q * d > n ? 1 : 0;
+  return q;
+}
+
+// ---------------------------------------------------------------------------
 // Cross-lane helpers built on DPP (data-parallel primitives inside the VALU,
 // no LDS round trip). DPP controls: quad_perm 0x00-0xff, row_shr:n 0x110+n,
 // row_mirror 0x140, row_half_mirror 0x141, row_bcast:15 0x142,
