@@ -434,13 +434,14 @@ pair_kernel(PairArgs a) {
   __shared__ uint32_t hist[kPairThreads];
   __shared__ uint32_t sh[2];
 
-  const int p = blockIdx.x, t = threadIdx.x;
-  const int b = p / a.Hkv, g = p - b * a.Hkv;
+  // grid (Hkv, B): the pair's indices need no division
+  const int g = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
+  const int p = b * a.Hkv + g;
   const PairLds L = pair_lds(dyn, a.max_per_seq, a.k, SELECT, PLAN, STH);
 
   using St = typename E::storage;
   const int c = t % LPT, r0 = t / LPT;
-  const int G = a.Hq / a.Hkv;
+  const int G = a.G;
 
   // --- loads that need nothing but the pair index, all issued up front:
   // thought range, sequence length, query rows, block-table row, given sel
@@ -700,8 +701,8 @@ __global__ void __launch_bounds__(kPairThreads)
 zoom_plan_kernel(PairArgs a) {
   extern __shared__ __align__(16) int32_t dyn[];
   __shared__ int wtmp[kPairWaves];
-  const int p = blockIdx.x, t = threadIdx.x;
-  const int b = p / a.Hkv;
+  const int b = blockIdx.y, t = threadIdx.x;  // grid (Hkv, B)
+  const int p = b * a.Hkv + blockIdx.x;
   int* flag = dyn;  // [up4(max_per_seq)]: 1 = consensus thought
   PairLds L{};
   L.bmask = reinterpret_cast<uint32_t*>(dyn + up4(a.max_per_seq));
@@ -783,7 +784,8 @@ static hipError_t launch_pair_t(const zr_geom& gm, PairArgs a, hipStream_t s) {
   }
   const size_t lds = pair_dyn_lds(a, SELECT, PLAN);
   if (kPairStaticLds + lds > kPairLdsLimit) return hipErrorInvalidValue;
-  const dim3 grid(gm.batch * gm.n_kv_heads);
+  a.G = gm.n_q_heads / gm.n_kv_heads;
+  const dim3 grid(gm.n_kv_heads, gm.batch);
   if (a.stage_th)
     hipLaunchKernelGGL((pair_kernel<E, D, SCORE, SELECT, PLAN, true>), grid, dim3(kPairThreads),
                        lds, s, a);
@@ -850,7 +852,7 @@ hipError_t launch_zoom_plan(const zr_geom& gm, const PairArgs& a0, hipStream_t s
   if (gm.batch == 0) return hipSuccess;
   PairArgs a = a0;
   a.bt_per = pair_bt_per(gm.max_blocks_per_seq);
-  hipLaunchKernelGGL(zoom_plan_kernel, dim3(gm.batch * gm.n_kv_heads), dim3(kPairThreads),
+  hipLaunchKernelGGL(zoom_plan_kernel, dim3(gm.n_kv_heads, gm.batch), dim3(kPairThreads),
                      zoom_lds(gm, a.max_per_seq), s, a);
   return hipGetLastError();
 }
