@@ -35,8 +35,8 @@ HBM_PEAK_GBS = 8000.0
 # soon as any of these files changes.
 TRAFFIC_SOURCES = ("zr_internal.h", "zr_pair.hip", "zr_attn.hip")
 TRAFFIC = {
-    "sources_sha256": "155f76f98c946982f1ddbe0048d3cada8ba542a1449d66866c9c7d32d9c22e63",
-    "bytes_per_call": 80908957,  # 79,689,985 fetched + 1,218,972 written
+    "sources_sha256": "fcb4715054094c9795fc5e7ccff53f54fb47e193003adcfa79aba968c9bf70c6",
+    "bytes_per_call": 80908614,  # 79,689,640 fetched + 1,218,974 written
 }
 
 
