@@ -27,16 +27,15 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 
-# HBM bytes per launch of the attention + combine kernels on this workload,
-# from hardware counters (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE, summed
-# over the two kernels, each scaled by the counter's reading for a known-size
-# copy).
+# HBM bytes per launch of the attention kernel on this workload, from hardware
+# counters (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE, each scaled by the
+# counter's reading for a known-size copy).
 # Valid only for the kernel sources they were taken with: reported as null as
 # soon as any of these files changes.
 TRAFFIC_SOURCES = ("zr_internal.h", "zr_pair.hip", "zr_attn.hip")
 TRAFFIC = {
-    "sources_sha256": "fcb4715054094c9795fc5e7ccff53f54fb47e193003adcfa79aba968c9bf70c6",
-    "bytes_per_call": 80908614,  # 79,689,640 fetched + 1,218,974 written
+    "sources_sha256": "5c69bc10b21ef1707e8bccb4755499b53c8c9c61b6ee61c65d259e2e3d59f7b8",
+    "bytes_per_call": 79653384,  # 78,565,486 fetched + 1,087,898 written
 }
 
 
@@ -182,10 +181,10 @@ def main():
     attn_us = timed(g_attn, args.steps)
     bytes_per_launch = float(np.mean([kv_bytes[i % L] for i in range(args.steps)]))
 
-    # dominant kernels: attention + combine alone, i.e. zr_sparse_decode_attn_cached
-    # on the lists zr_sparse_decode_attn leaves in each layer's workspace (same
-    # window, so the same attended set), timed with HIP events around a graph of
-    # back-to-back calls on the stream they run on
+    # attention + combine alone: zr_sparse_decode_attn_cached on the lists
+    # zr_sparse_decode_attn leaves in each layer's workspace (same window, so the
+    # same attended set), timed with HIP events around a graph of back-to-back
+    # calls on the stream they run on
     for st in steps:
         st.sparse_attn()
     steps[0].sparse_attn()
@@ -196,7 +195,19 @@ def main():
     assert torch.equal(ref_out, steps[0].out), "cached call differs from the full call"
     g_gather = capture(lambda i: steps[i % L].cached_attn(w0.window), args.steps)
     gather_us = timed(g_gather, args.steps)
-    achieved = bytes_per_launch / (gather_us * 1e-6) / 1e9
+    call_gbs = bytes_per_launch / (gather_us * 1e-6) / 1e9
+
+    # the dominant kernel alone: zr_sparse_decode_attn_partials launches only the
+    # attention kernel (its partials + zr_attn_combine give the same output bit
+    # for bit, checked here), timed the same way
+    steps[0].out.fill_(float("nan"))
+    steps[0].cached_partials(w0.window)
+    steps[0].combine()
+    torch.cuda.synchronize()
+    assert torch.equal(ref_out, steps[0].out), "partials + combine differ from the full call"
+    g_part = capture(lambda i: steps[i % L].cached_partials(w0.window), args.steps)
+    kernel_us = timed(g_part, args.steps)
+    achieved = bytes_per_launch / (kernel_us * 1e-6) / 1e9
 
     # selection reuse (ZoomR Sec. 3.4, Appendix A.3): the attended set is
     # rebuilt at semantic boundaries, about every 35 tokens. Each layer runs
@@ -397,11 +408,14 @@ def main():
                      "traffic": (TRAFFIC["bytes_per_call"]
                                  if TRAFFIC and TRAFFIC["sources_sha256"] == sources_sha256()
                                  else None),
-                     "kernel": "attn_mfma_kernel + attn_combine_kernel (one "
-                               "zr_sparse_decode_attn_cached call on the block lists of "
-                               "zr_sparse_decode_attn)",
-                     "avg_launch_us": round(gather_us, 3),
+                     "kernel": "attn_mfma_kernel (one zr_sparse_decode_attn_partials call "
+                               "on the block lists of zr_sparse_decode_attn)",
+                     "avg_launch_us": round(kernel_us, 3),
                      "algorithmic_bytes_per_launch": int(bytes_per_launch)},
+        "attn_and_combine": {"call": "zr_sparse_decode_attn_cached (attn_mfma_kernel + "
+                                     "attn_combine_kernel)",
+                             "avg_launch_us": round(gather_us, 3), "gbs": round(call_gbs, 1),
+                             "frac": round(call_gbs / HBM_PEAK_GBS, 4)},
         "sparse_attn_call_us": round(attn_us, 3),
         "sparse_attn_call_gbs": round(bytes_per_launch / (attn_us * 1e-6) / 1e9, 1),
         "step_as_three_calls_us": round(calls_us, 3),
@@ -416,7 +430,7 @@ def main():
                         "summary_keys_us": round(summary_us, 3),
                         "summary_thoughts_per_call": int(w0.B),
                         "summary_tokens_per_call": int(w0.th_len[which_np].sum())},
-        "effective_kv_gbs": round(achieved, 1),
+        "effective_kv_gbs": round(call_gbs, 1),
         "kv_tokens_per_step": int(np.mean([a.sum() for a in att])),
         "q_out_bytes_per_step": q_out_bytes,
         "dense_baseline": {"avg_launch_us": round(dense_us, 3), "kv_bytes": dense_bytes,

@@ -42,14 +42,35 @@ zr_status check_thoughts(const zr_thoughts* th, bool need_keys) {
   return ZR_OK;
 }
 
+// The workspace of the attention calls for `max_attended` (its layout depends on
+// the grid size), checked and laid out into *a.
+zr_status attention_workspace(const zr_geom* geom, int32_t max_attended, void* workspace,
+                              size_t ws_bytes, zr::AttnArgs* a) {
+  if (max_attended < 0) return ZR_E_SHAPE;
+  if (static_cast<int64_t>(geom->batch) * geom->n_kv_heads > ZR_MAX_PAIRS)
+    return ZR_E_UNSUPPORTED;
+  const int nwg = zr::attn_workgroups(*geom, max_attended);
+  const size_t need = zr::attn_workspace(*geom, nwg, nullptr, nullptr);
+  if (geom->batch > 0 && (!workspace || ws_bytes < need || !aligned16(workspace)))
+    return ZR_E_WORKSPACE;
+  zr::attn_workspace(*geom, nwg, workspace, a);
+  a->B = geom->batch;
+  a->Hq = geom->n_q_heads;
+  a->Hkv = geom->n_kv_heads;
+  return ZR_OK;
+}
+
+// `out` may be null only when need_out is false (the partials-only call).
 zr_status attention_common(const zr_geom* geom, const void* q, const void* k_pool,
                            const void* v_pool, const int32_t* block_table,
                            const int32_t* seq_lens, float scale, float* out, void* workspace,
-                           size_t ws_bytes, int32_t max_attended, zr::AttnArgs* a) {
+                           size_t ws_bytes, int32_t max_attended, zr::AttnArgs* a,
+                           bool need_out = true) {
   zr_status st = check_geom(geom);
   if (st != ZR_OK) return st;
-  if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !out) return ZR_E_NULL;
-  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out))
+  if (!q || !k_pool || !v_pool || !block_table || !seq_lens || (need_out && !out))
+    return ZR_E_NULL;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || (out && !aligned16(out)))
     return ZR_E_ALIGN;
   if (max_attended < 0) return ZR_E_SHAPE;
   if (!isfinite(scale)) return ZR_E_SHAPE;
@@ -59,20 +80,14 @@ zr_status attention_common(const zr_geom* geom, const void* q, const void* k_poo
   if (static_cast<int64_t>(geom->batch) * geom->n_kv_heads *
           (2 * static_cast<int64_t>(geom->max_blocks_per_seq) + 1) > INT32_MAX)
     return ZR_E_UNSUPPORTED;
-  const int nwg = zr::attn_workgroups(*geom, max_attended);
-  const size_t need = zr::attn_workspace(*geom, nwg, nullptr, nullptr);
-  if (geom->batch > 0 && (!workspace || ws_bytes < need || !aligned16(workspace)))
-    return ZR_E_WORKSPACE;
-  zr::attn_workspace(*geom, nwg, workspace, a);
+  st = attention_workspace(geom, max_attended, workspace, ws_bytes, a);
+  if (st != ZR_OK) return st;
   a->q = q;
   a->k_pool = k_pool;
   a->v_pool = v_pool;
   a->block_table = block_table;
   a->seq_lens = seq_lens;
   a->out = out;
-  a->B = geom->batch;
-  a->Hq = geom->n_q_heads;
-  a->Hkv = geom->n_kv_heads;
   a->max_blocks = geom->max_blocks_per_seq;
   a->num_blocks = geom->num_blocks;
   a->scale_log2 = scale * kLog2e;
@@ -267,6 +282,41 @@ ZR_API zr_status zr_sparse_decode_attn_cached(const zr_geom* geom, const void* q
   if (st != ZR_OK) return st;
   a.window = window;
   if (zr::launch_attention(*geom, a, false, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return ZR_E_LAUNCH;
+  return ZR_OK;
+}
+
+ZR_API zr_status zr_sparse_decode_attn_partials(const zr_geom* geom, const void* q,
+                                                const void* k_pool, const void* v_pool,
+                                                const int32_t* block_table,
+                                                const int32_t* seq_lens, int32_t window,
+                                                float scale, int32_t max_attended,
+                                                void* workspace, size_t ws_bytes,
+                                                void* stream) {
+  zr_status st = check_geom(geom);
+  if (st != ZR_OK) return st;
+  if (window < 0) return ZR_E_SHAPE;
+  zr::AttnArgs a{};
+  st = attention_common(geom, q, k_pool, v_pool, block_table, seq_lens, scale, nullptr,
+                        workspace, ws_bytes, max_attended, &a, false);
+  if (st != ZR_OK) return st;
+  a.window = window;
+  if (zr::launch_attention_partials(*geom, a, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return ZR_E_LAUNCH;
+  return ZR_OK;
+}
+
+ZR_API zr_status zr_attn_combine(const zr_geom* geom, int32_t max_attended, float* out,
+                                 void* workspace, size_t ws_bytes, void* stream) {
+  zr_status st = check_geom(geom);
+  if (st != ZR_OK) return st;
+  if (!out) return ZR_E_NULL;
+  if (!aligned16(out)) return ZR_E_ALIGN;
+  zr::AttnArgs a{};
+  st = attention_workspace(geom, max_attended, workspace, ws_bytes, &a);
+  if (st != ZR_OK) return st;
+  a.out = out;
+  if (zr::launch_combine(*geom, a, static_cast<hipStream_t>(stream)) != hipSuccess)
     return ZR_E_LAUNCH;
   return ZR_OK;
 }

@@ -1248,59 +1248,87 @@ size_t attn_workspace(const zr_geom& gm, int nwg, void* ws, AttnArgs* a) {
   return pref_b + cnt_b + ent_b + 2 * ml_b + acc_b;
 }
 
+// What a launch runs: the attention kernel (partials into the workspace), the
+// combine kernel (partials -> out), or both in turn.
+enum AttnParts { kAttnOnly = 1, kCombineOnly = 2, kAttnAndCombine = 3 };
+
 template <int G, int D>
-static hipError_t launch_mfma(const zr_geom& gm, const AttnArgs& a, bool dense, hipStream_t s) {
-  const dim3 grid(a.nwg);
-  if (dense)
-    hipLaunchKernelGGL((attn_mfma_kernel<G, D, kMfmaNBW, true>), grid, dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((attn_mfma_kernel<G, D, kMfmaNBW, false>), grid, dim3(kThreads), 0, s, a);
-  const hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+static hipError_t launch_combine_gd(const zr_geom& gm, const AttnArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((attn_combine_kernel<G, D>), dim3(gm.n_kv_heads, gm.batch), dim3(kThreads),
                      0, s, a);
   return hipGetLastError();
+}
+
+template <int G, int D>
+static hipError_t launch_mfma(const zr_geom& gm, const AttnArgs& a, bool dense, int parts,
+                              hipStream_t s) {
+  if (parts & kAttnOnly) {
+    const dim3 grid(a.nwg);
+    if (dense)
+      hipLaunchKernelGGL((attn_mfma_kernel<G, D, kMfmaNBW, true>), grid, dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((attn_mfma_kernel<G, D, kMfmaNBW, false>), grid, dim3(kThreads), 0, s, a);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  return (parts & kCombineOnly) ? launch_combine_gd<G, D>(gm, a, s) : hipSuccess;
 }
 
 template <typename E, int G, int D>
-static hipError_t launch_valu(const zr_geom& gm, const AttnArgs& a, bool dense, hipStream_t s) {
-  const dim3 grid(a.nwg);
-  if (dense)
-    hipLaunchKernelGGL((attn_valu_kernel<E, G, D, true>), grid, dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((attn_valu_kernel<E, G, D, false>), grid, dim3(kThreads), 0, s, a);
-  const hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((attn_combine_kernel<G, D>), dim3(gm.n_kv_heads, gm.batch), dim3(kThreads),
-                     0, s, a);
-  return hipGetLastError();
+static hipError_t launch_valu(const zr_geom& gm, const AttnArgs& a, bool dense, int parts,
+                              hipStream_t s) {
+  if (parts & kAttnOnly) {
+    const dim3 grid(a.nwg);
+    if (dense)
+      hipLaunchKernelGGL((attn_valu_kernel<E, G, D, true>), grid, dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((attn_valu_kernel<E, G, D, false>), grid, dim3(kThreads), 0, s, a);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  return (parts & kCombineOnly) ? launch_combine_gd<G, D>(gm, a, s) : hipSuccess;
 }
 
 template <int D>
-static hipError_t launch_d(const zr_geom& gm, const AttnArgs& a, bool dense, hipStream_t s) {
+static hipError_t launch_d(const zr_geom& gm, const AttnArgs& a, bool dense, int parts,
+                           hipStream_t s) {
   const int G = gm.n_q_heads / gm.n_kv_heads;
   if (gm.dtype == ZR_BF16) {
     switch (G) {
-      case 1: return launch_mfma<1, D>(gm, a, dense, s);
-      case 2: return launch_mfma<2, D>(gm, a, dense, s);
-      case 4: return launch_mfma<4, D>(gm, a, dense, s);
-      case 8: return launch_mfma<8, D>(gm, a, dense, s);
-      case 16: return launch_mfma<16, D>(gm, a, dense, s);
+      case 1: return launch_mfma<1, D>(gm, a, dense, parts, s);
+      case 2: return launch_mfma<2, D>(gm, a, dense, parts, s);
+      case 4: return launch_mfma<4, D>(gm, a, dense, parts, s);
+      case 8: return launch_mfma<8, D>(gm, a, dense, parts, s);
+      case 16: return launch_mfma<16, D>(gm, a, dense, parts, s);
       default: return hipErrorInvalidValue;
     }
   }
   switch (G) {
-    case 1: return launch_valu<F32, 1, D>(gm, a, dense, s);
-    case 2: return launch_valu<F32, 2, D>(gm, a, dense, s);
-    case 4: return launch_valu<F32, 4, D>(gm, a, dense, s);
-    case 8: return launch_valu<F32, 8, D>(gm, a, dense, s);
+    case 1: return launch_valu<F32, 1, D>(gm, a, dense, parts, s);
+    case 2: return launch_valu<F32, 2, D>(gm, a, dense, parts, s);
+    case 4: return launch_valu<F32, 4, D>(gm, a, dense, parts, s);
+    case 8: return launch_valu<F32, 8, D>(gm, a, dense, parts, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_attention(const zr_geom& gm, const AttnArgs& a, bool dense, hipStream_t s) {
+static hipError_t launch_parts(const zr_geom& gm, const AttnArgs& a, bool dense, int parts,
+                               hipStream_t s) {
   if (gm.batch == 0) return hipSuccess;
-  return gm.head_dim == 128 ? launch_d<128>(gm, a, dense, s) : launch_d<64>(gm, a, dense, s);
+  return gm.head_dim == 128 ? launch_d<128>(gm, a, dense, parts, s)
+                            : launch_d<64>(gm, a, dense, parts, s);
+}
+
+hipError_t launch_attention(const zr_geom& gm, const AttnArgs& a, bool dense, hipStream_t s) {
+  return launch_parts(gm, a, dense, kAttnAndCombine, s);
+}
+
+hipError_t launch_attention_partials(const zr_geom& gm, const AttnArgs& a, hipStream_t s) {
+  return launch_parts(gm, a, false, kAttnOnly, s);
+}
+
+hipError_t launch_combine(const zr_geom& gm, const AttnArgs& a, hipStream_t s) {
+  return launch_parts(gm, a, false, kCombineOnly, s);
 }
 
 }  // namespace zr

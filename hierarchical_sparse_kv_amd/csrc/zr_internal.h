@@ -265,5 +265,9 @@ int attn_workgroups(const zr_geom& g, int32_t max_attended);
 // acc [nwg + P][G][D].
 size_t attn_workspace(const zr_geom& g, int nwg, void* ws, AttnArgs* a);
 hipError_t launch_attention(const zr_geom& g, const AttnArgs& a, bool dense, hipStream_t s);
+// The sparse attention kernel alone (partials stay in the workspace), and the
+// combine kernel alone (the workspace's partials -> a.out).
+hipError_t launch_attention_partials(const zr_geom& g, const AttnArgs& a, hipStream_t s);
+hipError_t launch_combine(const zr_geom& g, const AttnArgs& a, hipStream_t s);
 
 }  // namespace zr

@@ -60,6 +60,10 @@ _SIGS = {
     "zr_sparse_decode_attn_cached": (ctypes.c_int, [_G, _P, _P, _P, _P, _P, ctypes.c_int32,
                                                     ctypes.c_float, ctypes.c_int32, _P, _P,
                                                     ctypes.c_size_t, _P]),
+    "zr_sparse_decode_attn_partials": (ctypes.c_int, [_G, _P, _P, _P, _P, _P, ctypes.c_int32,
+                                                      ctypes.c_float, ctypes.c_int32, _P,
+                                                      ctypes.c_size_t, _P]),
+    "zr_attn_combine": (ctypes.c_int, [_G, ctypes.c_int32, _P, _P, ctypes.c_size_t, _P]),
     "zr_consensus": (ctypes.c_int, [_G, _T, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                     _P, _P, _P, _P]),
     "zr_zoom_decode_attn": (ctypes.c_int, [_G, _P, _P, _P, _P, _P, _T, _P, _P, _P, _P,
@@ -144,6 +148,19 @@ def zr_sparse_decode_attn_cached(geom, q, k_pool, v_pool, block_table, seq_lens,
                                               seq_lens, int(window), float(scale),
                                               int(max_attended), out, workspace, int(ws_bytes),
                                               stream)
+
+
+def zr_sparse_decode_attn_partials(geom, q, k_pool, v_pool, block_table, seq_lens, window,
+                                   scale, max_attended, workspace, ws_bytes, stream=None) -> int:
+    return lib().zr_sparse_decode_attn_partials(ctypes.byref(geom), q, k_pool, v_pool,
+                                                block_table, seq_lens, int(window), float(scale),
+                                                int(max_attended), workspace, int(ws_bytes),
+                                                stream)
+
+
+def zr_attn_combine(geom, max_attended, out, workspace, ws_bytes, stream=None) -> int:
+    return lib().zr_attn_combine(ctypes.byref(geom), int(max_attended), out, workspace,
+                                 int(ws_bytes), stream)
 
 
 def zr_consensus(geom, th, sel, n_layers, k, c, votes, cons, agree, stream=None) -> int:
@@ -302,6 +319,25 @@ class DeviceStep:
             self.geom, _ptr(q), self.kp, self.vp, _ptr(self.block_table),
             _ptr(seq_lens), int(window), self.scale, self.max_attended, _ptr(out),
             _ptr(ws), ws.numel(), _stream()))
+
+    def cached_partials(self, window, seq_lens=None, q=None, workspace=None):
+        """The attention pass of cached_attn alone: partial softmax states
+        stay in the workspace for combine()."""
+        seq_lens = self.seq_lens if seq_lens is None else seq_lens
+        q = self.q if q is None else q
+        ws = self.workspace if workspace is None else workspace
+        check("zr_sparse_decode_attn_partials", zr_sparse_decode_attn_partials(
+            self.geom, _ptr(q), self.kp, self.vp, _ptr(self.block_table),
+            _ptr(seq_lens), int(window), self.scale, self.max_attended,
+            _ptr(ws), ws.numel(), _stream()))
+
+    def combine(self, out=None, workspace=None):
+        """Merge the partial states the last attention call left in the
+        workspace into `out`."""
+        out = self.out if out is None else out
+        ws = self.workspace if workspace is None else workspace
+        check("zr_attn_combine", zr_attn_combine(
+            self.geom, self.max_attended, _ptr(out), _ptr(ws), ws.numel(), _stream()))
 
     def append(self, k_new, v_new, free_blocks, free_count, status):
         """Append one token per sequence (zr_append_kv); updates this step's

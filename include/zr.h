@@ -20,6 +20,8 @@
  *   the workspace, for the decode steps between semantic boundaries, where
  *   ZoomR keeps the attended set and only the recent tokens grow (ZoomR
  *   Sec. 3.4 and Appendix A.3; Algorithm 1 rebuilds it at boundaries only).
+ *   zr_sparse_decode_attn_partials and zr_attn_combine are its two passes
+ *   (split-K attention, then the log-sum-exp merge) as separate calls.
  *   zr_dense_paged_decode_attn is the dense baseline: attention over every
  *   cached token through the same block table (same page, eq. 4).
  *   zr_consensus and zr_zoom_decode_attn are ZoomR's full multi-granularity
@@ -219,6 +221,37 @@ zr_status zr_sparse_decode_attn_cached(const zr_geom* geom, const void* q, const
                                        const int32_t* seq_lens, int32_t window, float scale,
                                        int32_t max_attended, float* out, void* workspace,
                                        size_t ws_bytes, void* stream);
+
+/*
+ * The two passes of zr_sparse_decode_attn_cached as separate calls: the
+ * split-K attention and the log-sum-exp combine (ZoomR Sec. 2 eq. A computed
+ * as a sum over blocks, KV-cache management page eq. 4, in pieces whose
+ * softmax states are merged afterwards).
+ *
+ * zr_sparse_decode_attn_partials runs the attention kernel only, on the block
+ * lists and with the arguments of zr_sparse_decode_attn_cached (no `out`): for
+ * every piece of the (b, g) lists it leaves the running maximum, sum and
+ * weighted value sum of each query head in the workspace.
+ * zr_attn_combine merges the partial states the last attention call on
+ * `workspace` left (this one, or any attention call, which combines them
+ * itself as well) into out[b][h] ([batch][n_q_heads][head_dim] float32,
+ * 16-byte aligned). It must get the geom and max_attended of that call, which
+ * fix the workspace layout; the workspace is only read.
+ * partials followed by combine give bit for bit the output of
+ * zr_sparse_decode_attn_cached with the same arguments. Workspace ownership
+ * and concurrency as zr_sparse_decode_attn.
+ * Errors: those of zr_sparse_decode_attn_cached; for zr_attn_combine
+ * ZR_E_NULL (out), ZR_E_ALIGN (out), ZR_E_SHAPE (max_attended < 0),
+ * ZR_E_UNSUPPORTED (geometry, batch * n_kv_heads > ZR_MAX_PAIRS),
+ * ZR_E_WORKSPACE, ZR_E_LAUNCH.
+ */
+zr_status zr_sparse_decode_attn_partials(const zr_geom* geom, const void* q, const void* k_pool,
+                                         const void* v_pool, const int32_t* block_table,
+                                         const int32_t* seq_lens, int32_t window, float scale,
+                                         int32_t max_attended, void* workspace,
+                                         size_t ws_bytes, void* stream);
+zr_status zr_attn_combine(const zr_geom* geom, int32_t max_attended, float* out,
+                          void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * One whole sparse decode step: zr_coarse_score, zr_select_topk and

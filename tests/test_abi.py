@@ -25,6 +25,7 @@ def test_exports_every_declared_symbol(L):
     assert declared == sorted(["zr_coarse_score", "zr_select_topk", "zr_score_topk",
                                "zr_sparse_decode_attn",
                                "zr_sparse_decode_attn_cached", "zr_sparse_decode_step",
+                               "zr_sparse_decode_attn_partials", "zr_attn_combine",
                                "zr_dense_paged_decode_attn", "zr_append_kv", "zr_summary_keys",
                                "zr_consensus", "zr_zoom_decode_attn",
                                "zr_workspace_bytes", "zr_status_string"])
@@ -174,6 +175,32 @@ def test_cached_errors(L):
     assert c(q=FAKE + 2) == zr.ZR_E_ALIGN
     assert c(workspace=None) == zr.ZR_E_WORKSPACE
     assert c(scale=float("inf")) == zr.ZR_E_SHAPE
+
+
+def test_partials_and_combine_errors(L):
+    g = _geom()
+    pt = lambda **kw: zr.zr_sparse_decode_attn_partials(**dict(dict(
+        geom=g, q=FAKE, k_pool=FAKE, v_pool=FAKE, block_table=FAKE, seq_lens=FAKE, window=16,
+        scale=0.1, max_attended=100, workspace=FAKE, ws_bytes=1 << 20), **kw))
+    assert pt(window=-1) == zr.ZR_E_SHAPE
+    assert pt(q=None) == zr.ZR_E_NULL
+    assert pt(v_pool=FAKE + 4) == zr.ZR_E_ALIGN
+    assert pt(workspace=None) == zr.ZR_E_WORKSPACE
+    assert pt(ws_bytes=16) == zr.ZR_E_WORKSPACE
+    assert pt(max_attended=-1) == zr.ZR_E_SHAPE
+    assert pt(geom=_geom(head_dim=96)) == zr.ZR_E_UNSUPPORTED
+    cb = lambda **kw: zr.zr_attn_combine(**dict(dict(
+        geom=g, max_attended=100, out=FAKE, workspace=FAKE, ws_bytes=1 << 20), **kw))
+    assert cb(out=None) == zr.ZR_E_NULL
+    assert cb(out=FAKE + 4) == zr.ZR_E_ALIGN
+    assert cb(max_attended=-1) == zr.ZR_E_SHAPE
+    assert cb(workspace=None) == zr.ZR_E_WORKSPACE
+    assert cb(workspace=FAKE + 8) == zr.ZR_E_WORKSPACE
+    # the layout grows with max_attended: a workspace sized for a small bound is too small
+    small = zr.zr_workspace_bytes(g, 16)
+    assert cb(max_attended=1 << 20, ws_bytes=small) == zr.ZR_E_WORKSPACE
+    assert cb(geom=_geom(n_q_heads=12)) == zr.ZR_E_UNSUPPORTED
+    assert cb(geom=_geom(batch=0), workspace=None) == zr.ZR_OK  # nothing to do
 
 
 def test_append_and_summary_errors(L):

@@ -301,6 +301,40 @@ def test_cached_selection_between_boundaries():
         assert torch.equal(st2.out, got), i
 
 
+@pytest.mark.parametrize("cfg", [0, 1, 3])
+def test_partials_then_combine_equal_the_cached_call(cfg):
+    """zr_sparse_decode_attn_partials then zr_attn_combine give bit for bit the
+    output of zr_sparse_decode_attn_cached (also with a grown window), and
+    zr_attn_combine after an attention call reproduces that call's output from
+    the partials it left, into any output buffer."""
+    w = synth.make_workload(cfg, device="cuda")
+    st = zr.step_from_workload(w)
+    st.step()
+    for win in (w.window, w.window + 3):
+        st.cached_attn(win)
+        torch.cuda.synchronize()
+        ref = st.out.clone()
+        st.out.fill_(float("nan"))
+        st.cached_partials(win)
+        st.combine()
+        torch.cuda.synchronize()
+        say(f"[gpu] cfg{cfg} window {win}: partials + combine vs cached call, "
+            f"max diff {torch.max(torch.abs(st.out - ref)).item():.3e}")
+        assert torch.equal(st.out, ref), (cfg, win)
+        other = torch.full_like(st.out, float("nan"))
+        st.combine(out=other)
+        torch.cuda.synchronize()
+        assert torch.equal(other, ref), (cfg, win)
+    # combine after a full call: the partials that call left
+    st.step()
+    torch.cuda.synchronize()
+    ref = st.out.clone()
+    other = torch.full_like(st.out, float("nan"))
+    st.combine(out=other)
+    torch.cuda.synchronize()
+    assert torch.equal(other, ref), cfg
+
+
 def test_pools_in_pinned_host_memory():
     """The K/V pools kept in pinned host memory (ZoomR Sec. 3.4: the full
     cache lives in CPU memory and each step moves the selected part to the
