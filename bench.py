@@ -34,8 +34,8 @@ HBM_PEAK_GBS = 8000.0
 # soon as any of these files changes.
 TRAFFIC_SOURCES = ("zr_internal.h", "zr_pair.hip", "zr_attn.hip")
 TRAFFIC = {
-    "sources_sha256": "5c69bc10b21ef1707e8bccb4755499b53c8c9c61b6ee61c65d259e2e3d59f7b8",
-    "bytes_per_call": 79653384,  # 78,565,486 fetched + 1,087,898 written
+    "sources_sha256": "e717f78e1cf8e5144f47d381b15680c196e43b0d0b2995110b4029369291e31b",
+    "bytes_per_call": 79654253,  # 78,566,353 fetched + 1,087,901 written
 }
 
 

@@ -1161,7 +1161,13 @@ attn_combine_kernel(AttnArgs a) {
   __shared__ MergeState sh[NGRP > 1 ? (NGRP - 1) * ITEMS : 1];
   const int g = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
   const int p = b * a.Hkv + g;
-  const int s0 = a.ws_pref[p], s1 = a.ws_pref[p + 1];
+  // slot range of the pair, kept inside this layout's nwg + P slots (a range
+  // written under another layout then reads wrong values, but no memory
+  // outside the workspace)
+  const int cap = a.nwg + a.B * a.Hkv;
+  const int r0 = a.ws_pref[p], r1 = a.ws_pref[p + 1];
+  const int s0 = r0 < 0 ? 0 : (r0 > cap ? cap : r0);
+  const int s1 = r1 < s0 ? s0 : (r1 > cap ? cap : r1);
   float4* out4 = reinterpret_cast<float4*>(a.out + (static_cast<size_t>(b) * a.Hq + g * G) * D);
   auto finish = [&](int idx, const MergeState& st) {
     const float inv = st.L > 0.f ? 1.f / st.L : 0.f;
