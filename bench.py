@@ -34,8 +34,8 @@ HBM_PEAK_GBS = 8000.0
 # soon as any of these files changes.
 TRAFFIC_SOURCES = ("zr_internal.h", "zr_pair.hip", "zr_attn.hip")
 TRAFFIC = {
-    "sources_sha256": "e717f78e1cf8e5144f47d381b15680c196e43b0d0b2995110b4029369291e31b",
-    "bytes_per_call": 79654253,  # 78,566,353 fetched + 1,087,901 written
+    "sources_sha256": "4fb7dd39039347ca2f18d8ab13a52bbd4547f15cbc1bf5731c8f85414aa7c275",
+    "bytes_per_call": 79654215,  # 78,566,313 fetched + 1,087,902 written
 }
 
 

@@ -213,9 +213,10 @@ struct AttnArgs {
   float* ws_l;               // [nwg + P][G]
   float* ws_acc;             // [nwg + P][G][D]
   float* out;                // [B][Hq][D]
-  int32_t B, Hq, Hkv, max_blocks, num_blocks;
-  int32_t window;            // sparse: window tokens appended after the cached entries
+  int32_t B, Hq, Hkv;
   int32_t nwg;               // workgroups of the grid (at most nwg + P partial slots)
+  int32_t max_blocks, num_blocks;
+  int32_t window;            // sparse: window tokens appended after the cached entries
   float scale_log2;          // scale * log2(e)
 };
 
