@@ -236,8 +236,10 @@ zr_status zr_sparse_decode_attn_cached(const zr_geom* geom, const void* q, const
  * `workspace` left (this one, or any attention call, which combines them
  * itself as well) into out[b][h] ([batch][n_q_heads][head_dim] float32,
  * 16-byte aligned). It must get the geom and max_attended of that call, which
- * fix the workspace layout (with others the output is wrong, but nothing
- * outside the workspace is read); the workspace is only read.
+ * fix the workspace layout (zr_dense_paged_decode_attn lays it out for
+ * max_attended = 16 * max_blocks_per_seq; with other values the output is
+ * wrong, but nothing outside the workspace is read); the workspace is only
+ * read.
  * partials followed by combine give bit for bit the output of
  * zr_sparse_decode_attn_cached with the same arguments. Workspace ownership
  * and concurrency as zr_sparse_decode_attn.
