@@ -176,6 +176,8 @@ struct PairArgs {
   int32_t n_total, max_per_seq, Hq, Hkv, k, window, max_blocks, num_blocks;
   int32_t bt_per;             // block-table entries per thread (set by the launcher)
   int32_t G;                  // query heads per KV head (set by the launcher)
+  float spec_avg;             // > 0: summary-key rows loaded ahead of the thought range,
+  int32_t spec_margin;        //   from b * spec_avg - spec_margin (set by the launcher)
   int32_t stage_th;           // 1: thought spans staged in LDS
   // multi-granularity plan (zoom): votes, consensus set, summary spans, prompt
   const int32_t* votes;       // [n_total]

@@ -43,6 +43,13 @@ constexpr int kRankMax = kPairThreads;  // up to this many thoughts: ranking by 
 constexpr int kBtRegs = 16;             // block-table entries prefetched per thread
 constexpr int kSelRegs = (ZR_MAX_K + kPairThreads - 1) / kPairThreads;  // given sel per thread
 constexpr int kMaxGroup = 16;           // query heads per KV head
+constexpr int kScoreR = 4;              // summary-key rows in flight per lane
+
+// Summary-key rows one scoring batch covers (all lanes, kScoreR rows each).
+template <typename E, int D>
+constexpr int score_batch_rows() {
+  return kPairThreads / (D / (16 / E::kBytes)) * kScoreR;
+}
 
 // Larger key = better score. NaN maps below every number; -0 maps like +0.
 __device__ __forceinline__ uint32_t order_key(float f) {
@@ -422,13 +429,17 @@ __device__ void emit_list(const PairArgs& a, const PairLds& L, int p, int b, int
 // ---------------------------------------------------------------------------
 // STH: the thought spans are staged in LDS (a template flag, so that the
 // span reads stay LDS reads and never wait on outstanding global stores).
-template <typename E, int D, bool SCORE, bool SELECT, bool PLAN, bool STH>
+// SPEC: the first batch of summary-key rows is loaded before the thought
+// range arrives (a template flag, so that kernels without it keep the plain
+// load order and registers).
+template <typename E, int D, bool SCORE, bool SELECT, bool PLAN, bool STH, bool SPEC>
 __global__ void __launch_bounds__(kPairThreads)
 pair_kernel(PairArgs a) {
   constexpr int VPL = 16 / E::kBytes;  // elements per 16-byte load
   constexpr int LPT = D / VPL;         // lanes per thought row
   constexpr int TPP = kPairThreads / LPT;
-  constexpr int R = 4;                 // rows in flight per lane
+  constexpr int R = kScoreR;           // rows in flight per lane
+  constexpr int NSPEC = TPP * R;       // rows of the speculative batch
   extern __shared__ __align__(16) int32_t dyn[];
   __shared__ int wtmp[kPairWaves];
   __shared__ uint32_t hist[kPairThreads];
@@ -454,6 +465,25 @@ pair_kernel(PairArgs a) {
 #pragma unroll
     for (int h = 0; h < kMaxGroup; ++h)
       if (h < G) qv[h] = *reinterpret_cast<const uint4*>(qg + h * D + c * VPL);
+  }
+  // Summary-key rows before the thought range arrives (when the launcher
+  // enables it): sequences hold about spec_avg thoughts each, so the NSPEC
+  // rows from b * spec_avg - spec_margin usually contain [lo, hi); if not,
+  // the rows are loaded again once the range is known.
+  const St* kb = static_cast<const St*>(a.kbar);
+  constexpr bool spec = SCORE && SPEC;
+  int g0 = 0;
+  uint4 us[R];
+  if (spec) {
+    g0 = static_cast<int>(static_cast<float>(b) * a.spec_avg) - a.spec_margin;
+    g0 = g0 < 0 ? 0 : g0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      int j = g0 + r0 + r * TPP;
+      j = j < a.n_total ? j : a.n_total - 1;  // a valid row; the result is dropped
+      us[r] = *reinterpret_cast<const uint4*>(kb + (static_cast<size_t>(j) * a.Hkv + g) * D +
+                                              c * VPL);
+    }
   }
   int btr[kBtRegs];
   const bool bt_pref = a.bt_per <= kBtRegs;
@@ -484,7 +514,7 @@ pair_kernel(PairArgs a) {
     ths0 = a.th_start[lo + t];
     thl0 = a.th_len[lo + t];
   }
-  const St* kb = static_cast<const St*>(a.kbar);
+  const bool hit = spec && lo >= g0 && lo + n <= g0 + NSPEC;  // uniform (false unless SPEC)
   uint4 u[R];
   auto load_rows = [&](int i0) {
 #pragma unroll
@@ -495,7 +525,7 @@ pair_kernel(PairArgs a) {
                                              c * VPL);
     }
   };
-  if (SCORE && n > 0) load_rows(0);
+  if (SCORE && n > 0 && !hit) load_rows(0);
 
   int tw = 0, nb = 0;
   if (PLAN) {
@@ -537,11 +567,9 @@ pair_kernel(PairArgs a) {
         for (int v = 0; v < VPL; ++v) qs[v] += static_cast<double>(x[v]);
       }
     }
-    for (int i0 = 0; i0 < n; i0 += TPP * R) {
-      uint4 cur[R];
-#pragma unroll
-      for (int r = 0; r < R; ++r) cur[r] = u[r];
-      if (i0 + TPP * R < n) load_rows(i0 + TPP * R);  // next batch in flight
+    // the rows of one batch: lane row r is thought i0 + r0 + r TPP of the
+    // sequence (negative or >= n: not the sequence's, dropped)
+    auto score_rows = [&](const uint4 (&cur)[R], int i0) {
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         float x[VPL];
@@ -551,11 +579,22 @@ pair_kernel(PairArgs a) {
         for (int v = 0; v < VPL; ++v) acc = fma(qs[v], static_cast<double>(x[v]), acc);
         acc = group_sum_f64<LPT>(acc);
         const int i = i0 + r0 + r * TPP;
-        if (c == 0 && i < n) {
+        if (c == 0 && i >= 0 && i < n) {
           const float f = static_cast<float>(acc);
           a.scores[static_cast<size_t>(lo + i) * a.Hkv + g] = f;
           if (SELECT) L.keys[i] = order_key(f);
         }
+      }
+    };
+    if (hit) {
+      score_rows(us, g0 - lo);
+    } else {
+      for (int i0 = 0; i0 < n; i0 += TPP * R) {
+        uint4 cur[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) cur[r] = u[r];
+        if (i0 + TPP * R < n) load_rows(i0 + TPP * R);  // next batch in flight
+        score_rows(cur, i0);
       }
     }
   } else if (SELECT) {
@@ -785,13 +824,35 @@ static hipError_t launch_pair_t(const zr_geom& gm, PairArgs a, hipStream_t s) {
   const size_t lds = pair_dyn_lds(a, SELECT, PLAN);
   if (kPairStaticLds + lds > kPairLdsLimit) return hipErrorInvalidValue;
   a.G = gm.n_q_heads / gm.n_kv_heads;
+  a.spec_avg = 0.f;
+  a.spec_margin = 0;
+  if (SCORE && a.n_total > 0 && gm.batch > 0) {
+    // only for even batches (the caller's bound on thoughts per sequence
+    // within 1.25x of the mean), where the guess lands, and when one batch of
+    // rows holds a whole sequence; elsewhere the extra rows would only delay
+    // the loads that follow them
+    constexpr int rows = score_batch_rows<E, D>();
+    const float avg = static_cast<float>(a.n_total) / static_cast<float>(gm.batch);
+    if (a.max_per_seq <= rows && static_cast<float>(a.max_per_seq) <= 1.25f * avg) {
+      a.spec_avg = avg;
+      a.spec_margin = static_cast<int>((static_cast<float>(rows) - avg) * 0.5f);
+    }
+  }
   const dim3 grid(gm.n_kv_heads, gm.batch);
-  if (a.stage_th)
-    hipLaunchKernelGGL((pair_kernel<E, D, SCORE, SELECT, PLAN, true>), grid, dim3(kPairThreads),
-                       lds, s, a);
+  const dim3 block(kPairThreads);
+  const bool spec = SCORE && a.spec_avg > 0.f;
+  if (a.stage_th && spec)
+    hipLaunchKernelGGL((pair_kernel<E, D, SCORE, SELECT, PLAN, true, SCORE>), grid, block, lds, s,
+                       a);
+  else if (a.stage_th)
+    hipLaunchKernelGGL((pair_kernel<E, D, SCORE, SELECT, PLAN, true, false>), grid, block, lds, s,
+                       a);
+  else if (spec)
+    hipLaunchKernelGGL((pair_kernel<E, D, SCORE, SELECT, PLAN, false, SCORE>), grid, block, lds,
+                       s, a);
   else
-    hipLaunchKernelGGL((pair_kernel<E, D, SCORE, SELECT, PLAN, false>), grid, dim3(kPairThreads),
-                       lds, s, a);
+    hipLaunchKernelGGL((pair_kernel<E, D, SCORE, SELECT, PLAN, false, false>), grid, block, lds,
+                       s, a);
   return hipGetLastError();
 }
 
