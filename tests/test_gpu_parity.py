@@ -301,6 +301,30 @@ def test_cached_selection_between_boundaries():
         assert torch.equal(st2.out, got), i
 
 
+def test_summary_rows_loaded_ahead_hit_and_miss():
+    """An even batch of 16 sequences (13K-16K tokens): the launcher loads the
+    summary-key rows ahead of the thought ranges, at positions guessed from
+    b * n_total / B. The rule is evaluated here on the host to make sure that
+    some sequences' ranges fall inside the guessed rows and some do not, so both
+    the rows loaded ahead and the fallback load are checked against the oracle
+    in one launch."""
+    w = synth.make_workload(1, seed=4, device="cuda",
+                            overrides=dict(B=16, seq_len=("uniform", 13000, 16384)))
+    sp = np.asarray(w.seq_ptr)
+    rows = 64  # bf16, head_dim 128: 16 rows per pass x 4 in flight
+    avg = np.float32(sp[-1]) / np.float32(w.B)
+    assert w.max_per_seq <= rows and np.float32(w.max_per_seq) <= np.float32(1.25) * avg
+    margin = int((np.float32(rows) - avg) * np.float32(0.5))
+    hits = 0
+    for b in range(w.B):
+        g0 = max(0, int(np.float32(b) * avg) - margin)
+        n = min(int(sp[b + 1] - sp[b]), w.max_per_seq)
+        hits += int(sp[b] >= g0 and sp[b] + n <= g0 + rows)
+    say(f"[gpu] rows loaded ahead: {hits} of {w.B} sequences inside the guessed rows")
+    assert 0 < hits < w.B
+    run_and_check(w, "even-b16")
+
+
 @pytest.mark.parametrize("cfg", [0, 1, 3])
 def test_partials_then_combine_equal_the_cached_call(cfg):
     """zr_sparse_decode_attn_partials then zr_attn_combine give bit for bit the
