@@ -418,6 +418,27 @@ def test_range_meeting_more_than_64_pairs(n_short):
     run_and_check(w, f"ranges-over-64-pairs-{8 * len(lens)}", check_dense=True)
 
 
+@pytest.mark.parametrize("seed", [5, 9, 12, 37])
+def test_random_even_batches(seed):
+    """Seeded random even batches (lengths within 8 % of each other), where
+    the summary-key rows are loaded ahead of the thought ranges for bf16 and
+    fp32, head_dim 128: seeds 5 and 12 have every sequence inside the guessed
+    rows, seeds 9 and 37 only some."""
+    rng = np.random.default_rng(5000 + seed)
+    dtype = ["bf16", "f32"][seed % 2]
+    d = [128, 64][(seed // 2) % 2]
+    Hkv = [1, 2, 8][seed % 3]
+    G = [1, 2, 4, 8][rng.integers(0, 4)]
+    B = int(rng.integers(1, 25))
+    L = int(rng.integers(800, 9000))
+    lens = (L * (1 + 0.08 * (rng.random(B) * 2 - 1))).astype(int)
+    th = ("uniform", int(rng.integers(40, 120)), int(rng.integers(150, 400)))
+    w = synth.make_workload(1, seed=seed, device="cuda", seq_lens=lens.tolist(), overrides=dict(
+        B=B, dtype=dtype, d=d, Hq=Hkv * G, Hkv=Hkv, thought=th, k=int(rng.integers(0, 12)),
+        window=int(rng.integers(0, 300))))
+    run_and_check(w, f"even-{seed}")
+
+
 @pytest.mark.parametrize("seed", range(8))
 def test_random_shapes(seed):
     """Seeded random batches: 1-48 sequences of 0-6000 tokens, 1/2/8 KV heads,
