@@ -652,10 +652,14 @@ pair_kernel(PairArgs a) {
 // ---------------------------------------------------------------------------
 // Consensus (ZoomR Sec. 3.3, "Global Aggregation and Consensus"): one
 // workgroup per sequence. Votes v_i = the number of (layer, KV head) top-k
-// rows holding thought i (LDS atomics; rows hold distinct indices, as the
-// selector writes them); the consensus set is the c thoughts with the most
-// votes among those with any, ties to the lower index, in ascending index;
-// agreement = votes of the consensus set over all votes (ZoomR Sec. 4).
+// rows holding thought i, a row counting once however often it lists i (v_i
+// is a sum of set-membership indicators). One thread per row walks its
+// entries: an index above every earlier index of the row is new (rows written
+// by the selector ascend, so they never look back); any other index is
+// compared with the earlier entries. Votes are LDS atomics. The consensus set
+// is the c thoughts with the most votes among those with any, ties to the
+// lower index, in ascending index; agreement = votes of the consensus set
+// over all votes (ZoomR Sec. 4).
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(kPairThreads)
 consensus_kernel(ConsArgs a) {
@@ -675,11 +679,32 @@ consensus_kernel(ConsArgs a) {
   for (int i = t; i < keys_fill(n); i += kPairThreads) L.keys[i] = 0u;
   __syncthreads();
   const int rows = a.n_layers * a.Hkv;
-  for (int e = t; e < rows * a.k; e += kPairThreads) {
-    const int r = e / a.k, j = e - r * a.k;
+  constexpr int kRowBatch = 8;  // row entries loaded at once
+  for (int r = t; r < rows; r += kPairThreads) {
     const int l = r / a.Hkv, g = r - l * a.Hkv;
-    const int i = a.sel[((static_cast<size_t>(l) * a.B + b) * a.Hkv + g) * a.k + j];
-    if (i >= 0 && i < n) atomicAdd(&L.keys[i], 1u);
+    const int32_t* row = a.sel + ((static_cast<size_t>(l) * a.B + b) * a.Hkv + g) * a.k;
+    int top = -1;  // largest valid index met so far in the row
+    for (int j0 = 0; j0 < a.k; j0 += kRowBatch) {
+      int v[kRowBatch];
+#pragma unroll
+      for (int u = 0; u < kRowBatch; ++u) v[u] = j0 + u < a.k ? row[j0 + u] : -1;
+#pragma unroll
+      for (int u = 0; u < kRowBatch; ++u) {
+        const int i = v[u];
+        if (i < 0 || i >= n) continue;
+        bool fresh = i > top;
+        if (!fresh) {  // not above every earlier index: look for it among them
+          fresh = true;
+          for (int jj = 0; jj < j0 + u; ++jj)
+            if (row[jj] == i) {
+              fresh = false;
+              break;
+            }
+        }
+        if (fresh) atomicAdd(&L.keys[i], 1u);
+        top = i > top ? i : top;
+      }
+    }
   }
   __syncthreads();
   int mine = 0;
@@ -812,6 +837,32 @@ bool pair_lds_ok(const zr_geom& gm, int max_per_seq, int k, bool select, bool pl
          kPairLdsLimit;
 }
 
+// Whether the scorer loads its first batch of summary-key rows before the
+// thought range arrives, and where: only for even batches (the caller's bound
+// on thoughts per sequence within 1.25x of the mean), where the guess lands,
+// and when one batch of rows holds a whole sequence; elsewhere the extra rows
+// would only delay the loads that follow them. Sequence b's guess starts at
+// max(0, (int)(b * per_seq) - margin), float32 product, and covers `rows`
+// rows. per_seq = 0 (and rows = margin = 0) when the rule is off.
+void summary_prefetch_rule(const zr_geom& gm, int n_total, int max_per_seq, int* rows,
+                           float* per_seq, int* margin) {
+  *rows = 0;
+  *per_seq = 0.f;
+  *margin = 0;
+  if (n_total <= 0 || gm.batch <= 0) return;
+  int r;
+  if (gm.dtype == ZR_BF16)
+    r = gm.head_dim == 128 ? score_batch_rows<BF16, 128>() : score_batch_rows<BF16, 64>();
+  else
+    r = gm.head_dim == 128 ? score_batch_rows<F32, 128>() : score_batch_rows<F32, 64>();
+  const float avg = static_cast<float>(n_total) / static_cast<float>(gm.batch);
+  if (max_per_seq <= r && static_cast<float>(max_per_seq) <= 1.25f * avg) {
+    *rows = r;
+    *per_seq = avg;
+    *margin = static_cast<int>((static_cast<float>(r) - avg) * 0.5f);
+  }
+}
+
 template <typename E, int D, bool SCORE, bool SELECT, bool PLAN>
 static hipError_t launch_pair_t(const zr_geom& gm, PairArgs a, hipStream_t s) {
   a.bt_per = pair_bt_per(gm.max_blocks_per_seq);
@@ -826,17 +877,9 @@ static hipError_t launch_pair_t(const zr_geom& gm, PairArgs a, hipStream_t s) {
   a.G = gm.n_q_heads / gm.n_kv_heads;
   a.spec_avg = 0.f;
   a.spec_margin = 0;
-  if (SCORE && a.n_total > 0 && gm.batch > 0) {
-    // only for even batches (the caller's bound on thoughts per sequence
-    // within 1.25x of the mean), where the guess lands, and when one batch of
-    // rows holds a whole sequence; elsewhere the extra rows would only delay
-    // the loads that follow them
-    constexpr int rows = score_batch_rows<E, D>();
-    const float avg = static_cast<float>(a.n_total) / static_cast<float>(gm.batch);
-    if (a.max_per_seq <= rows && static_cast<float>(a.max_per_seq) <= 1.25f * avg) {
-      a.spec_avg = avg;
-      a.spec_margin = static_cast<int>((static_cast<float>(rows) - avg) * 0.5f);
-    }
+  if (SCORE) {
+    int rows = 0;
+    summary_prefetch_rule(gm, a.n_total, a.max_per_seq, &rows, &a.spec_avg, &a.spec_margin);
   }
   const dim3 grid(gm.n_kv_heads, gm.batch);
   const dim3 block(kPairThreads);

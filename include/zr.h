@@ -335,16 +335,18 @@ zr_status zr_summary_keys(const zr_geom* geom, const void* k_pool, const int32_t
 /*
  * Votes and consensus (ZoomR, Sec. 3.3, eqs. for I_all and v_i; Sec. 4, the
  * agreeability metric AG). sel holds n_layers stacked selections, [n_layers]
- * [batch][n_kv_heads][k] as zr_select_topk writes them (local thought
- * indices, distinct within a row, -1 = none). For every sequence b:
- *   votes[i] = number of (layer, KV head) rows holding thought i  ([n_total]);
+ * [batch][n_kv_heads][k], each row a set of local thought indices (-1 =
+ * none; any order, as zr_select_topk writes them or otherwise). For every
+ * sequence b:
+ *   votes[i] = number of (layer, KV head) rows holding thought i, a row
+ *              counting once however often it lists i  ([n_total]);
  *   cons[b][0..) = the min(c, |I_all|) thoughts with the most votes among those
  *                  with at least one, ties to the lower index, ascending, -1
  *                  padded to c  ([batch][c]);
  *   agree[b] = sum of the consensus thoughts' votes / sum of all votes (0 if
  *              there are none)  ([batch] float32).
- * Indices outside [0, N_b) in sel are ignored; a repeated index within one
- * row is counted each time it appears. n_layers = 0 or k = 0 gives no votes.
+ * Indices outside [0, N_b) in sel are ignored. n_layers = 0 or k = 0 gives
+ * no votes.
  * Errors: ZR_E_NULL, ZR_E_SHAPE (n_layers, k, c < 0; k, c > ZR_MAX_K),
  * ZR_E_UNSUPPORTED (max_per_seq too large for on-chip memory), ZR_E_LAUNCH.
  */
@@ -375,6 +377,22 @@ zr_status zr_zoom_decode_attn(const zr_geom* geom, const void* q, const void* k_
                               int32_t n_prompt, int32_t window, float scale,
                               int32_t max_attended, float* out, void* workspace,
                               size_t ws_bytes, void* stream);
+
+/*
+ * How the scorer of zr_coarse_score, zr_score_topk and zr_sparse_decode_step
+ * schedules its summary-key loads (introspection for tests and tuning; no
+ * passage of the pages defines it, the results never depend on it). On even
+ * batches it loads a batch of `rows` summary-key rows before sequence b's
+ * thought range [seq_ptr[b], seq_ptr[b+1]) is known, starting at row
+ *   max(0, (int)((float)b * per_seq) - margin)
+ * and uses them when they hold the whole range (else it loads the range's
+ * rows once it is known). Host pointers; *rows = *margin = 0 and
+ * *per_seq = 0 when the rule is off for this geometry and thought counts.
+ * Errors: ZR_E_NULL, ZR_E_SHAPE (n_total or max_per_seq < 0), and the
+ * geometry errors of the other calls.
+ */
+zr_status zr_summary_prefetch_rule(const zr_geom* geom, int32_t n_total, int32_t max_per_seq,
+                                   int32_t* rows, float* per_seq, int32_t* margin);
 
 /* Workspace bytes the attention calls need for a grid sized for
  * `max_attended` tokens per (sequence, KV head): per-(b, g) block lists

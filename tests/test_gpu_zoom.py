@@ -73,6 +73,44 @@ def test_consensus_parity(thought, summary, c):
     assert np.max(np.abs(agree.cpu().numpy() - a_ref)) <= 1e-6
 
 
+@pytest.mark.parametrize("k", [12, 70])
+def test_consensus_repeated_and_out_of_range_indices(k):
+    """Rows with repeated indices in any order, -1 holes and indices at or past
+    the sequence's thought count: a row gives each thought one vote however
+    often it lists it (ZoomR Sec. 3.3: v_i is a sum of set-membership
+    indicators), as the oracle counts; k = 70 crosses several batches of row
+    entries in the kernel."""
+    w = _zoom_workload()
+    st = zr.step_from_workload(w)
+    rng = np.random.default_rng(77 + k)
+    n_layers, c = 3, 3
+    sel = np.full((n_layers, w.B, w.Hkv, k), -1, np.int32)
+    for l in range(n_layers):
+        for b in range(w.B):
+            n = int(w.seq_ptr[b + 1] - w.seq_ptr[b])
+            for g in range(w.Hkv):
+                row = rng.integers(0, max(1, min(n, 9)), k)   # few distinct values: many repeats
+                kind = rng.random(k)
+                row[kind < 0.15] = -1
+                row[(kind >= 0.15) & (kind < 0.25)] = n + rng.integers(0, 5)
+                if (l + b + g) % 4 == 0:
+                    row = np.sort(row)                         # ascending with repeats
+                sel[l, b, g] = row
+    votes = torch.empty(max(w.n_total, 1), dtype=torch.int32, device="cuda")
+    cons = torch.empty((w.B, c), dtype=torch.int32, device="cuda")
+    agree = torch.empty(w.B, dtype=torch.float32, device="cuda")
+    st.consensus(_dev(sel), c, votes, cons, agree)
+    torch.cuda.synchronize()
+    v_ref, c_ref, a_ref = O.consensus(sel, w.seq_ptr, c)
+    got = votes.cpu().numpy()[:w.n_total]
+    say(f"[gpu] consensus with repeats, k={k}: max votes {int(v_ref.max())} "
+        f"(rows {n_layers * w.Hkv}), entries listed {int((sel >= 0).sum())}")
+    assert int(v_ref.max()) <= n_layers * w.Hkv
+    assert np.array_equal(got, v_ref)
+    assert np.array_equal(cons.cpu().numpy(), c_ref)
+    assert np.max(np.abs(agree.cpu().numpy() - a_ref)) <= 1e-6
+
+
 def test_zoom_attention_parity_and_cached_steps():
     w = _zoom_workload()
     T0 = (w.seq_lens - 5).astype(np.int32)
