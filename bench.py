@@ -48,33 +48,92 @@ def sources_sha256():
 METRIC = "decode steps/s and effective KV GB/s (% of HBM peak), 16K tokens, batch 8"
 
 
+def attended_counts(sel, seq_lens, seq_ptr, th_start, th_len, window):
+    """Tokens the sparse attention gathers per (sequence, KV head), counted on
+    the host from a selection read back from the GPU, for byte accounting:
+    the window [T - W, T) plus each selected thought's span clipped below
+    T - W (spans do not overlap; a repeated index counts once). int64 [B][Hkv]."""
+    sel = np.asarray(sel)
+    B, Hkv = sel.shape[0], sel.shape[1]
+    n = np.zeros((B, Hkv), dtype=np.int64)
+    for b in range(B):
+        T = int(seq_lens[b])
+        tw = max(0, T - int(window))
+        lo, hi = int(seq_ptr[b]), int(seq_ptr[b + 1])
+        st = np.asarray(th_start[lo:hi], np.int64)
+        en = st + np.asarray(th_len[lo:hi], np.int64)
+        for g in range(Hkv):
+            idx = np.unique(sel[b, g][(sel[b, g] >= 0) & (sel[b, g] < hi - lo)])
+            clipped = np.minimum(en[idx], tw) - np.maximum(st[idx], 0)
+            n[b, g] = (T - tw) + int(np.maximum(0, clipped).sum())
+    return n
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(w, budget_s):
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, budget_s, max_threads=16):
     """The CPU oracle, as it stands, on layer 0 of the same workload: whole
-    decode steps (scores, top-k, attention for all 64 (b, g) pairs), repeated
-    until ``budget_s`` seconds of CPU work, one thread."""
+    decode steps (scores, top-k, attention for every (sequence, KV head)
+    pair), repeated for about ``budget_s`` seconds in two legs of equal
+    budget: one thread, then one Python thread per usable host core (at most
+    ``max_threads``, the CPU share of one GPU on the box), each running the
+    oracle on a contiguous run of the pairs (numpy releases the interpreter
+    lock inside its array loops; each thread's BLAS is held to one thread)."""
+    from concurrent.futures import ThreadPoolExecutor
+
     from threadpoolctl import threadpool_limits
 
     from hierarchical_sparse_kv_amd import synth
     from oracle import zr_oracle as O
     f = synth.to_numpy_f32
     q, kp, vp, kb = f(w.q), f(w.k_pool), f(w.v_pool), f(w.summary_keys)
-    n = 0
-    t0 = time.perf_counter()
+    pairs = [(b, g) for b in range(w.B) for g in range(w.Hkv)]
+
+    def run(chunk):
+        O.sparse_decode_step(q, kp, vp, w.block_table, w.seq_lens, w.seq_ptr, w.th_start,
+                             w.th_len, kb, w.k, w.window, w.scale, pairs=chunk)
+
+    def leg(n_threads, budget):
+        chunks = [pairs[i * len(pairs) // n_threads:(i + 1) * len(pairs) // n_threads]
+                  for i in range(n_threads)]
+        n = 0
+        with ThreadPoolExecutor(n_threads) as ex:
+            t0 = time.perf_counter()
+            while True:
+                if n_threads == 1:
+                    run(pairs)
+                else:
+                    list(ex.map(run, chunks))
+                n += 1
+                el = time.perf_counter() - t0
+                if el >= budget:
+                    return n, el
+
+    usable = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    n_thr = max(1, min(max_threads, usable or 1, len(pairs)))
     with threadpool_limits(limits=1):
-        while True:
-            O.sparse_decode_step(q, kp, vp, w.block_table, w.seq_lens, w.seq_ptr, w.th_start,
-                                 w.th_len, kb, w.k, w.window, w.scale)
-            n += 1
-            el = time.perf_counter() - t0
-            if el >= budget_s:
-                break
-    return {"value": n / el, "unit": "steps/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n} full oracle decode step(s) of layer 0 (all {w.B * w.Hkv} (sequence, "
-                      f"KV head) pairs, float64 numpy, 1 thread) in {el:.1f} s"}
+        n1, el1 = leg(1, budget_s / 2)
+        nn, eln = leg(n_thr, budget_s / 2)
+    return {"value": nn / eln, "unit": "steps/s", "cores": n_thr, "kind": "oracle",
+            "single_thread_steps_per_s": n1 / el1, "host_cores": os.cpu_count(),
+            "usable_cores": usable, "cpu_model": cpu_model(),
+            "sample": f"full oracle decode steps of layer 0 (all {len(pairs)} (sequence, KV head) "
+                      f"pairs, float64 numpy): {n1} step(s) on 1 thread in {el1:.1f} s, then "
+                      f"{nn} step(s) on {n_thr} threads (contiguous runs of pairs) in {eln:.1f} s"}
 
 
 def main():
@@ -83,7 +142,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--layers", type=int, default=32)
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-others", action="store_true",
                     help="skip the attention figures on the ragged and 64K-token workloads")
@@ -133,7 +192,7 @@ def main():
     for st in steps:
         st.step()
     torch.cuda.synchronize()
-    att = [zr.attended_counts(st.sel.cpu().numpy(), w.seq_lens, w.seq_ptr, w.th_start, w.th_len,
+    att = [attended_counts(st.sel.cpu().numpy(), w.seq_lens, w.seq_ptr, w.th_start, w.th_len,
                               w.window) for st, w in zip(steps, layers)]
     kv_bytes = [int(a.sum()) * 2 * d * s_bytes for a in att]
     dense_bytes = int(w0.seq_lens.sum()) * w0.Hkv * 2 * d * s_bytes
@@ -176,6 +235,34 @@ def main():
     us_per_step = timed(g_step, args.steps)
     ms_per_step = us_per_step / 1e3
     calls_us = timed(g_calls, args.steps)
+
+    # per-step latency (KV-cache management page, "Measuring a cache design":
+    # percentiles, not only the mean): one graph per layer holding one step,
+    # replayed n_lat times with layers rotating and an event recorded between
+    # consecutive replays. A sleep kernel holds the GPU while the host queues
+    # every replay, so the intervals are back-to-back step times on the GPU.
+    g_one = [capture(lambda i, l=l: steps[l].step(), 1) for l in range(L)]
+    n_lat = max(args.steps, 200)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_lat + 1)]
+    torch.cuda.synchronize()
+    t_q = time.perf_counter()
+    torch.cuda._sleep(int(2.4e9 * 0.2))  # ~0.2 s of GPU cycles
+    evs[0].record()
+    for i in range(n_lat):
+        g_one[i % L].replay()
+        evs[i + 1].record()
+    queued_ms = (time.perf_counter() - t_q) * 1e3
+    torch.cuda.synchronize()
+    lat = np.array([evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(n_lat)])
+    latency = {"steps": n_lat, "mean_us": round(float(lat.mean()), 3),
+               "p50_us": round(float(np.percentile(lat, 50)), 3),
+               "p90_us": round(float(np.percentile(lat, 90)), 3),
+               "p99_us": round(float(np.percentile(lat, 99)), 3),
+               "max_us": round(float(lat.max()), 3),
+               "host_queue_ms": round(queued_ms, 1),
+               "note": "one graph replay per step, events between replays, GPU held by a "
+                       "sleep kernel while the host queued them"}
+    del g_one
 
     # the whole sparse attention call (block lists, attention, combine)
     attn_us = timed(g_attn, args.steps)
@@ -334,7 +421,7 @@ def main():
             for w, st in zip(ws_, ss_):
                 st.step()
                 torch.cuda.synchronize()
-                a_ = zr.attended_counts(st.sel.cpu().numpy(), w.seq_lens, w.seq_ptr, w.th_start,
+                a_ = attended_counts(st.sel.cpu().numpy(), w.seq_lens, w.seq_ptr, w.th_start,
                                         w.th_len, w.window)
                 byts.append(int(a_.sum()) * 2 * w.d * synth.ELEM_BYTES[w.dtype])
             g_o = capture(lambda i: ss_[i % 4].cached_attn(ws_[i % 4].window), 40)
@@ -420,6 +507,7 @@ def main():
         "sparse_attn_call_gbs": round(bytes_per_launch / (attn_us * 1e-6) / 1e9, 1),
         "step_as_three_calls_us": round(calls_us, 3),
         "tokens_per_s": round(steps_per_s * w0.B, 1),
+        "latency": latency,
         "selection_reuse": {"period_steps": R, "us_per_step": round(period_us, 3),
                             "steps_per_s": round(1e6 / period_us, 1)},
         "speedup_vs_dense_attention": round(dense_us / attn_us, 3),

@@ -75,6 +75,7 @@ _SIGS = {
     "zr_dense_paged_decode_attn": (ctypes.c_int, [_G, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P,
                                                   ctypes.c_size_t, _P]),
     "zr_workspace_bytes": (ctypes.c_size_t, [_G, ctypes.c_int32]),
+    "zr_summary_prefetch_rule": (ctypes.c_int, [_G, ctypes.c_int32, ctypes.c_int32, _P, _P, _P]),
     "zr_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 
@@ -198,6 +199,17 @@ def zr_dense_paged_decode_attn(geom, q, k_pool, v_pool, block_table, seq_lens, s
 
 def zr_workspace_bytes(geom, max_attended) -> int:
     return int(lib().zr_workspace_bytes(ctypes.byref(geom), int(max_attended)))
+
+
+def zr_summary_prefetch_rule(geom, n_total, max_per_seq):
+    """(status, rows, per_seq, margin) of the scorer's summary-key prefetch
+    rule for this geometry and thought counts (host values)."""
+    rows, margin = ctypes.c_int32(), ctypes.c_int32()
+    per_seq = ctypes.c_float()
+    st = lib().zr_summary_prefetch_rule(ctypes.byref(geom), int(n_total), int(max_per_seq),
+                                        ctypes.addressof(rows), ctypes.addressof(per_seq),
+                                        ctypes.addressof(margin))
+    return st, rows.value, per_seq.value, margin.value
 
 
 # --------------------------------------------------------------------------
@@ -427,24 +439,3 @@ def step_from_workload(w, k=None, meta=None):
     return DeviceStep(w.q, w.k_pool, w.v_pool, bt, lens, ptr, ts, tl, w.summary_keys,
                       max(w.max_per_seq, 1), k, w.window, w.scale,
                       max_attended_bound(w.seq_lens, w.seq_ptr, w.th_len, k, w.window))
-
-
-def attended_counts(sel, seq_lens, seq_ptr, th_start, th_len, window):
-    """Tokens the sparse kernel gathers per (sequence, KV head), from a
-    selection read back to the host: the window [T - W, T) plus each selected
-    thought's span clipped below T - W (every token once; thoughts do not
-    overlap, repeated indices count once). Used for byte accounting; int64
-    [B][Hkv]."""
-    sel = np.asarray(sel)
-    B, Hkv = sel.shape[0], sel.shape[1]
-    n = np.zeros((B, Hkv), dtype=np.int64)
-    for b in range(B):
-        T = int(seq_lens[b])
-        tw = max(0, T - int(window))
-        lo, hi = int(seq_ptr[b]), int(seq_ptr[b + 1])
-        st = np.asarray(th_start[lo:hi], np.int64)
-        en = st + np.asarray(th_len[lo:hi], np.int64)
-        for g in range(Hkv):
-            idx = np.unique(sel[b, g][(sel[b, g] >= 0) & (sel[b, g] < hi - lo)])
-            n[b, g] = (T - tw) + int(np.maximum(0, np.minimum(en[idx], tw) - np.maximum(st[idx], 0)).sum())
-    return n
