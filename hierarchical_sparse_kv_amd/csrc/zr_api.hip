@@ -139,6 +139,22 @@ ZR_API size_t zr_workspace_bytes(const zr_geom* geom, int32_t max_attended) {
   return zr::attn_workspace(*geom, zr::attn_workgroups(*geom, max_attended), nullptr, nullptr);
 }
 
+ZR_API zr_status zr_summary_prefetch_rule(const zr_geom* geom, int32_t n_total,
+                                          int32_t max_per_seq, int32_t* rows, float* per_seq,
+                                          int32_t* margin) {
+  zr_status st = check_geom(geom);
+  if (st != ZR_OK) return st;
+  if (!rows || !per_seq || !margin) return ZR_E_NULL;
+  if (n_total < 0 || max_per_seq < 0) return ZR_E_SHAPE;
+  int r, m;
+  float a;
+  zr::summary_prefetch_rule(*geom, n_total, max_per_seq, &r, &a, &m);
+  *rows = r;
+  *per_seq = a;
+  *margin = m;
+  return ZR_OK;
+}
+
 ZR_API zr_status zr_coarse_score(const zr_geom* geom, const void* q, const zr_thoughts* th,
                                  float* scores, void* stream) {
   zr_status st = check_geom(geom);

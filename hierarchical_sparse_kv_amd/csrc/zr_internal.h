@@ -252,6 +252,10 @@ hipError_t launch_append(const zr_geom& g, const AppendArgs& a, hipStream_t s);
 hipError_t launch_summary_keys(const zr_geom& g, const SummaryArgs& a, int n_which,
                                hipStream_t s);
 hipError_t launch_pair(const zr_geom& g, const PairArgs& a, int mode, hipStream_t s);
+// The scorer's rule for loading summary-key rows ahead of the thought range
+// (rows = 0 when off); the launcher and zr_summary_prefetch_rule share it.
+void summary_prefetch_rule(const zr_geom& g, int n_total, int max_per_seq, int* rows,
+                           float* per_seq, int* margin);
 // Whether the pair kernel's LDS fits (with nothing optional staged).
 bool pair_lds_ok(const zr_geom& g, int max_per_seq, int k, bool select, bool plan);
 hipError_t launch_consensus(const ConsArgs& a, hipStream_t s);

@@ -8,7 +8,7 @@ import math
 import numpy as np
 import torch
 
-from hierarchical_sparse_kv_amd import synth
+from hierarchical_sparse_kv_amd import synth, zr
 from oracle import zr_oracle as O
 
 TOL = {"f32": 1e-5, "bf16": 2e-3}
@@ -135,3 +135,20 @@ def plant_near_ties(w, per_pair=(1, 2, 2), seed=0):
                         break
     w.summary_keys.copy_(torch.as_tensor(kbar).to(w.summary_keys.dtype))
     return counts
+
+
+def prefetch_hits(st, w):
+    """Number of sequences whose thought range lies inside the summary-key
+    rows the scorer loads ahead of it, under the rule the library reports
+    (zr_summary_prefetch_rule); 0 when the rule is off."""
+    status, rows, per, margin = zr.zr_summary_prefetch_rule(st.geom, w.n_total, w.max_per_seq)
+    assert status == zr.ZR_OK
+    if rows == 0:
+        return 0
+    sp = np.asarray(w.seq_ptr)
+    hits = 0
+    for b in range(w.B):
+        g0 = max(0, int(np.float32(b) * np.float32(per)) - margin)
+        n = min(int(sp[b + 1] - sp[b]), w.max_per_seq)
+        hits += int(sp[b] >= g0 and sp[b] + n <= g0 + rows)
+    return hits

@@ -28,6 +28,7 @@ def test_exports_every_declared_symbol(L):
                                "zr_sparse_decode_attn_partials", "zr_attn_combine",
                                "zr_dense_paged_decode_attn", "zr_append_kv", "zr_summary_keys",
                                "zr_consensus", "zr_zoom_decode_attn",
+                               "zr_summary_prefetch_rule",
                                "zr_workspace_bytes", "zr_status_string"])
     out = subprocess.run(["nm", "-D", "--defined-only", zr.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
@@ -245,3 +246,21 @@ def test_consensus_and_zoom_errors(L):
     assert zm(cons=None) == zr.ZR_E_NULL
     assert zm(out=FAKE + 4) == zr.ZR_E_ALIGN
     assert zm(ws_bytes=8) == zr.ZR_E_WORKSPACE
+
+
+def test_summary_prefetch_rule(L):
+    """The scorer's prefetch rule, read from the library (no GPU): on for even
+    batches whose sequences fit one batch of rows, off otherwise; argument
+    errors are reported."""
+    g = _geom(batch=8, n_q_heads=32, n_kv_heads=8, head_dim=128, dtype=zr.ZR_BF16)
+    st, rows, per, margin = zr.zr_summary_prefetch_rule(g, 456, 64)
+    assert st == zr.ZR_OK and rows == 64 and abs(per - 57.0) < 1e-6 and margin == 3
+    # uneven (max per sequence above 1.25x the mean) or too many per sequence: off
+    assert zr.zr_summary_prefetch_rule(g, 456, 80)[1:] == (0, 0.0, 0)
+    assert zr.zr_summary_prefetch_rule(g, 8 * 100, 100)[1:] == (0, 0.0, 0)
+    assert zr.zr_summary_prefetch_rule(g, 0, 0)[1:] == (0, 0.0, 0)
+    # fp32, head_dim 128: 32 rows per batch
+    g32 = _geom(batch=8, n_q_heads=32, n_kv_heads=8, head_dim=128, dtype=zr.ZR_F32)
+    assert zr.zr_summary_prefetch_rule(g32, 8 * 30, 32)[1] == 32
+    assert zr.zr_summary_prefetch_rule(g, -1, 0)[0] == zr.ZR_E_SHAPE
+    assert zr.zr_summary_prefetch_rule(_geom(head_dim=96), 10, 2)[0] == zr.ZR_E_UNSUPPORTED

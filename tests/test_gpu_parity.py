@@ -302,24 +302,16 @@ def test_cached_selection_between_boundaries():
 
 
 def test_summary_rows_loaded_ahead_hit_and_miss():
-    """An even batch of 16 sequences (13K-16K tokens): the launcher loads the
+    """An even batch of 16 sequences (13K-16K tokens): the scorer loads the
     summary-key rows ahead of the thought ranges, at positions guessed from
-    b * n_total / B. The rule is evaluated here on the host to make sure that
-    some sequences' ranges fall inside the guessed rows and some do not, so both
-    the rows loaded ahead and the fallback load are checked against the oracle
-    in one launch."""
+    b * n_total / B. The library's own rule (zr_summary_prefetch_rule) shows
+    that some sequences' ranges fall inside the guessed rows and some do not,
+    so both the rows loaded ahead and the fallback load are checked against
+    the oracle in one launch."""
     w = synth.make_workload(1, seed=4, device="cuda",
                             overrides=dict(B=16, seq_len=("uniform", 13000, 16384)))
-    sp = np.asarray(w.seq_ptr)
-    rows = 64  # bf16, head_dim 128: 16 rows per pass x 4 in flight
-    avg = np.float32(sp[-1]) / np.float32(w.B)
-    assert w.max_per_seq <= rows and np.float32(w.max_per_seq) <= np.float32(1.25) * avg
-    margin = int((np.float32(rows) - avg) * np.float32(0.5))
-    hits = 0
-    for b in range(w.B):
-        g0 = max(0, int(np.float32(b) * avg) - margin)
-        n = min(int(sp[b + 1] - sp[b]), w.max_per_seq)
-        hits += int(sp[b] >= g0 and sp[b] + n <= g0 + rows)
+    st = zr.step_from_workload(w)
+    hits = P.prefetch_hits(st, w)
     say(f"[gpu] rows loaded ahead: {hits} of {w.B} sequences inside the guessed rows")
     assert 0 < hits < w.B
     run_and_check(w, "even-b16")
@@ -436,6 +428,12 @@ def test_random_even_batches(seed):
     w = synth.make_workload(1, seed=seed, device="cuda", seq_lens=lens.tolist(), overrides=dict(
         B=B, dtype=dtype, d=d, Hq=Hkv * G, Hkv=Hkv, thought=th, k=int(rng.integers(0, 12)),
         window=int(rng.integers(0, 300))))
+    hits = P.prefetch_hits(zr.step_from_workload(w), w)
+    say(f"[gpu] even-{seed}: {hits} of {B} sequences inside the rows loaded ahead")
+    if seed in (5, 12):
+        assert hits == B
+    else:
+        assert 0 < hits < B
     run_and_check(w, f"even-{seed}")
 
 
