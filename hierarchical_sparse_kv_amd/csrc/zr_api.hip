@@ -2,6 +2,8 @@
 // stream. Nothing here allocates, frees or synchronizes.
 #include <math.h>
 
+#include <mutex>
+
 #include "zr_internal.h"
 
 #define ZR_API extern "C" __attribute__((visibility("default")))
@@ -129,6 +131,8 @@ ZR_API const char* zr_status_string(zr_status s) {
     case ZR_E_WORKSPACE: return "workspace missing, misaligned or smaller than zr_workspace_bytes()";
     case ZR_E_LAUNCH: return "the HIP runtime reported a launch error";
     case ZR_E_ALIGN: return "q, pools, out or summary keys are not 16-byte aligned";
+    case ZR_E_SCRATCH:
+      return "the call needs more than the built scratch memory (ZR_NOALLOC_SCRATCH_BYTES)";
   }
   return "unknown zr_status";
 }
@@ -481,4 +485,67 @@ ZR_API zr_status zr_dense_paged_decode_attn(const zr_geom* geom, const void* q,
   if (zr::launch_attention(*geom, a, true, static_cast<hipStream_t>(stream)) != hipSuccess)
     return ZR_E_LAUNCH;
   return ZR_OK;
+}
+
+// ---------------------------------------------------------------------------
+// The sparse decode step without a caller workspace: its kernels use a
+// file-scope device array instead. In host code `scratch` names a host-side
+// stand-in, not device memory, so its device address is taken once per
+// device (hipGetSymbolAddress, with that device current) and only that
+// address is handed to the kernels.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kScratchBytes = ZR_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's `scratch` (nullptr and *err set on failure).
+void* scratch_address(hipError_t* err) {
+  int dev = -1;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (*err != hipSuccess || !p) {
+      if (*err == hipSuccess) *err = hipErrorInvalidSymbol;
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+ZR_API zr_status zr_sparse_decode_step_noalloc(const zr_geom* geom, const void* q,
+                                               const void* k_pool, const void* v_pool,
+                                               const int32_t* block_table,
+                                               const int32_t* seq_lens, const zr_thoughts* th,
+                                               int32_t k, int32_t window, float scale,
+                                               int32_t max_attended, float* scores, int32_t* sel,
+                                               float* out, void* stream) {
+  zr_status st = check_geom(geom);
+  if (st != ZR_OK) return st;
+  if (max_attended < 0) return ZR_E_SHAPE;
+  if (static_cast<int64_t>(geom->batch) * geom->n_kv_heads > ZR_MAX_PAIRS)
+    return ZR_E_UNSUPPORTED;
+  const size_t need = zr::attn_workspace(*geom, zr::attn_workgroups(*geom, max_attended),
+                                         nullptr, nullptr);
+  if (need > kScratchBytes) return ZR_E_SCRATCH;
+  if (geom->batch == 0) return ZR_OK;
+  hipError_t err;
+  void* ws = scratch_address(&err);
+  if (!ws) return ZR_E_LAUNCH;
+  return zr_sparse_decode_step(geom, q, k_pool, v_pool, block_table, seq_lens, th, k, window,
+                               scale, max_attended, scores, sel, out, ws, kScratchBytes, stream);
 }

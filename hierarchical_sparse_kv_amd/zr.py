@@ -19,7 +19,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libzr.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "zr.h")
 
-ZR_OK, ZR_E_NULL, ZR_E_SHAPE, ZR_E_UNSUPPORTED, ZR_E_WORKSPACE, ZR_E_LAUNCH, ZR_E_ALIGN = range(7)
+(ZR_OK, ZR_E_NULL, ZR_E_SHAPE, ZR_E_UNSUPPORTED, ZR_E_WORKSPACE, ZR_E_LAUNCH, ZR_E_ALIGN,
+ ZR_E_SCRATCH) = range(8)
+ZR_NOALLOC_SCRATCH_BYTES = 16 << 20
 ZR_APPEND_OK, ZR_APPEND_NO_FREE_BLOCK, ZR_APPEND_TABLE_FULL, ZR_APPEND_BAD_BLOCK = range(4)
 ZR_F32, ZR_BF16 = 0, 1
 DTYPE_CODE = {torch.float32: ZR_F32, torch.bfloat16: ZR_BF16}
@@ -57,6 +59,9 @@ _SIGS = {
     "zr_sparse_decode_step": (ctypes.c_int, [_G, _P, _P, _P, _P, _P, _T, ctypes.c_int32,
                                              ctypes.c_int32, ctypes.c_float, ctypes.c_int32,
                                              _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "zr_sparse_decode_step_noalloc": (ctypes.c_int, [_G, _P, _P, _P, _P, _P, _T, ctypes.c_int32,
+                                                     ctypes.c_int32, ctypes.c_float,
+                                                     ctypes.c_int32, _P, _P, _P, _P]),
     "zr_sparse_decode_attn_cached": (ctypes.c_int, [_G, _P, _P, _P, _P, _P, ctypes.c_int32,
                                                     ctypes.c_float, ctypes.c_int32, _P, _P,
                                                     ctypes.c_size_t, _P]),
@@ -141,6 +146,14 @@ def zr_sparse_decode_step(geom, q, k_pool, v_pool, block_table, seq_lens, th, k,
                                        seq_lens, ctypes.byref(th), int(k), int(window),
                                        float(scale), int(max_attended), scores, sel, out,
                                        workspace, int(ws_bytes), stream)
+
+
+def zr_sparse_decode_step_noalloc(geom, q, k_pool, v_pool, block_table, seq_lens, th, k, window,
+                                  scale, max_attended, scores, sel, out, stream=None) -> int:
+    return lib().zr_sparse_decode_step_noalloc(ctypes.byref(geom), q, k_pool, v_pool,
+                                               block_table, seq_lens, ctypes.byref(th), int(k),
+                                               int(window), float(scale), int(max_attended),
+                                               scores, sel, out, stream)
 
 
 def zr_sparse_decode_attn_cached(geom, q, k_pool, v_pool, block_table, seq_lens, window, scale,
@@ -405,6 +418,17 @@ class DeviceStep:
             _ptr(self.block_table), _ptr(seq_lens), self.th, self.k, self.window,
             self.scale, self.max_attended, _ptr(scores), _ptr(sel) if self.k else None,
             _ptr(out), _ptr(self.workspace), self.workspace.numel(), _stream()))
+
+    def step_noalloc(self, scores=None, sel=None, out=None):
+        """The same step through zr_sparse_decode_step_noalloc (no workspace:
+        the library's built-in device scratch)."""
+        scores = self.scores if scores is None else scores
+        sel = self.sel if sel is None else sel
+        out = self.out if out is None else out
+        check("zr_sparse_decode_step_noalloc", zr_sparse_decode_step_noalloc(
+            self.geom, _ptr(self.q), self.kp, self.vp, _ptr(self.block_table),
+            _ptr(self.seq_lens), self.th, self.k, self.window, self.scale, self.max_attended,
+            _ptr(scores), _ptr(sel) if self.k else None, _ptr(out), _stream()))
 
     def step_calls(self):
         """The same step as three calls: score, select, attend."""

@@ -38,7 +38,8 @@
  *   - All array arguments are DEVICE pointers (memory of the current HIP
  *     device); the zr_geom / zr_thoughts structs themselves are host memory
  *     and are read during the call only.
- *   - The caller owns every buffer. The library never allocates, frees or
+ *   - The caller owns every buffer (except the built-in device array of
+ *     zr_sparse_decode_step_noalloc). The library never allocates, frees or
  *     synchronizes; each call only enqueues kernels on `stream` (a hipStream_t
  *     passed as void*, NULL = the legacy default stream) and returns.
  *   - Host-visible arguments are validated before anything is enqueued; on a
@@ -93,7 +94,8 @@ typedef enum {
   ZR_E_UNSUPPORTED = 3, /* valid request this build has no kernel for */
   ZR_E_WORKSPACE = 4,   /* workspace NULL or smaller than zr_workspace_bytes() */
   ZR_E_LAUNCH = 5,      /* the HIP runtime reported an error */
-  ZR_E_ALIGN = 6        /* q, pools, out or summary keys not 16-byte aligned */
+  ZR_E_ALIGN = 6,       /* q, pools, out or summary keys not 16-byte aligned */
+  ZR_E_SCRATCH = 7      /* zr_sparse_decode_step_noalloc: more than ZR_NOALLOC_SCRATCH_BYTES needed */
 } zr_status;
 
 typedef enum { ZR_F32 = 0, ZR_BF16 = 1 } zr_dtype;
@@ -103,6 +105,7 @@ typedef enum { ZR_F32 = 0, ZR_BF16 = 1 } zr_dtype;
 #define ZR_MAX_K 1024                 /* k of zr_select_topk / zr_sparse_decode_attn */
 #define ZR_MAX_THOUGHTS_PER_SEQ 8192  /* zr_thoughts.max_per_seq */
 #define ZR_MAX_PAIRS 4096             /* batch * n_kv_heads of the attention and step calls */
+#define ZR_NOALLOC_SCRATCH_BYTES (16u << 20) /* device scratch of zr_sparse_decode_step_noalloc */
 
 /* Per-sequence results of zr_append_kv. */
 #define ZR_APPEND_OK 0              /* token appended, seq_lens[b] grew by one */
@@ -272,6 +275,31 @@ zr_status zr_sparse_decode_step(const zr_geom* geom, const void* q, const void* 
                                 int32_t window, float scale, int32_t max_attended,
                                 float* scores, int32_t* sel, float* out, void* workspace,
                                 size_t ws_bytes, void* stream);
+
+/*
+ * zr_sparse_decode_step for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same step with the same arguments minus the workspace,
+ * whose role a device array built into the library takes, ZR_NOALLOC_SCRATCH_BYTES
+ * (16 MiB) on each GPU the library runs on, held until the process ends.
+ * The call allocates nothing. Results are bit-identical to
+ * zr_sparse_decode_step with a workspace of its own. The array's address is
+ * looked up on the first call on each device (with that device current).
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (other streams, other threads) race, and the block lists a call
+ * leaves there are overwritten by the next call (zr_sparse_decode_attn_cached
+ * cannot reuse them).
+ * Errors: those of zr_sparse_decode_step; ZR_E_SCRATCH when
+ * zr_workspace_bytes(geom, max_attended) exceeds ZR_NOALLOC_SCRATCH_BYTES
+ * (checked before anything is enqueued); ZR_E_LAUNCH also when the array's
+ * address cannot be obtained.
+ */
+zr_status zr_sparse_decode_step_noalloc(const zr_geom* geom, const void* q, const void* k_pool,
+                                        const void* v_pool, const int32_t* block_table,
+                                        const int32_t* seq_lens, const zr_thoughts* th,
+                                        int32_t k, int32_t window, float scale,
+                                        int32_t max_attended, float* scores, int32_t* sel,
+                                        float* out, void* stream);
 
 /*
  * Dense paged decode attention (the baseline): softmax attention of every

@@ -25,6 +25,7 @@ def test_exports_every_declared_symbol(L):
     assert declared == sorted(["zr_coarse_score", "zr_select_topk", "zr_score_topk",
                                "zr_sparse_decode_attn",
                                "zr_sparse_decode_attn_cached", "zr_sparse_decode_step",
+                               "zr_sparse_decode_step_noalloc",
                                "zr_sparse_decode_attn_partials", "zr_attn_combine",
                                "zr_dense_paged_decode_attn", "zr_append_kv", "zr_summary_keys",
                                "zr_consensus", "zr_zoom_decode_attn",
@@ -39,7 +40,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_status_strings(L):
-    for s in range(7):
+    for s in range(8):
         assert zr.status_string(s)
     assert zr.status_string(99) == "unknown zr_status"
 
@@ -264,3 +265,18 @@ def test_summary_prefetch_rule(L):
     assert zr.zr_summary_prefetch_rule(g32, 8 * 30, 32)[1] == 32
     assert zr.zr_summary_prefetch_rule(g, -1, 0)[0] == zr.ZR_E_SHAPE
     assert zr.zr_summary_prefetch_rule(_geom(head_dim=96), 10, 2)[0] == zr.ZR_E_UNSUPPORTED
+
+
+def test_noalloc_step_errors(L):
+    """Argument checks of zr_sparse_decode_step_noalloc that return before any
+    device call: a workspace larger than the built scratch is ZR_E_SCRATCH."""
+    g = _geom()
+    f = lambda geom, **kw: zr.zr_sparse_decode_step_noalloc(**dict(dict(
+        geom=geom, q=FAKE, k_pool=FAKE, v_pool=FAKE, block_table=FAKE, seq_lens=FAKE, th=_th(),
+        k=2, window=16, scale=0.1, max_attended=100, scores=FAKE, sel=FAKE, out=FAKE), **kw))
+    big = _geom(batch=512, n_q_heads=32, n_kv_heads=8, max_blocks_per_seq=8192)
+    assert zr.zr_workspace_bytes(big, 100) > zr.ZR_NOALLOC_SCRATCH_BYTES
+    assert f(big) == zr.ZR_E_SCRATCH
+    assert f(g, max_attended=-1) == zr.ZR_E_SHAPE
+    assert f(_geom(head_dim=96)) == zr.ZR_E_UNSUPPORTED
+    assert f(_geom(batch=0)) == zr.ZR_OK  # nothing to do, nothing touched
