@@ -438,29 +438,125 @@ def main():
             del ws_, ss_, g_o, g_s
             torch.cuda.empty_cache()
 
-    # host-offloaded cache (ZoomR Sec. 3.4): layer 0's pools in pinned host
-    # memory; the kernels read only the attended blocks over PCIe
+    # host-offloaded cache (ZoomR Sec. 3.4, "Decoding Stage"): pools in pinned
+    # host memory, each step bringing only the attended set to the GPU.
+    # Direct: the attention kernels read the listed blocks over the host link.
+    # Staged: zr_stage_selected copies each layer's listed tiles and window
+    # into a device staging pool, then attention runs on it; serially (stage,
+    # attend, next layer) and pipelined (layer i + 1 staged on a second
+    # stream while layer i attends, two staging buffers). 32 layer steps
+    # rotate over 4 layers' host pools, each with its own selection.
     offload = None
     if not args.no_offload:
-        kp_h, vp_h = w0.k_pool.cpu().pin_memory(), w0.v_pool.cpu().pin_memory()
-        hs = zr.DeviceStep(w0.q, kp_h, vp_h, w0.block_table, w0.seq_lens, w0.seq_ptr,
-                           w0.th_start, w0.th_len, w0.summary_keys, w0.max_per_seq, w0.k,
-                           w0.window, w0.scale, steps[0].max_attended)
-        hs.step()
+        log("[bench] host-memory pools")
+        n_host = min(4, L)
+        hosts, pinned = [], []
+        for l in range(n_host):
+            w = layers[l]
+            kp_h, vp_h = w.k_pool.cpu().pin_memory(), w.v_pool.cpu().pin_memory()
+            pinned.append((kp_h, vp_h))
+            hosts.append(zr.DeviceStep(w.q, kp_h, vp_h, steps[0].block_table, steps[0].seq_lens,
+                                       steps[0].seq_ptr, steps[0].th_start, steps[0].th_len,
+                                       w.summary_keys, w0.max_per_seq, w0.k, w0.window,
+                                       w0.scale, steps[0].max_attended))
         torch.cuda.synchronize()
+        hs0 = hosts[0]
         n_off = 10
-        g_off = capture(lambda i: hs.sparse_attn(sel=steps[0].sel), n_off)
+        g_off = capture(lambda i: hs0.sparse_attn(sel=steps[0].sel), n_off)
         g_off.replay()
         off_us = timed(g_off, n_off)
-        g_offd = capture(lambda i: hs.dense_attn(), 2)
+        g_offd = capture(lambda i: hs0.dense_attn(), 2)
         g_offd.replay()
         offd_us = timed(g_offd, 2)
-        offload = {"pools": "pinned host memory, read by the kernels over PCIe (layer 0)",
-                   "sparse_attn_us": round(off_us, 1),
-                   "sparse_h2d_gbs": round(kv_bytes[0] / (off_us * 1e-6) / 1e9, 2),
-                   "dense_attn_us": round(offd_us, 1),
-                   "dense_h2d_gbs": round(dense_bytes / (offd_us * 1e-6) / 1e9, 2)}
-        del hs, kp_h, vp_h
+        stage_blocks = min(w0.max_blocks, -(-steps[0].max_attended // 16) + w0.k + 2)
+        bufs = [zr.Staging(hs0, stage_blocks) for _ in range(2)]
+        n_lay = 32
+
+        def stage_only(i):
+            hosts[i % n_host].stage(bufs[i % 2], sel=steps[i % n_host].sel)
+
+        def serial(i):
+            hosts[i % n_host].stage(bufs[0], sel=steps[i % n_host].sel)
+            hosts[i % n_host].attend_staged(bufs[0])
+
+        g_stage = capture(stage_only, n_lay)
+        g_serial = capture(serial, n_lay)
+        # pipelined: a second stream (default priority) stages while the
+        # capture stream attends; events order stage i before attention i and
+        # attention i before staging i + 2 into the same buffer
+        g_pipe = torch.cuda.CUDAGraph()
+        s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+        s1.wait_stream(torch.cuda.current_stream())
+        ev_st = [torch.cuda.Event() for _ in range(n_lay)]
+        ev_at = [torch.cuda.Event() for _ in range(n_lay)]
+        with torch.cuda.stream(s1):
+            with torch.cuda.graph(g_pipe, stream=s1):
+                s2.wait_stream(s1)
+                for i in range(n_lay):
+                    with torch.cuda.stream(s2):
+                        if i >= 2:
+                            s2.wait_event(ev_at[i - 2])
+                        hosts[i % n_host].stage(bufs[i % 2], sel=steps[i % n_host].sel)
+                        ev_st[i].record(s2)
+                    s1.wait_event(ev_st[i])
+                    hosts[i % n_host].attend_staged(bufs[i % 2])
+                    ev_at[i].record(s1)
+                s1.wait_stream(s2)
+        torch.cuda.current_stream().wait_stream(s1)
+        torch.cuda.synchronize()
+        # the staged output equals the direct one (same lists, bit for bit)
+        hs0.sparse_attn(sel=steps[0].sel)
+        torch.cuda.synchronize()
+        direct_out = hs0.out.clone()
+        hs0.stage(bufs[0], sel=steps[0].sel)
+        hs0.attend_staged(bufs[0])
+        torch.cuda.synchronize()
+        assert torch.equal(direct_out, hs0.out), "staged attention differs from direct"
+        assert int(bufs[0].dropped.sum().item()) == 0, "staging pool too small"
+        for g_ in (g_stage, g_serial, g_pipe):
+            g_.replay()
+        torch.cuda.synchronize()
+        stage_us = timed(g_stage, n_lay)
+        serial_us = timed(g_serial, n_lay)
+        pipe_us = timed(g_pipe, n_lay)
+        # bytes moved per layer step: whole (block, KV head) tiles of keys and
+        # values, for each pair's listed span blocks and window blocks
+        tile = 16 * d * s_bytes
+        moved = []
+        for l in range(n_host):
+            sel_l = steps[l].sel.cpu().numpy()
+            nb = 0
+            for b in range(w0.B):
+                T = int(w0.seq_lens[b])
+                tw = max(0, T - w0.window)
+                lo = int(w0.seq_ptr[b])
+                for g in range(w0.Hkv):
+                    blocks = set()
+                    for t_ in sel_l[b, g]:
+                        if t_ < 0:
+                            continue
+                        s0 = int(w0.th_start[lo + t_])
+                        e = min(s0 + int(w0.th_len[lo + t_]), tw)
+                        if e > s0:
+                            blocks |= set(range(s0 // 16, (e - 1) // 16 + 1))
+                    nb += len(blocks) + (((T - 1) // 16 - tw // 16 + 1) if T > tw else 0)
+            moved.append(nb * 2 * tile)
+        moved_b = float(np.mean(moved))
+        offload = {"pools": f"pinned host memory ({n_host} layers, {n_lay} layer steps)",
+                   "direct_sparse_attn_us": round(off_us, 1),
+                   "direct_sparse_h2d_gbs": round(kv_bytes[0] / (off_us * 1e-6) / 1e9, 2),
+                   "direct_dense_attn_us": round(offd_us, 1),
+                   "direct_dense_h2d_gbs": round(dense_bytes / (offd_us * 1e-6) / 1e9, 2),
+                   "stage_blocks_per_seq": stage_blocks,
+                   "staged_bytes_per_layer": int(moved_b),
+                   "stage_us_per_layer": round(stage_us, 1),
+                   "stage_h2d_gbs": round(moved_b / (stage_us * 1e-6) / 1e9, 2),
+                   "serial_us_per_layer": round(serial_us, 1),
+                   "pipelined_us_per_layer": round(pipe_us, 1),
+                   "staging_device_bytes": int(2 * (bufs[0].k_stage.numel() * 2
+                                                    * bufs[0].k_stage.element_size())),
+                   "full_cache_bytes_per_layer": dense_bytes}
+        del hosts, pinned, bufs, g_stage, g_serial, g_pipe, g_off, g_offd
 
     # dense baseline (same caches, every token) for context
     dense_us = timed(g_dense, L)

@@ -487,6 +487,70 @@ ZR_API zr_status zr_dense_paged_decode_attn(const zr_geom* geom, const void* q,
   return ZR_OK;
 }
 
+ZR_API zr_status zr_stage_selected(const zr_geom* geom, const void* k_pool, const void* v_pool,
+                                   const int32_t* block_table, const int32_t* seq_lens,
+                                   const zr_thoughts* th, const int32_t* sel, int32_t k,
+                                   int32_t window, int32_t max_attended, void* workspace,
+                                   size_t ws_bytes, int32_t stage_blocks, void* k_stage,
+                                   void* v_stage, void* stage_workspace, size_t stage_ws_bytes,
+                                   int32_t* dropped, void* stream) {
+  zr_status st = check_geom(geom);
+  if (st != ZR_OK) return st;
+  st = check_thoughts(th, false);
+  if (st != ZR_OK) return st;
+  if (k < 0 || k > ZR_MAX_K || window < 0 || max_attended < 0) return ZR_E_SHAPE;
+  if (stage_blocks < 1 || stage_blocks > geom->max_blocks_per_seq) return ZR_E_SHAPE;
+  if (!k_pool || !v_pool || !block_table || !seq_lens || !k_stage || !v_stage || !dropped ||
+      (k > 0 && !sel))
+    return ZR_E_NULL;
+  if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(k_stage) || !aligned16(v_stage))
+    return ZR_E_ALIGN;
+  if (static_cast<int64_t>(geom->batch) * geom->n_kv_heads > ZR_MAX_PAIRS)
+    return ZR_E_UNSUPPORTED;
+  // staging pool row indices are int32 inside the kernels, as the pools'
+  if (static_cast<int64_t>(geom->batch) * stage_blocks * geom->n_kv_heads * ZR_BLOCK_SIZE >
+      INT32_MAX)
+    return ZR_E_UNSUPPORTED;
+  if (!zr::pair_lds_ok(*geom, th->max_per_seq, k, false, true)) return ZR_E_UNSUPPORTED;
+  zr::AttnArgs a{}, sa{};
+  st = attention_workspace(geom, max_attended, workspace, ws_bytes, &a);
+  if (st != ZR_OK) return st;
+  zr_geom gs = *geom;
+  gs.num_blocks = geom->batch > 0 ? geom->batch * stage_blocks : 1;
+  st = attention_workspace(&gs, max_attended, stage_workspace, stage_ws_bytes, &sa);
+  if (st != ZR_OK) return st;
+  if (geom->batch == 0) return ZR_OK;
+  zr::PairArgs pa{};
+  pa.seq_ptr = th->seq_ptr;
+  pa.th_start = th->start;
+  pa.th_len = th->len;
+  pa.sel = const_cast<int32_t*>(sel);  // read only in this mode
+  fill_plan(*geom, *th, k, window, block_table, seq_lens, a, &pa);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (zr::launch_pair(*geom, pa, zr::kModePlan, s) != hipSuccess) return ZR_E_LAUNCH;
+  zr::StageArgs ga{};
+  ga.k_pool = k_pool;
+  ga.v_pool = v_pool;
+  ga.block_table = block_table;
+  ga.seq_lens = seq_lens;
+  ga.counts = a.counts;
+  ga.entries = a.entries;
+  ga.k_stage = k_stage;
+  ga.v_stage = v_stage;
+  ga.s_counts = const_cast<int32_t*>(sa.counts);  // written by the stage kernel
+  ga.s_entries = const_cast<int2*>(sa.entries);
+  ga.dropped = dropped;
+  ga.Hkv = geom->n_kv_heads;
+  ga.max_blocks = geom->max_blocks_per_seq;
+  ga.num_blocks = geom->num_blocks;
+  ga.window = window;
+  ga.stage_blocks = stage_blocks;
+  const int tile = ZR_BLOCK_SIZE * geom->head_dim * (geom->dtype == ZR_BF16 ? 2 : 4);
+  ga.lg_pieces = __builtin_ctz(static_cast<unsigned>(tile / 16));
+  if (zr::launch_stage(*geom, ga, s) != hipSuccess) return ZR_E_LAUNCH;
+  return ZR_OK;
+}
+
 // ---------------------------------------------------------------------------
 // The sparse decode step without a caller workspace: its kernels use a
 // file-scope device array instead. In host code `scratch` names a host-side

@@ -247,7 +247,25 @@ struct SummaryArgs {
   int32_t B, Hkv, max_blocks, num_blocks, n_total;
 };
 
+// Staging of a step's attended tiles into device memory (zr_stage.hip).
+struct StageArgs {
+  const void* k_pool;         // source pools (device memory or device-mapped host memory)
+  const void* v_pool;
+  const int32_t* block_table; // [B][max_blocks]
+  const int32_t* seq_lens;    // [B]
+  const int32_t* counts;      // [P] cached list lengths (pair kernel)
+  const int2* entries;        // [P][max_blocks] cached lists (pair kernel)
+  void* k_stage;              // [B * stage_blocks][Hkv][16][D]
+  void* v_stage;              // [B * stage_blocks][Hkv][D][16]
+  int32_t* s_counts;          // [P] staged list lengths
+  int2* s_entries;            // [P][max_blocks] staged lists
+  int32_t* dropped;           // [P] entries that did not fit
+  int32_t Hkv, max_blocks, num_blocks, window, stage_blocks;
+  int32_t lg_pieces;          // log2(16-byte pieces per tile): tile = 16 * D * element bytes
+};
+
 // Host-side launchers (defined next to their kernels).
+hipError_t launch_stage(const zr_geom& g, const StageArgs& a, hipStream_t s);
 hipError_t launch_append(const zr_geom& g, const AppendArgs& a, hipStream_t s);
 hipError_t launch_summary_keys(const zr_geom& g, const SummaryArgs& a, int n_which,
                                hipStream_t s);

@@ -62,6 +62,9 @@ _SIGS = {
     "zr_sparse_decode_step_noalloc": (ctypes.c_int, [_G, _P, _P, _P, _P, _P, _T, ctypes.c_int32,
                                                      ctypes.c_int32, ctypes.c_float,
                                                      ctypes.c_int32, _P, _P, _P, _P]),
+    "zr_stage_selected": (ctypes.c_int, [_G, _P, _P, _P, _P, _T, _P, ctypes.c_int32,
+                                         ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_size_t,
+                                         ctypes.c_int32, _P, _P, _P, ctypes.c_size_t, _P, _P]),
     "zr_sparse_decode_attn_cached": (ctypes.c_int, [_G, _P, _P, _P, _P, _P, ctypes.c_int32,
                                                     ctypes.c_float, ctypes.c_int32, _P, _P,
                                                     ctypes.c_size_t, _P]),
@@ -154,6 +157,15 @@ def zr_sparse_decode_step_noalloc(geom, q, k_pool, v_pool, block_table, seq_lens
                                                block_table, seq_lens, ctypes.byref(th), int(k),
                                                int(window), float(scale), int(max_attended),
                                                scores, sel, out, stream)
+
+
+def zr_stage_selected(geom, k_pool, v_pool, block_table, seq_lens, th, sel, k, window,
+                      max_attended, workspace, ws_bytes, stage_blocks, k_stage, v_stage,
+                      stage_workspace, stage_ws_bytes, dropped, stream=None) -> int:
+    return lib().zr_stage_selected(ctypes.byref(geom), k_pool, v_pool, block_table, seq_lens,
+                                   ctypes.byref(th), sel, int(k), int(window), int(max_attended),
+                                   workspace, int(ws_bytes), int(stage_blocks), k_stage, v_stage,
+                                   stage_workspace, int(stage_ws_bytes), dropped, stream)
 
 
 def zr_sparse_decode_attn_cached(geom, q, k_pool, v_pool, block_table, seq_lens, window, scale,
@@ -430,11 +442,56 @@ class DeviceStep:
             _ptr(self.seq_lens), self.th, self.k, self.window, self.scale, self.max_attended,
             _ptr(scores), _ptr(sel) if self.k else None, _ptr(out), _stream()))
 
+    def stage(self, staging, sel=None, window=None):
+        """Build this step's block lists from `sel` and copy the listed K/V
+        tiles (and the window's) from the pools, which may be in pinned host
+        memory, into `staging` (zr_stage_selected)."""
+        sel = self.sel if sel is None else sel
+        window = self.window if window is None else int(window)
+        check("zr_stage_selected", zr_stage_selected(
+            self.geom, self.kp, self.vp, _ptr(self.block_table), _ptr(self.seq_lens), self.th,
+            _ptr(sel) if self.k else None, self.k, window, self.max_attended,
+            _ptr(self.workspace), self.workspace.numel(), staging.stage_blocks,
+            _ptr(staging.k_stage), _ptr(staging.v_stage), _ptr(staging.workspace),
+            staging.workspace.numel(), _ptr(staging.dropped), _stream()))
+
+    def attend_staged(self, staging, out=None, q=None):
+        """Attention over what the last stage() call moved into `staging`
+        (zr_sparse_decode_attn_cached on the staging pools, no window)."""
+        out = self.out if out is None else out
+        q = self.q if q is None else q
+        check("zr_sparse_decode_attn_cached", zr_sparse_decode_attn_cached(
+            staging.geom, _ptr(q), _ptr(staging.k_stage), _ptr(staging.v_stage),
+            _ptr(self.block_table), _ptr(self.seq_lens), 0, self.scale, self.max_attended,
+            _ptr(out), _ptr(staging.workspace), staging.workspace.numel(), _stream()))
+
     def step_calls(self):
         """The same step as three calls: score, select, attend."""
         self.coarse_score()
         self.select_topk()
         self.sparse_attn()
+
+
+class Staging:
+    """Device buffers that receive a step's attended K/V tiles
+    (zr_stage_selected): staging pools for `stage_blocks` blocks per
+    sequence, their block lists and the per-pair count of entries that did
+    not fit. `geom` is the staged geometry (num_blocks = batch *
+    stage_blocks)."""
+
+    def __init__(self, step: "DeviceStep", stage_blocks: int):
+        g = step.geom
+        self.stage_blocks = int(stage_blocks)
+        dev = step.q.device
+        nb = max(g.batch * self.stage_blocks, 1)
+        dt = step.q.dtype
+        self.k_stage = torch.empty((nb, g.n_kv_heads, 16, g.head_dim), dtype=dt, device=dev)
+        self.v_stage = torch.empty((nb, g.n_kv_heads, g.head_dim, 16), dtype=dt, device=dev)
+        self.geom = zr_geom(g.batch, g.n_q_heads, g.n_kv_heads, g.head_dim, 16,
+                            g.max_blocks_per_seq, nb, g.dtype)
+        ws = zr_workspace_bytes(self.geom, step.max_attended)
+        self.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=dev)
+        self.dropped = torch.empty(max(g.batch * g.n_kv_heads, 1), dtype=torch.int32, device=dev)
 
 
 def max_attended_bound(seq_lens, seq_ptr, th_len, k, window):

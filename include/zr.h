@@ -277,6 +277,46 @@ zr_status zr_sparse_decode_step(const zr_geom* geom, const void* q, const void* 
                                 size_t ws_bytes, void* stream);
 
 /*
+ * The per-step host-to-device move of the attended set, for pools kept in
+ * host memory (ZoomR Sec. 3.4, "Decoding Stage": the full cache stays in CPU
+ * memory and each generation step loads only the entries of I_f to the GPU).
+ * k_pool / v_pool may be device-mapped pinned host memory (or device memory).
+ * The call
+ *   1. builds each (sequence b, KV head g) pair's block list from `sel` and
+ *      `th` into `workspace`, as zr_sparse_decode_attn does (selected spans
+ *      clipped below T - window; the same lists zr_sparse_decode_attn_cached
+ *      reads);
+ *   2. copies, for every pair, the key and value tiles of the listed blocks
+ *      and then of the window [T - window, T) into the staging pools:
+ *      entry j of pair (b, g) goes to staging block b * stage_blocks + j,
+ *      KV head g (k_stage [batch * stage_blocks][n_kv_heads][16][head_dim],
+ *      v_stage [batch * stage_blocks][n_kv_heads][head_dim][16], device
+ *      memory, 16-byte aligned);
+ *   3. writes the pairs' lists again with staging block ids into
+ *      `stage_workspace` (at least zr_workspace_bytes(geom_stage,
+ *      max_attended) bytes, geom_stage = geom with num_blocks = batch *
+ *      stage_blocks).
+ * zr_sparse_decode_attn_cached(geom_stage, q, k_stage, v_stage, block_table,
+ * seq_lens, 0, scale, max_attended, out, stage_workspace, ...) then gives,
+ * bit for bit, zr_sparse_decode_attn on the original pools with the same
+ * sel and window. Entries past stage_blocks of a pair are not staged (that
+ * attention then leaves them out): dropped[p] ([batch * n_kv_heads] int32)
+ * receives their number, 0 when the pair fits. A pair lists at most
+ * ceil(max_attended / 16) + k + 2 blocks when max_attended bounds its
+ * attended tokens.
+ * Errors: ZR_E_NULL, ZR_E_SHAPE (k, window, max_attended < 0; k > ZR_MAX_K;
+ * stage_blocks outside [1, max_blocks_per_seq]), ZR_E_ALIGN, ZR_E_WORKSPACE
+ * (either workspace), ZR_E_UNSUPPORTED, ZR_E_LAUNCH.
+ */
+zr_status zr_stage_selected(const zr_geom* geom, const void* k_pool, const void* v_pool,
+                            const int32_t* block_table, const int32_t* seq_lens,
+                            const zr_thoughts* th, const int32_t* sel, int32_t k, int32_t window,
+                            int32_t max_attended, void* workspace, size_t ws_bytes,
+                            int32_t stage_blocks, void* k_stage, void* v_stage,
+                            void* stage_workspace, size_t stage_ws_bytes, int32_t* dropped,
+                            void* stream);
+
+/*
  * zr_sparse_decode_step for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid
  * allocation): the same step with the same arguments minus the workspace,

@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol(L):
                                "zr_sparse_decode_attn_partials", "zr_attn_combine",
                                "zr_dense_paged_decode_attn", "zr_append_kv", "zr_summary_keys",
                                "zr_consensus", "zr_zoom_decode_attn",
-                               "zr_summary_prefetch_rule",
+                               "zr_summary_prefetch_rule", "zr_stage_selected",
                                "zr_workspace_bytes", "zr_status_string"])
     out = subprocess.run(["nm", "-D", "--defined-only", zr.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
@@ -280,3 +280,25 @@ def test_noalloc_step_errors(L):
     assert f(g, max_attended=-1) == zr.ZR_E_SHAPE
     assert f(_geom(head_dim=96)) == zr.ZR_E_UNSUPPORTED
     assert f(_geom(batch=0)) == zr.ZR_OK  # nothing to do, nothing touched
+
+
+def test_stage_selected_errors(L):
+    g = _geom()
+    f = lambda **kw: zr.zr_stage_selected(**dict(dict(
+        geom=g, k_pool=FAKE, v_pool=FAKE, block_table=FAKE, seq_lens=FAKE, th=_th(), sel=FAKE,
+        k=2, window=16, max_attended=100, workspace=FAKE, ws_bytes=1 << 20, stage_blocks=4,
+        k_stage=FAKE, v_stage=FAKE, stage_workspace=FAKE, stage_ws_bytes=1 << 20,
+        dropped=FAKE), **kw))
+    assert f(stage_blocks=0) == zr.ZR_E_SHAPE
+    assert f(stage_blocks=5) == zr.ZR_E_SHAPE   # more than max_blocks_per_seq
+    assert f(k=-1) == zr.ZR_E_SHAPE
+    assert f(window=-1) == zr.ZR_E_SHAPE
+    assert f(sel=None) == zr.ZR_E_NULL
+    assert f(dropped=None) == zr.ZR_E_NULL
+    assert f(k_stage=None) == zr.ZR_E_NULL
+    assert f(v_stage=FAKE + 8) == zr.ZR_E_ALIGN
+    assert f(workspace=None) == zr.ZR_E_WORKSPACE
+    assert f(stage_workspace=None) == zr.ZR_E_WORKSPACE
+    assert f(stage_ws_bytes=16) == zr.ZR_E_WORKSPACE
+    assert f(geom=_geom(head_dim=96)) == zr.ZR_E_UNSUPPORTED
+    assert f(geom=_geom(batch=0)) == zr.ZR_OK

@@ -354,8 +354,9 @@ def test_partials_then_combine_equal_the_cached_call(cfg):
 def test_pools_in_pinned_host_memory():
     """The K/V pools kept in pinned host memory (ZoomR Sec. 3.4: the full
     cache lives in CPU memory and each step moves the selected part to the
-    GPU): the kernels read only the listed blocks over PCIe, and every output
-    equals the run on device-resident pools bit for bit."""
+    GPU): the kernels read only the listed blocks over the host link. Every
+    output equals the oracle (sparse and dense) and the run on
+    device-resident pools bit for bit."""
     w = _small(1, k=5)
     st = zr.step_from_workload(w)
     st.step()
@@ -367,12 +368,94 @@ def test_pools_in_pinned_host_memory():
     say(f"[gpu] pinned pools: host {kp.data_ptr():#x} -> device {hs.kp:#x}")
     hs.step()
     torch.cuda.synchronize()
+    h = P.host(w)
+    orc = P.oracle_step(w, h)
+    events = P.compare_selection(hs.sel.cpu().numpy(), orc["scores"], w.seq_ptr, w.k, w.Hkv)
+    if events:
+        orc = P.oracle_step(w, h, sel=hs.sel.cpu().numpy())
+    err = float(np.max(np.abs(hs.out.cpu().numpy() - orc["out"])))
+    say(f"[gpu] pinned pools: max|out - oracle| = {err:.3e}")
+    assert err <= P.TOL[w.dtype]
     assert torch.equal(hs.scores, ref[0]) and torch.equal(hs.sel, ref[1])
     assert torch.equal(hs.out, ref[2])
     st.dense_attn()
     hs.dense_attn()
     torch.cuda.synchronize()
+    ref_d = O.dense_decode_step(h["q"], h["k_pool"], h["v_pool"], w.block_table, w.seq_lens,
+                                w.scale)
+    err_d = float(np.max(np.abs(hs.out.cpu().numpy() - ref_d)))
+    say(f"[gpu] pinned pools, dense: max|out - oracle| = {err_d:.3e}")
+    assert err_d <= P.TOL[w.dtype]
     assert torch.equal(hs.out, st.out)
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
+def test_staged_attended_set_from_host_pools(dtype, d):
+    """zr_stage_selected moves each pair's listed tiles and window from pools
+    in pinned host memory into a device staging pool; attention over it
+    equals the oracle and, bit for bit, the attention over device-resident
+    pools with the same selection and window (also with a grown window, as
+    between semantic boundaries)."""
+    w = _small(1, k=5, dtype=dtype, d=d)
+    st = zr.step_from_workload(w)
+    st.step()
+    torch.cuda.synchronize()
+    kp, vp = w.k_pool.cpu().pin_memory(), w.v_pool.cpu().pin_memory()
+    hs = zr.DeviceStep(w.q, kp, vp, w.block_table, w.seq_lens, w.seq_ptr, w.th_start, w.th_len,
+                       w.summary_keys, w.max_per_seq, w.k, w.window, w.scale, st.max_attended)
+    blocks = -(-st.max_attended // 16) + w.k + 2
+    sg = zr.Staging(hs, min(blocks, w.max_blocks))
+    h = P.host(w)
+    sel = st.sel.clone()
+    for win in (w.window, w.window + 7):
+        hs.stage(sg, sel=sel, window=win)
+        hs.attend_staged(sg)
+        st.window = win
+        st.sparse_attn(sel=sel)
+        torch.cuda.synchronize()
+        assert int(sg.dropped.sum().item()) == 0
+        assert torch.equal(hs.out, st.out), win
+        ref = O.sparse_decode_step(h["q"], h["k_pool"], h["v_pool"], w.block_table, w.seq_lens,
+                                   w.seq_ptr, w.th_start, w.th_len, h["kbar"], w.k, win, w.scale,
+                                   sel=sel.cpu().numpy())
+        err = float(np.max(np.abs(hs.out.cpu().numpy() - ref["out"])))
+        say(f"[gpu] staged {dtype} window {win}: {sg.stage_blocks} blocks per sequence, "
+            f"max|out - oracle| = {err:.3e}")
+        assert err <= P.TOL[w.dtype]
+
+
+def test_staging_reports_entries_that_do_not_fit():
+    """With room for fewer blocks than a pair lists, dropped[p] counts the
+    entries left out (the pair's list length minus the room)."""
+    w = _small(1, k=5)
+    st = zr.step_from_workload(w)
+    st.step()
+    torch.cuda.synchronize()
+    full = zr.Staging(st, w.max_blocks)
+    st.stage(full)
+    small = zr.Staging(st, 3)
+    st.stage(small)
+    torch.cuda.synchronize()
+    assert int(full.dropped.sum().item()) == 0
+    got = small.dropped.cpu().numpy()
+    # a pair's list: the blocks of its selected spans clipped below the
+    # window start, then the window's blocks
+    for b in range(w.B):
+        T = int(w.seq_lens[b])
+        lo, hi = int(w.seq_ptr[b]), int(w.seq_ptr[b + 1])
+        tw = max(0, T - w.window)
+        for g in range(w.Hkv):
+            sel = st.sel.cpu().numpy()[b, g]
+            blocks = set()
+            for i in sel[sel >= 0]:
+                s0 = int(w.th_start[lo + i])
+                e = min(s0 + int(w.th_len[lo + i]), tw)
+                if e > s0:
+                    blocks |= set(range(s0 // 16, (e - 1) // 16 + 1))
+            wb = ((T - 1) // 16 - tw // 16 + 1) if T > tw else 0
+            n = len(blocks) + wb
+            assert got[b * w.Hkv + g] == max(0, n - 3), (b, g, n)
+    assert got.sum() > 0
 
 
 def test_many_pairs_and_largest_k():
