@@ -26,16 +26,18 @@
 // release/acquire per workgroup, which on this GPU writes back and
 // invalidates the whole L2; the kernel boundary is far cheaper.)
 //
-// bf16 kernel (matrix cores). With the block's 16 slots as the rows:
-//   S^T[slot][head] = K_block (16 x d) . Q^T (d x 16 heads, zero padded)
-// on v_mfma_f32_16x16x32_bf16. In the output layout each lane holds four
-// consecutive slots of one head, which is exactly the A-operand layout of
+// bf16 kernel (matrix cores), on chunks of two blocks (32 slots):
+//   S^T[slot][head] = K (16 slots x d) . Q^T (d x 16 heads, zero padded)
+// on v_mfma_f32_16x16x32_bf16, twice per chunk, with the key rows taken in an
+// order that leaves each lane 8 consecutive slots of one block for one head:
+// exactly the A-operand layout of
 //   O[head][dim] += P[head][slot] . V[slot][dim]
-// on v_mfma_f32_16x16x16_bf16, so P never leaves the lane. V blocks are stored
-// dimension-major, so each lane's B operand (4 slots of one dimension) is one
-// 8-byte load and a wave reads a block's values as contiguous 512-byte
-// segments. P is split into bf16 hi + lo parts (p - hi rounded again), so the
-// probabilities keep ~16 significant bits; products accumulate in fp32.
+// on v_mfma_f32_16x16x32_bf16 over the chunk's 32 slots, so P never leaves
+// the lane. V blocks are stored dimension-major, so each lane's B operand (8
+// slots of one dimension) is one 16-byte load and a wave reads a block's
+// values as contiguous 512-byte segments. P is split into bf16 hi + lo parts
+// (p - hi rounded again), so the probabilities keep ~16 significant bits;
+// products accumulate in fp32.
 //
 // fp32 kernel (vector ALU): key rows are read with 16-byte loads, LPR lanes per
 // row, logits reduced across the row's lanes with shuffles; probabilities go
@@ -597,19 +599,30 @@ __device__ __forceinline__ float bf16_at(const bf16x4& v, int i) {
   return __uint_as_float(static_cast<uint32_t>(static_cast<uint16_t>(v[i])) << 16);
 }
 
+// One chunk is two blocks: the K dimension of the P.V product is their 32
+// slots. Lane group lg (lanes 16 lg .. 16 lg + 15) owns the 8 consecutive
+// slots 8 (lg & 1) .. +7 of block lg >> 1, so that its value operand of
+// v_mfma_f32_16x16x32_bf16 (8 slots of one dimension) is one 16-byte load
+// from the dimension-major value tile, and its probabilities come from the
+// two S^T products below without any exchange between lanes: product hf
+// takes as row i the key of block i >> 3, slot 8 ((i >> 2) & 1) + 4 hf +
+// (i & 3), and its output rows 4 lg .. 4 lg + 3 are then slots
+// 8 (lg & 1) + 4 hf .. +3 of block lg >> 1.
 template <int D, int NBW>
 struct Chunk {
-  bf16x8 k[NBW][D / 32];  // K rows: lane holds slot l16, dims 32 kk + 8 lg .. +7 (A operand)
-  bf16x4 v[NBW][D / 16];  // V: lane holds dim 16 nt + l16, slots 4 lg .. +3 (B operand)
-  uint32_t msk[NBW];
+  static_assert(NBW == 2, "a chunk is two blocks");
+  bf16x8 k[2][D / 32];  // K rows of product hf: lane holds row l16, dims 32 kk + 8 lg .. +7
+  bf16x8 v[D / 16];     // V: lane holds dim 16 nt + l16, slots 8 (lg & 1) .. +7 of block lg >> 1
+  uint32_t msk[2];      // slot masks of the two blocks (uniform)
 };
 
 // Issue the loads of this wave's chunk `c` (entries held lane-wise in
 // pb_l/msk_l). Branch-free, so the compiler keeps the next chunk's loads in
-// flight while the current one is computed: a lane whose slot (or 4-slot
-// group) is outside the set re-reads a line that an attended slot's lane
-// fetches anyway, and its values are cleared (keys need no clearing: their
-// logits are replaced by -inf).
+// flight while the current one is computed: a lane whose key row is outside
+// the set re-reads the row of the block's first attended slot (a line that
+// is fetched anyway), and its logit is replaced by -inf; value slots outside
+// the set are cleared before use (a value tile is read whole: each of its
+// 32-byte dimension rows holds all 16 slots).
 template <int D, int NBW>
 __device__ __forceinline__ void load_chunk(const AttnArgs& a, int g, int c, int pb_l,
                                            uint32_t msk_l, Chunk<D, NBW>& ch) {
@@ -617,23 +630,37 @@ __device__ __forceinline__ void load_chunk(const AttnArgs& a, int g, int c, int 
   const int lane = threadIdx.x & 63, l16 = lane & 15, lg = lane >> 4;
   const uint16_t* kpool = static_cast<const uint16_t*>(a.k_pool);
   const uint16_t* vpool = static_cast<const uint16_t*>(a.v_pool);
-#pragma unroll
-  for (int i = 0; i < NBW; ++i) {
-    const int pb = __builtin_amdgcn_readlane(pb_l, c * NBW + i);
-    const uint32_t msk = __builtin_amdgcn_readlane(static_cast<int>(msk_l), c * NBW + i);
-    ch.msk[i] = msk;
+  const int pb0 = __builtin_amdgcn_readlane(pb_l, c * 2);
+  const int pb1 = __builtin_amdgcn_readlane(pb_l, c * 2 + 1);
+  const uint32_t m0 = __builtin_amdgcn_readlane(static_cast<int>(msk_l), c * 2);
+  const uint32_t m1 = __builtin_amdgcn_readlane(static_cast<int>(msk_l), c * 2 + 1);
+  ch.msk[0] = m0;
+  ch.msk[1] = m1;
+  // keys: row l16 of product hf is block l16 >> 3
+  {
+    const bool hi = (l16 >> 3) != 0;
+    const int pb = hi ? pb1 : pb0;
+    const uint32_t msk = hi ? m1 : m0;
     const int first = msk ? __builtin_ctz(msk) : 0;
     const size_t tile = static_cast<size_t>(pb) * a.Hkv + g;
-    const int kslot = ((msk >> l16) & 1u) ? l16 : first;
-    const uint16_t* krow = kpool + (tile * kBlock + kslot) * D + 8 * lg;
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) ch.k[i][kk] = *reinterpret_cast<const bf16x8*>(krow + 32 * kk);
-    const uint32_t m4 = (msk >> (4 * lg)) & 0xfu;
-    const int vgrp = m4 ? lg : (first >> 2);
-    const uint16_t* vcol = vpool + tile * (D * kBlock) + l16 * kBlock + 4 * vgrp;
+    for (int hf = 0; hf < 2; ++hf) {
+      const int s = 8 * ((l16 >> 2) & 1) + 4 * hf + (l16 & 3);
+      const int kslot = ((msk >> s) & 1u) ? s : first;
+      const uint16_t* krow = kpool + (tile * kBlock + kslot) * D + 8 * lg;
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk)
+        ch.k[hf][kk] = *reinterpret_cast<const bf16x8*>(krow + 32 * kk);
+    }
+  }
+  // values: lane group lg reads block lg >> 1, slots 8 (lg & 1) .. +7
+  {
+    const int pb = (lg >> 1) ? pb1 : pb0;
+    const size_t tile = static_cast<size_t>(pb) * a.Hkv + g;
+    const uint16_t* vcol = vpool + tile * (D * kBlock) + l16 * kBlock + 8 * (lg & 1);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
-      ch.v[i][nt] = *reinterpret_cast<const bf16x4*>(vcol + nt * 16 * kBlock);
+      ch.v[nt] = *reinterpret_cast<const bf16x8*>(vcol + nt * 16 * kBlock);
   }
 }
 
@@ -649,36 +676,39 @@ __device__ __forceinline__ void compute_chunk(const AttnArgs& a, Chunk<D, NBW>& 
                                               MfmaState& stt) {
   constexpr int KS = D / 32, NT = D / 16;
   const int lane = threadIdx.x & 63, lg = lane >> 4;
+  // this lane group's 8 slots of its block
+  const uint32_t m8 = (((lg >> 1) ? ch.msk[1] : ch.msk[0]) >> (8 * (lg & 1))) & 0xffu;
   // clear value slots outside the set (never trust their bits): one 16-bit
-  // lane mask per slot of this lane's 4-slot group
+  // lane mask per slot
+  {
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 keep;
 #pragma unroll
-  for (int i = 0; i < NBW; ++i) {
-    const uint32_t m4 = (ch.msk[i] >> (4 * lg)) & 0xfu;
-    const uint32_t w0 = ((m4 & 1u) ? 0x0000ffffu : 0u) | ((m4 & 2u) ? 0xffff0000u : 0u);
-    const uint32_t w1 = ((m4 & 4u) ? 0x0000ffffu : 0u) | ((m4 & 8u) ? 0xffff0000u : 0u);
+    for (int w = 0; w < 4; ++w)
+      keep[w] = (((m8 >> (2 * w)) & 1u) ? 0x0000ffffu : 0u) |
+                (((m8 >> (2 * w + 1)) & 1u) ? 0xffff0000u : 0u);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-      u32x2 bits = __builtin_bit_cast(u32x2, ch.v[i][nt]);
-      bits.x &= w0;
-      bits.y &= w1;
-      ch.v[i][nt] = __builtin_bit_cast(bf16x4, bits);
+      u32x4 bits = __builtin_bit_cast(u32x4, ch.v[nt]);
+      bits &= keep;
+      ch.v[nt] = __builtin_bit_cast(bf16x8, bits);
     }
   }
-  // S^T = K . Q^T: lane holds slots 4 lg + r of head l16
-  float z[NBW][4];
+  // S^T = K . Q^T: product hf gives this lane slots 8 (lg & 1) + 4 hf + r of
+  // block lg >> 1, head l16
+  float z[2][4];
   float mc = kNegInf;
 #pragma unroll
-  for (int i = 0; i < NBW; ++i) {
+  for (int hf = 0; hf < 2; ++hf) {
     f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk)
-      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ch.k[i][kk], qop[kk], sacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ch.k[hf][kk], qop[kk], sacc, 0, 0, 0);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const bool on = (ch.msk[i] >> (4 * lg + r)) & 1u;
-      z[i][r] = on ? sacc[r] * a.scale_log2 : kNegInf;
-      mc = fmaxf(mc, z[i][r]);
+      const bool on = (m8 >> (4 * hf + r)) & 1u;
+      z[hf][r] = on ? sacc[r] * a.scale_log2 : kNegInf;
+      mc = fmaxf(mc, z[hf][r]);
     }
   }
   mc = fmaxf(mc, __shfl_xor(mc, 16));
@@ -697,22 +727,29 @@ __device__ __forceinline__ void compute_chunk(const AttnArgs& a, Chunk<D, NBW>& 
   }
   stt.m_run = m_new;
   stt.first = false;
+  float pr[8];
 #pragma unroll
-  for (int i = 0; i < NBW; ++i) {
-    float pr[4];
+  for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      pr[r] = z[i][r] != kNegInf ? exp2f(z[i][r] - m_new) : 0.f;
-      stt.l_run += pr[r];
+      const float zz = z[hf][r];
+      pr[4 * hf + r] = zz != kNegInf ? exp2f(zz - m_new) : 0.f;
+      stt.l_run += pr[4 * hf + r];
     }
-    const bf16x4 phi = pack_bf16x4(pr[0], pr[1], pr[2], pr[3]);
-    const bf16x4 plo = pack_bf16x4(pr[0] - bf16_at(phi, 0), pr[1] - bf16_at(phi, 1),
-                                   pr[2] - bf16_at(phi, 2), pr[3] - bf16_at(phi, 3));
+  // P as bf16 hi + lo parts (about 16 significant bits), slots in the order
+  // of the value operand
+  const bf16x4 h0 = pack_bf16x4(pr[0], pr[1], pr[2], pr[3]);
+  const bf16x4 h1 = pack_bf16x4(pr[4], pr[5], pr[6], pr[7]);
+  const bf16x4 l0 = pack_bf16x4(pr[0] - bf16_at(h0, 0), pr[1] - bf16_at(h0, 1),
+                                pr[2] - bf16_at(h0, 2), pr[3] - bf16_at(h0, 3));
+  const bf16x4 l1 = pack_bf16x4(pr[4] - bf16_at(h1, 0), pr[5] - bf16_at(h1, 1),
+                                pr[6] - bf16_at(h1, 2), pr[7] - bf16_at(h1, 3));
+  const bf16x8 phi = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
+  const bf16x8 plo = __builtin_shufflevector(l0, l1, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      o[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, ch.v[i][nt], o[nt], 0, 0, 0);
-      o[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, ch.v[i][nt], o[nt], 0, 0, 0);
-    }
+  for (int nt = 0; nt < NT; ++nt) {
+    o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi, ch.v[nt], o[nt], 0, 0, 0);
+    o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo, ch.v[nt], o[nt], 0, 0, 0);
   }
 }
 
