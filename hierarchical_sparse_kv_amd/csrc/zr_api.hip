@@ -89,6 +89,8 @@ zr_status attention_common(const zr_geom* geom, const void* q, const void* k_poo
   a->v_pool = v_pool;
   a->block_table = block_table;
   a->seq_lens = seq_lens;
+  a->plan_lens = seq_lens;
+  a->horizon = 0;
   a->out = out;
   a->max_blocks = geom->max_blocks_per_seq;
   a->num_blocks = geom->num_blocks;
@@ -302,6 +304,52 @@ ZR_API zr_status zr_sparse_decode_attn_cached(const zr_geom* geom, const void* q
   if (st != ZR_OK) return st;
   a.window = window;
   if (zr::launch_attention(*geom, a, false, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return ZR_E_LAUNCH;
+  return ZR_OK;
+}
+
+ZR_API zr_status zr_reuse_plan(const zr_geom* geom, const int32_t* block_table,
+                               const int32_t* seq_lens, int32_t window, int32_t horizon,
+                               int32_t max_attended, void* workspace, size_t ws_bytes,
+                               void* stream) {
+  zr_status st = check_geom(geom);
+  if (st != ZR_OK) return st;
+  if (window < 0 || horizon < 0 || max_attended < 0) return ZR_E_SHAPE;
+  if (horizon > geom->max_blocks_per_seq * ZR_BLOCK_SIZE) return ZR_E_SHAPE;
+  if (!block_table || !seq_lens) return ZR_E_NULL;
+  if (static_cast<int64_t>(geom->batch) * geom->n_kv_heads *
+          (2 * static_cast<int64_t>(geom->max_blocks_per_seq) + 1) > INT32_MAX)
+    return ZR_E_UNSUPPORTED;
+  zr::AttnArgs a{};
+  st = attention_workspace(geom, max_attended, workspace, ws_bytes, &a);
+  if (st != ZR_OK) return st;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.plan_lens = seq_lens;
+  a.window = window;
+  a.horizon = horizon;
+  a.max_blocks = geom->max_blocks_per_seq;
+  a.num_blocks = geom->num_blocks;
+  a.ws_pref = a.reuse_pref;  // the split's slot bases, kept apart from other calls'
+  if (zr::launch_reuse_plan(*geom, a, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return ZR_E_LAUNCH;
+  return ZR_OK;
+}
+
+ZR_API zr_status zr_sparse_decode_attn_reuse(const zr_geom* geom, const void* q,
+                                             const void* k_pool, const void* v_pool,
+                                             const int32_t* block_table,
+                                             const int32_t* seq_lens, float scale,
+                                             int32_t max_attended, float* out, void* workspace,
+                                             size_t ws_bytes, void* stream) {
+  zr_status st = check_geom(geom);
+  if (st != ZR_OK) return st;
+  zr::AttnArgs a{};
+  st = attention_common(geom, q, k_pool, v_pool, block_table, seq_lens, scale, out, workspace,
+                        ws_bytes, max_attended, &a, false);
+  if (st != ZR_OK) return st;
+  a.window = 0;  // the records (or the settings zr_reuse_plan kept) fix the window
+  if (zr::launch_attention_reuse(*geom, a, static_cast<hipStream_t>(stream)) != hipSuccess)
     return ZR_E_LAUNCH;
   return ZR_OK;
 }

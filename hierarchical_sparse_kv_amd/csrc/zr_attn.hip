@@ -68,11 +68,6 @@ typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 // ---------------------------------------------------------------------------
 // Work assignment
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int cached_len(const AttnArgs& a, int b) {
-  const int T = a.seq_lens[b];
-  const int cap = a.max_blocks * kBlock;
-  return T < 0 ? 0 : (T > cap ? cap : T);
-}
 
 // The pairs' lists, concatenated in pair order (total entries), are cut into
 // nr = min(nwg, total) ranges: workgroup w takes entries [R(w), R(w + 1)) of
@@ -102,17 +97,26 @@ struct PairList {
   int T, tw, ncache, n;
 };
 
+// The plan covers the window [T0 - window, T0 + horizon) of the planned
+// length T0 (plan_lens); the current length T (seq_lens, at most T0 +
+// horizon) ends the attended slots. An ordinary call plans on the current
+// length (plan_lens = seq_lens) with no horizon.
 template <bool DENSE>
 __device__ __forceinline__ PairList pair_list(const AttnArgs& a, int p) {
   PairList r;
-  r.T = cached_len(a, div_small(p, a.Hkv));
-  r.tw = DENSE ? 0 : (r.T - a.window > 0 ? r.T - a.window : 0);
+  const int b = div_small(p, a.Hkv);
+  const int cap = a.max_blocks * kBlock;
+  const int t_plan = a.plan_lens[b], t_now = a.seq_lens[b];
+  const int T0 = t_plan < 0 ? 0 : (t_plan > cap ? cap : t_plan);
+  const int Tp = T0 + a.horizon < cap ? T0 + a.horizon : cap;
+  r.T = t_now < 0 ? 0 : (t_now > Tp ? Tp : t_now);
+  r.tw = DENSE ? 0 : (T0 - a.window > 0 ? T0 - a.window : 0);
   r.ncache = 0;
   if (!DENSE) {
     const int c = a.counts[p];
     r.ncache = c < 0 ? 0 : (c > a.max_blocks ? a.max_blocks : c);
   }
-  const int wb = r.T > r.tw ? ((r.T - 1) >> 4) - (r.tw >> 4) + 1 : 0;
+  const int wb = Tp > r.tw ? ((Tp - 1) >> 4) - (r.tw >> 4) + 1 : 0;
   r.n = r.ncache + wb;
   return r;
 }
@@ -205,7 +209,7 @@ __device__ int plan_wave(const AttnArgs& a, PlanLds& sm, bool records, Assign* s
   const bool publish = w == 0 && threadIdx.x < 64;
   const int K = (P + 63) / 64;
   const int p0 = lane * K;
-  int n[kLanePairs], T[kLanePairs], nc[kLanePairs];
+  int n[kLanePairs], T[kLanePairs], tws[kLanePairs], nc[kLanePairs];
   int nsum = 0;
 #pragma unroll
   for (int j = 0; j < kLanePairs; ++j) {
@@ -213,10 +217,10 @@ __device__ int plan_wave(const AttnArgs& a, PlanLds& sm, bool records, Assign* s
     if (j < K && p0 + j < P) L = pair_list<DENSE>(a, p0 + j);
     n[j] = L.n;
     T[j] = L.T;
+    tws[j] = L.tw;
     nc[j] = L.ncache;
     nsum += L.n;
   }
-  auto window_start = [&](int t) { return DENSE ? 0 : (t - a.window > 0 ? t - a.window : 0); };
   const int incl = wave_incl_sum(nsum);
   const int total = __builtin_amdgcn_readlane(incl, 63);
   const int run = incl - nsum;  // first entry of this lane's pairs
@@ -255,7 +259,7 @@ __device__ int plan_wave(const AttnArgs& a, PlanLds& sm, bool records, Assign* s
     }
     if (w >= total_s) return 0;
     const bool mine = w >= srun && w < srun + ssum;
-    int pj = 0, tj = 0, cj = 0, nj = 0, sj = 1, r = 0;
+    int pj = 0, tj = 0, twj = 0, cj = 0, nj = 0, sj = 1, r = 0;
     if (mine) {
       int r0 = srun;
 #pragma unroll
@@ -264,6 +268,7 @@ __device__ int plan_wave(const AttnArgs& a, PlanLds& sm, bool records, Assign* s
           r = w - r0;
           pj = p0 + j;
           tj = T[j];
+          twj = tws[j];
           cj = nc[j];
           nj = n[j];
           sj = S[j];
@@ -275,8 +280,8 @@ __device__ int plan_wave(const AttnArgs& a, PlanLds& sm, bool records, Assign* s
     const int lo = floor_div(static_cast<int64_t>(r) * nj, sj);
     const int hi = floor_div(static_cast<int64_t>(r + 1) * nj, sj);
     const int src = __ffsll(static_cast<unsigned long long>(__ballot(mine))) - 1;
-    lane_segment(src, pj, tj, window_start(tj), cj, lo, hi, w, sa);
-    if (records && mine) put_record(sm, 0, pj, tj, window_start(tj), cj, lo, hi, w);
+    lane_segment(src, pj, tj, twj, cj, lo, hi, w, sa);
+    if (records && mine) put_record(sm, 0, pj, tj, twj, cj, lo, hi, w);
     return 1;
   }
 
@@ -316,7 +321,7 @@ __device__ int plan_wave(const AttnArgs& a, PlanLds& sm, bool records, Assign* s
     for (int j = 0; j < kLanePairs; ++j) {
       const int e = st + n[j];
       if (n[j] > 0 && st < R1 && e > R0) {
-        const int v[7] = {p0 + j, T[j], window_start(T[j]), nc[j], (st > R0 ? st : R0) - st,
+        const int v[7] = {p0 + j, T[j], tws[j], nc[j], (st > R0 ? st : R0) - st,
                           (e < R1 ? e : R1) - st, bs + w - range_of(st, total, nr)};
         if (put && ord < kMaxSeg) put_record(sm, ord, v[0], v[1], v[2], v[3], v[4], v[5], v[6]);
         if (put && ord == kMaxSeg - 1) {  // more segments follow only if this one ends inside
@@ -359,7 +364,8 @@ __device__ int plan_block(const AttnArgs& a, PlanLds& sm) {
   const int t = threadIdx.x, w = blockIdx.x;
   const int per_t = (P + kThreads - 1) / kThreads;  // <= kPairsPerThread
   const int p0 = t * per_t;
-  int nreg[kPairsPerThread], treg[kPairsPerThread], creg[kPairsPerThread];
+  int nreg[kPairsPerThread], treg[kPairsPerThread], twreg[kPairsPerThread],
+      creg[kPairsPerThread];
   int mine = 0;
 #pragma unroll
   for (int j = 0; j < kPairsPerThread; ++j) {
@@ -368,6 +374,7 @@ __device__ int plan_block(const AttnArgs& a, PlanLds& sm) {
     if (j < per_t && p < P) L = pair_list<DENSE>(a, p);
     nreg[j] = L.n;
     treg[j] = L.T;
+    twreg[j] = L.tw;
     creg[j] = L.ncache;
     mine += L.n;
   }
@@ -411,7 +418,7 @@ __device__ int plan_block(const AttnArgs& a, PlanLds& sm) {
         const int slot = bs + w - range_of(st, total, nr);
         if (ord < kMaxSeg)
           put_record(sm, ord, p0 + j, treg[j],
-                     DENSE ? 0 : (treg[j] - a.window > 0 ? treg[j] - a.window : 0), creg[j],
+                     twreg[j], creg[j],
                      (st > R0 ? st : R0) - st, (e < R1 ? e : R1) - st, slot);
         if (ord == kMaxSeg - 1) {  // more segments follow only if this one ends inside
           sm.next_p = p0 + j + 1;
@@ -505,6 +512,15 @@ __device__ int plan_work(const AttnArgs& a, PlanLds& sm, bool records, Assign* s
   return nseg;
 }
 
+// Slots of [tw, T) in logical block lb (0 when the block holds none of them:
+// a block planned ahead of the current length).
+__device__ __forceinline__ uint32_t window_mask(int lb, int tw, int T) {
+  const int b0 = lb << 4;
+  const int from = (tw > b0 ? tw : b0) - b0;
+  const int to = (T < b0 + kBlock ? T : b0 + kBlock) - b0;
+  return to > from ? ((1u << to) - 1u) & ~((1u << from) - 1u) : 0u;
+}
+
 // Entry j of the pair's list -> physical block and slot mask ((0, 0) when j
 // is -1 or the block id is out of range).
 template <bool DENSE>
@@ -522,11 +538,8 @@ __device__ __forceinline__ void resolve_entry(const AttnArgs& a, const Assign& a
   } else {
     // window block: slots of [tw, T) in logical block lb
     const int lb = (as.tw >> 4) + (j - as.ncache);
-    const int b0 = lb << 4;
-    const int from = (as.tw > b0 ? as.tw : b0) - b0;
-    const int to = (as.T < b0 + kBlock ? as.T : b0 + kBlock) - b0;
-    blk = a.block_table[static_cast<size_t>(b) * a.max_blocks + lb];
-    m = ((1u << to) - 1u) & ~((1u << from) - 1u);
+    m = window_mask(lb, as.tw, as.T);
+    blk = m ? a.block_table[static_cast<size_t>(b) * a.max_blocks + lb] : -1;
   }
   if (blk < 0 || blk >= a.num_blocks) return;
   *pb = blk;
@@ -623,17 +636,45 @@ struct Chunk {
 // is fetched anyway), and its logit is replaced by -inf; value slots outside
 // the set are cleared before use (a value tile is read whole: each of its
 // 32-byte dimension rows holds all 16 slots).
+// The segment a chunk belongs to: its KV head, and for entries taken from a
+// segment record its sequence, window start and current length.
+struct SegCtx {
+  int g, b, tw, T;
+};
+
+// Entry `idx` of the wave's lane-held entries (scalar). An entry from a
+// segment record may be a window entry: its slots follow the current length
+// and a block not yet cached at the boundary is looked up in the block table.
+__device__ __forceinline__ void chunk_entry(const AttnArgs& a, const SegCtx& sc, bool from_rec,
+                                            int pb_l, uint32_t msk_l, int idx, int* pb,
+                                            uint32_t* msk) {
+  int p = __builtin_amdgcn_readlane(pb_l, idx);
+  uint32_t w = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(msk_l), idx));
+  if (from_rec && (w & kWindowEntry)) {  // uniform
+    const int lb = static_cast<int>(w & ~kWindowEntry);
+    w = window_mask(lb, sc.tw, sc.T);
+    if (p == -1 && w) p = a.block_table[static_cast<size_t>(sc.b) * a.max_blocks + lb];
+    if (p < 0 || p >= a.num_blocks) {
+      p = 0;
+      w = 0u;
+    }
+  }
+  *pb = p;
+  *msk = w & 0xffffu;
+}
+
 template <int D, int NBW>
-__device__ __forceinline__ void load_chunk(const AttnArgs& a, int g, int c, int pb_l,
-                                           uint32_t msk_l, Chunk<D, NBW>& ch) {
+__device__ __forceinline__ void load_chunk(const AttnArgs& a, const SegCtx& sc, bool from_rec,
+                                           int c, int pb_l, uint32_t msk_l, Chunk<D, NBW>& ch) {
   constexpr int KS = D / 32, NT = D / 16;
   const int lane = threadIdx.x & 63, l16 = lane & 15, lg = lane >> 4;
+  const int g = sc.g;
   const uint16_t* kpool = static_cast<const uint16_t*>(a.k_pool);
   const uint16_t* vpool = static_cast<const uint16_t*>(a.v_pool);
-  const int pb0 = __builtin_amdgcn_readlane(pb_l, c * 2);
-  const int pb1 = __builtin_amdgcn_readlane(pb_l, c * 2 + 1);
-  const uint32_t m0 = __builtin_amdgcn_readlane(static_cast<int>(msk_l), c * 2);
-  const uint32_t m1 = __builtin_amdgcn_readlane(static_cast<int>(msk_l), c * 2 + 1);
+  int pb0, pb1;
+  uint32_t m0, m1;
+  chunk_entry(a, sc, from_rec, pb_l, msk_l, c * 2, &pb0, &m0);
+  chunk_entry(a, sc, from_rec, pb_l, msk_l, c * 2 + 1, &pb1, &m1);
   ch.msk[0] = m0;
   ch.msk[1] = m1;
   // keys: row l16 of product hf is block l16 >> 3
@@ -801,7 +842,7 @@ __device__ __forceinline__ void load_q(const AttnArgs& a, int p, bf16x8 (&qop)[D
 // crosses from A to B stores its A state to LDS slot 0 and starts B with
 // B's query (kept in LDS: each lane reads back what it wrote itself). Three
 // or more segments (short pairs) are taken one after the other.
-template <int G, int D, int NBW, bool DENSE>
+template <int G, int D, int NBW, bool DENSE, bool REUSE>
 __global__ void __launch_bounds__(kThreads, 2)
 attn_mfma_kernel(AttnArgs a) {
   constexpr int KS = D / 32, NT = D / 16;
@@ -816,7 +857,47 @@ attn_mfma_kernel(AttnArgs a) {
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int l16 = lane & 15;
   Assign sa, sb;
-  const int nseg = plan_work<DENSE>(a, psm, false, &sa, &sb);
+  int nseg;
+  bool from_rec = false;  // segments and entries from this workgroup's record
+  int rec_b = 0;          // first record entry of segment B
+  if constexpr (REUSE) {
+    if (blockIdx.x == 0)  // the slot bases of the records' split, for the combine kernel
+      for (int i = threadIdx.x; i <= a.B * a.Hkv; i += kThreads) a.ws_pref[i] = a.reuse_pref[i];
+    const ReuseRecord& rec = a.records[blockIdx.x];
+    const int nr = __builtin_amdgcn_readfirstlane(rec.nseg);
+    if (nr == 0) return;  // uniform
+    if (nr > 0) {
+      from_rec = true;
+      nseg = nr;
+      auto seg = [&](int s, Assign* as) {
+        const int4 x = rec.seg[s][0], y = rec.seg[s][1];
+        as->p = __builtin_amdgcn_readfirstlane(x.x);
+        as->tw = __builtin_amdgcn_readfirstlane(x.y);
+        as->ncache = __builtin_amdgcn_readfirstlane(x.z);
+        as->slot = __builtin_amdgcn_readfirstlane(x.w);
+        as->lo = __builtin_amdgcn_readfirstlane(y.x);
+        as->hi = __builtin_amdgcn_readfirstlane(y.y);
+        const int tp = __builtin_amdgcn_readfirstlane(y.w);
+        const int t = a.seq_lens[div_small(as->p, a.Hkv)];
+        as->T = t < 0 ? 0 : (t > tp ? tp : t);
+      };
+      seg(0, &sa);
+      if (nr > 1) {
+        seg(1, &sb);
+        rec_b = __builtin_amdgcn_readfirstlane(rec.seg[1][1].z);
+      }
+    } else {
+      // the record did not fit: the plan of zr_reuse_plan again, on the
+      // boundary's lengths and settings
+      a.plan_lens = a.reuse_lens;
+      a.window = __builtin_amdgcn_readfirstlane(a.reuse_meta[0]);
+      a.horizon = __builtin_amdgcn_readfirstlane(a.reuse_meta[1]);
+      a.ws_pref = a.reuse_pref;  // (workgroup 0 would publish the same bases again)
+      nseg = plan_work<DENSE>(a, psm, false, &sa, &sb);
+    }
+  } else {
+    nseg = plan_work<DENSE>(a, psm, false, &sa, &sb);
+  }
   if (nseg == 0) return;  // uniform over the workgroup
 
   if (nseg <= 2) {
@@ -826,6 +907,8 @@ attn_mfma_kernel(AttnArgs a) {
     }
     const int gA = sa.p - div_small(sa.p, a.Hkv) * a.Hkv;
     const int gB = sb.p - div_small(sb.p, a.Hkv) * a.Hkv;
+    const SegCtx xA{gA, div_small(sa.p, a.Hkv), sa.tw, sa.T};
+    const SegCtx xB{gB, div_small(sb.p, a.Hkv), sb.tw, sb.T};
     const int nA = (sa.hi - sa.lo + NBW - 1) / NBW, nB = (sb.hi - sb.lo + NBW - 1) / NBW;
     const int ntot = nA + nB;
     const int nck_all = ntot > wave ? (ntot - wave + kWaves - 1) / kWaves : 0;
@@ -848,7 +931,17 @@ attn_mfma_kernel(AttnArgs a) {
       const bool inB = k >= nA;
       Assign al = inB ? sb : sa;
       const int j = inB ? sb.lo + (k - nA) * NBW + e % NBW : sa.lo + k * NBW + e % NBW;
-      resolve_entry<DENSE>(a, al, div_small(al.p, a.Hkv), j < al.hi ? j : -1, &pb_l, &msk_l);
+      if (from_rec) {  // uniform: the record holds A's entries, then B's from rec_b
+        pb_l = 0;
+        msk_l = 0;
+        if (j < al.hi) {
+          const int2 r = a.records[blockIdx.x].ent[inB ? rec_b + j - sb.lo : j - sa.lo];
+          pb_l = r.x;
+          msk_l = static_cast<uint32_t>(r.y);
+        }
+      } else {
+        resolve_entry<DENSE>(a, al, div_small(al.p, a.Hkv), j < al.hi ? j : -1, &pb_l, &msk_l);
+      }
     };
     // the entries first: the first K/V loads wait for them, the queries are
     // needed only once those loads have returned
@@ -880,19 +973,20 @@ attn_mfma_kernel(AttnArgs a) {
         }
       };
       Chunk<D, NBW> cA, cB;
-      load_chunk<D, NBW>(a, c0 < iB ? gA : gB, 0, pb_l, msk_l, cA);
+      load_chunk<D, NBW>(a, c0 < iB ? xA : xB, from_rec, 0, pb_l, msk_l, cA);
       if (c0 == 0 && keep_b) {  // B's query to LDS once the first loads are out
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) q_b[kk][lane] = qb[kk];
       }
       for (int c = 0; c < nck; c += 2) {
         switch_at(c);
-        if (c + 1 < nck) load_chunk<D, NBW>(a, c0 + c + 1 < iB ? gA : gB, c + 1, pb_l, msk_l, cB);
+        if (c + 1 < nck)
+          load_chunk<D, NBW>(a, c0 + c + 1 < iB ? xA : xB, from_rec, c + 1, pb_l, msk_l, cB);
         compute_chunk<D, NBW>(a, cA, qop, o, stt);
         if (c + 1 < nck) {
           switch_at(c + 1);
           if (c + 2 < nck)
-            load_chunk<D, NBW>(a, c0 + c + 2 < iB ? gA : gB, c + 2, pb_l, msk_l, cA);
+            load_chunk<D, NBW>(a, c0 + c + 2 < iB ? xA : xB, from_rec, c + 2, pb_l, msk_l, cA);
           compute_chunk<D, NBW>(a, cB, qop, o, stt);
         }
       }
@@ -936,7 +1030,7 @@ attn_mfma_kernel(AttnArgs a) {
       const int nck = nck_all - c0 < CPB ? nck_all - c0 : CPB;
       for (int c = 0; c < nck; ++c) {
         Chunk<D, NBW> ch;
-        load_chunk<D, NBW>(a, g, c, pb_l, msk_l, ch);
+        load_chunk<D, NBW>(a, SegCtx{g, b, as.tw, as.T}, false, c, pb_l, msk_l, ch);
         compute_chunk<D, NBW>(a, ch, qop, o, stt);
       }
     }
@@ -956,7 +1050,7 @@ __device__ __forceinline__ float row_sum(float v) {
   return v;
 }
 
-template <typename E, int G, int D, bool DENSE>
+template <typename E, int G, int D, bool DENSE, bool REUSE>
 __global__ void __launch_bounds__(kThreads)
 attn_valu_kernel(AttnArgs a) {
   using St = typename E::storage;
@@ -1114,6 +1208,15 @@ attn_valu_kernel(AttnArgs a) {
     write_partial<G, D>(a, as.slot, red_m, red_l, red_o);
   };
 
+  if constexpr (REUSE) {  // the plan of zr_reuse_plan, on the boundary's lengths and settings
+    if (blockIdx.x == 0)  // the slot bases of that split, for the combine kernel
+      for (int i = threadIdx.x; i <= a.B * a.Hkv; i += kThreads) a.ws_pref[i] = a.reuse_pref[i];
+    __syncthreads();
+    a.ws_pref = a.reuse_pref;
+    a.plan_lens = a.reuse_lens;
+    a.window = __builtin_amdgcn_readfirstlane(a.reuse_meta[0]);
+    a.horizon = __builtin_amdgcn_readfirstlane(a.reuse_meta[1]);
+  }
   Assign sa, sb;
   const int nseg = plan_work<DENSE>(a, psm, true, &sa, &sb);
   if (nseg == 0) return;  // uniform over the workgroup
@@ -1250,6 +1353,71 @@ attn_combine_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Segment records for the attention calls between semantic boundaries (ZoomR
+// Sec. 3.4: the attended set is rebuilt only at a boundary, while the window
+// keeps growing): the split an attention call would plan on the current
+// lengths T0 with the window planned through T0 + horizon, and each
+// workgroup's segments with their list entries resolved (window entries keep
+// their logical block, their slots follow the length of each later call).
+// One workgroup per attention workgroup; a workgroup whose share has more
+// than two segments or kRecEntries entries is marked for planning in the
+// kernel. Workgroup 0 keeps the lengths and settings that planning needs
+// and publishes the slot bases the combine kernel reads.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(kThreads)
+reuse_plan_kernel(AttnArgs a) {
+  __shared__ PlanLds psm;
+  const int w = blockIdx.x, t = threadIdx.x;
+  if (w == 0) {
+    for (int b = t; b < a.B; b += kThreads) a.reuse_lens[b] = a.seq_lens[b];
+    if (t == 0) {
+      a.reuse_meta[0] = a.window;
+      a.reuse_meta[1] = a.horizon;
+    }
+  }
+  Assign sa, sb;
+  const int nseg = plan_work<false>(a, psm, true, &sa, &sb);
+  ReuseRecord& rec = a.records[w];
+  const int nA = nseg >= 1 ? sa.hi - sa.lo : 0, nB = nseg >= 2 ? sb.hi - sb.lo : 0;
+  const bool fits = nseg <= 2 && nA + nB <= kRecEntries;
+  const int cap = a.max_blocks * kBlock;
+  if (t == 0) {
+    rec.nseg = fits ? nseg : -1;
+    if (fits) {
+      for (int i = 0; i < nseg; ++i) {
+        const Assign& as = i ? sb : sa;
+        const int tp = as.T + a.horizon < cap ? as.T + a.horizon : cap;
+        rec.seg[i][0] = make_int4(as.p, as.tw, as.ncache, as.slot);
+        rec.seg[i][1] = make_int4(as.lo, as.hi, i ? nA : 0, tp);
+      }
+    }
+  }
+  if (!fits) return;
+  for (int e = t; e < nA + nB; e += kThreads) {
+    const bool inB = e >= nA;
+    const int p = inB ? sb.p : sa.p, tw = inB ? sb.tw : sa.tw, nc = inB ? sb.ncache : sa.ncache;
+    const int T0 = inB ? sb.T : sa.T;
+    const int j = inB ? sb.lo + (e - nA) : sa.lo + e;
+    int2 r;
+    if (j < nc) {
+      const int2 en = a.entries[static_cast<size_t>(p) * a.max_blocks + j];
+      const bool ok = en.x >= 0 && en.x < a.num_blocks;
+      r = ok ? make_int2(en.x, en.y & 0xffff) : make_int2(0, 0);
+    } else {
+      // a window block: cached at the boundary (its id now), or not yet (-1)
+      const int lb = (tw >> 4) + (j - nc);
+      int blk = -1;
+      if ((lb << 4) < T0) {
+        blk = a.block_table[static_cast<size_t>(div_small(p, a.Hkv)) * a.max_blocks + lb];
+        blk = blk >= 0 && blk < a.num_blocks ? blk : -2;  // -2: never read
+      }
+      r = make_int2(blk, static_cast<int>(static_cast<uint32_t>(lb) | kWindowEntry));
+    }
+    rec.ent[e] = r;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
 constexpr int kMfmaNBW = 2;
@@ -1273,6 +1441,11 @@ size_t attn_workspace(const zr_geom& gm, int nwg, void* ws, AttnArgs* a) {
   const size_t ent_b = P * static_cast<size_t>(gm.max_blocks_per_seq) * sizeof(int2);
   const size_t ml_b = up16(slots * G * sizeof(float));
   const size_t acc_b = slots * G * gm.head_dim * sizeof(float);
+  static_assert(sizeof(ReuseRecord) % 16 == 0, "records keep the regions 16-byte aligned");
+  const size_t rec_b = static_cast<size_t>(nwg) * sizeof(ReuseRecord);
+  const size_t rlen_b = up16(static_cast<size_t>(gm.batch) * sizeof(int32_t));
+  const size_t rpref_b = pref_b;
+  const size_t meta_b = 4 * sizeof(int32_t);
   if (ws && a) {
     char* c = static_cast<char*>(ws);
     a->ws_pref = reinterpret_cast<int32_t*>(c);
@@ -1286,9 +1459,17 @@ size_t attn_workspace(const zr_geom& gm, int nwg, void* ws, AttnArgs* a) {
     a->ws_l = reinterpret_cast<float*>(c);
     c += ml_b;
     a->ws_acc = reinterpret_cast<float*>(c);
+    c += acc_b;
+    a->records = reinterpret_cast<ReuseRecord*>(c);
+    c += rec_b;
+    a->reuse_lens = reinterpret_cast<int32_t*>(c);
+    c += rlen_b;
+    a->reuse_pref = reinterpret_cast<int32_t*>(c);
+    c += rpref_b;
+    a->reuse_meta = reinterpret_cast<int32_t*>(c);
     a->nwg = nwg;
   }
-  return pref_b + cnt_b + ent_b + 2 * ml_b + acc_b;
+  return pref_b + cnt_b + ent_b + 2 * ml_b + acc_b + rec_b + rlen_b + rpref_b + meta_b;
 }
 
 // What a launch runs: the attention kernel (partials into the workspace), the
@@ -1302,15 +1483,24 @@ static hipError_t launch_combine_gd(const zr_geom& gm, const AttnArgs& a, hipStr
   return hipGetLastError();
 }
 
+// Which attention kernel: sparse (lists + window), dense (every block), or
+// sparse between semantic boundaries (segment records).
+enum AttnKind { kSparse = 0, kDense = 1, kReuse = 2 };
+
 template <int G, int D>
-static hipError_t launch_mfma(const zr_geom& gm, const AttnArgs& a, bool dense, int parts,
+static hipError_t launch_mfma(const zr_geom& gm, const AttnArgs& a, int kind, int parts,
                               hipStream_t s) {
   if (parts & kAttnOnly) {
     const dim3 grid(a.nwg);
-    if (dense)
-      hipLaunchKernelGGL((attn_mfma_kernel<G, D, kMfmaNBW, true>), grid, dim3(kThreads), 0, s, a);
+    if (kind == kDense)
+      hipLaunchKernelGGL((attn_mfma_kernel<G, D, kMfmaNBW, true, false>), grid, dim3(kThreads), 0,
+                         s, a);
+    else if (kind == kReuse)
+      hipLaunchKernelGGL((attn_mfma_kernel<G, D, kMfmaNBW, false, true>), grid, dim3(kThreads), 0,
+                         s, a);
     else
-      hipLaunchKernelGGL((attn_mfma_kernel<G, D, kMfmaNBW, false>), grid, dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((attn_mfma_kernel<G, D, kMfmaNBW, false, false>), grid, dim3(kThreads),
+                         0, s, a);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
@@ -1318,14 +1508,17 @@ static hipError_t launch_mfma(const zr_geom& gm, const AttnArgs& a, bool dense, 
 }
 
 template <typename E, int G, int D>
-static hipError_t launch_valu(const zr_geom& gm, const AttnArgs& a, bool dense, int parts,
+static hipError_t launch_valu(const zr_geom& gm, const AttnArgs& a, int kind, int parts,
                               hipStream_t s) {
   if (parts & kAttnOnly) {
     const dim3 grid(a.nwg);
-    if (dense)
-      hipLaunchKernelGGL((attn_valu_kernel<E, G, D, true>), grid, dim3(kThreads), 0, s, a);
+    if (kind == kDense)
+      hipLaunchKernelGGL((attn_valu_kernel<E, G, D, true, false>), grid, dim3(kThreads), 0, s, a);
+    else if (kind == kReuse)
+      hipLaunchKernelGGL((attn_valu_kernel<E, G, D, false, true>), grid, dim3(kThreads), 0, s, a);
     else
-      hipLaunchKernelGGL((attn_valu_kernel<E, G, D, false>), grid, dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((attn_valu_kernel<E, G, D, false, false>), grid, dim3(kThreads), 0, s,
+                         a);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
@@ -1333,45 +1526,55 @@ static hipError_t launch_valu(const zr_geom& gm, const AttnArgs& a, bool dense, 
 }
 
 template <int D>
-static hipError_t launch_d(const zr_geom& gm, const AttnArgs& a, bool dense, int parts,
+static hipError_t launch_d(const zr_geom& gm, const AttnArgs& a, int kind, int parts,
                            hipStream_t s) {
   const int G = gm.n_q_heads / gm.n_kv_heads;
   if (gm.dtype == ZR_BF16) {
     switch (G) {
-      case 1: return launch_mfma<1, D>(gm, a, dense, parts, s);
-      case 2: return launch_mfma<2, D>(gm, a, dense, parts, s);
-      case 4: return launch_mfma<4, D>(gm, a, dense, parts, s);
-      case 8: return launch_mfma<8, D>(gm, a, dense, parts, s);
-      case 16: return launch_mfma<16, D>(gm, a, dense, parts, s);
+      case 1: return launch_mfma<1, D>(gm, a, kind, parts, s);
+      case 2: return launch_mfma<2, D>(gm, a, kind, parts, s);
+      case 4: return launch_mfma<4, D>(gm, a, kind, parts, s);
+      case 8: return launch_mfma<8, D>(gm, a, kind, parts, s);
+      case 16: return launch_mfma<16, D>(gm, a, kind, parts, s);
       default: return hipErrorInvalidValue;
     }
   }
   switch (G) {
-    case 1: return launch_valu<F32, 1, D>(gm, a, dense, parts, s);
-    case 2: return launch_valu<F32, 2, D>(gm, a, dense, parts, s);
-    case 4: return launch_valu<F32, 4, D>(gm, a, dense, parts, s);
-    case 8: return launch_valu<F32, 8, D>(gm, a, dense, parts, s);
+    case 1: return launch_valu<F32, 1, D>(gm, a, kind, parts, s);
+    case 2: return launch_valu<F32, 2, D>(gm, a, kind, parts, s);
+    case 4: return launch_valu<F32, 4, D>(gm, a, kind, parts, s);
+    case 8: return launch_valu<F32, 8, D>(gm, a, kind, parts, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-static hipError_t launch_parts(const zr_geom& gm, const AttnArgs& a, bool dense, int parts,
+static hipError_t launch_parts(const zr_geom& gm, const AttnArgs& a, int kind, int parts,
                                hipStream_t s) {
   if (gm.batch == 0) return hipSuccess;
-  return gm.head_dim == 128 ? launch_d<128>(gm, a, dense, parts, s)
-                            : launch_d<64>(gm, a, dense, parts, s);
+  return gm.head_dim == 128 ? launch_d<128>(gm, a, kind, parts, s)
+                            : launch_d<64>(gm, a, kind, parts, s);
 }
 
 hipError_t launch_attention(const zr_geom& gm, const AttnArgs& a, bool dense, hipStream_t s) {
-  return launch_parts(gm, a, dense, kAttnAndCombine, s);
+  return launch_parts(gm, a, dense ? kDense : kSparse, kAttnAndCombine, s);
 }
 
 hipError_t launch_attention_partials(const zr_geom& gm, const AttnArgs& a, hipStream_t s) {
-  return launch_parts(gm, a, false, kAttnOnly, s);
+  return launch_parts(gm, a, kSparse, kAttnOnly, s);
 }
 
 hipError_t launch_combine(const zr_geom& gm, const AttnArgs& a, hipStream_t s) {
-  return launch_parts(gm, a, false, kCombineOnly, s);
+  return launch_parts(gm, a, kSparse, kCombineOnly, s);
+}
+
+hipError_t launch_reuse_plan(const zr_geom& gm, const AttnArgs& a, hipStream_t s) {
+  if (gm.batch == 0) return hipSuccess;
+  hipLaunchKernelGGL(reuse_plan_kernel, dim3(a.nwg), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attention_reuse(const zr_geom& gm, const AttnArgs& a, hipStream_t s) {
+  return launch_parts(gm, a, kReuse, a.out ? kAttnAndCombine : kAttnOnly, s);
 }
 
 }  // namespace zr

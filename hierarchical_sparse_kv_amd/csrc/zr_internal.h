@@ -197,6 +197,20 @@ struct ConsArgs {
   int32_t B, Hkv, k, n_layers, c, n_total, max_per_seq;
 };
 
+// A workgroup's share of the attention between semantic boundaries, taken
+// once per boundary (zr_reuse_plan): its one or two segments and their list
+// entries. A cached entry is (physical block, slot mask); a window entry is
+// (physical block, or -1 for a block not yet cached at the boundary;
+// logical block | kWindowEntry), its slots taken from the current length.
+constexpr int kRecEntries = 192;
+constexpr uint32_t kWindowEntry = 0x80000000u;
+struct ReuseRecord {
+  int32_t nseg;       // 0: no work; 1 or 2: the segments below; -1: plan in the kernel
+  int32_t pad[3];
+  int4 seg[2][2];     // {p, tw, ncache, slot}, {lo, hi, first record entry, planned end T0 + horizon}
+  int2 ent[kRecEntries];
+};
+
 // Attention launch parameters (device pointers + sizes), passed by value.
 // Pair p = b * Hkv + g attends its counts[p] list entries entries[p][0..)
 // (sparse only) and then the blocks of its window [T - window, T) (dense:
@@ -208,6 +222,12 @@ struct AttnArgs {
   const void* v_pool;
   const int32_t* block_table;
   const int32_t* seq_lens;
+  const int32_t* plan_lens;  // [B] lengths the split is planned on (= seq_lens, or the boundary's)
+  int32_t horizon;           // window tokens planned past plan_lens (0 = none)
+  ReuseRecord* records;      // [nwg] (reuse calls)
+  int32_t* reuse_lens;       // [B] the boundary's lengths, kept by zr_reuse_plan
+  int32_t* reuse_pref;       // [P + 1] the slot bases of that split, kept by zr_reuse_plan
+  int32_t* reuse_meta;       // {window, horizon, -, -} kept by zr_reuse_plan
   const int32_t* counts;     // [P] (sparse)
   const int2* entries;       // [P][max_blocks] (sparse)
   int32_t* ws_pref;          // [P + 1]: first partial slot of each pair
@@ -287,12 +307,17 @@ int attn_workgroups(const zr_geom& g, int32_t max_attended);
 // Bytes of workspace for `nwg` workgroups; fills the AttnArgs pointers when
 // `ws` is not null. Layout (each region 16-byte aligned): ws_pref [P + 1],
 // counts [P], entries [P][max_blocks] (int2), m and l [nwg + P][G],
-// acc [nwg + P][G][D].
+// acc [nwg + P][G][D], records [nwg], reuse_lens [B], reuse_pref [P + 1],
+// reuse_meta [4].
 size_t attn_workspace(const zr_geom& g, int nwg, void* ws, AttnArgs* a);
 hipError_t launch_attention(const zr_geom& g, const AttnArgs& a, bool dense, hipStream_t s);
 // The sparse attention kernel alone (partials stay in the workspace), and the
 // combine kernel alone (the workspace's partials -> a.out).
 hipError_t launch_attention_partials(const zr_geom& g, const AttnArgs& a, hipStream_t s);
 hipError_t launch_combine(const zr_geom& g, const AttnArgs& a, hipStream_t s);
+// Segment records for the calls between semantic boundaries, and the
+// attention (+ combine when a.out is set) that reads them.
+hipError_t launch_reuse_plan(const zr_geom& g, const AttnArgs& a, hipStream_t s);
+hipError_t launch_attention_reuse(const zr_geom& g, const AttnArgs& a, hipStream_t s);
 
 }  // namespace zr

@@ -65,6 +65,10 @@ _SIGS = {
     "zr_stage_selected": (ctypes.c_int, [_G, _P, _P, _P, _P, _T, _P, ctypes.c_int32,
                                          ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_size_t,
                                          ctypes.c_int32, _P, _P, _P, ctypes.c_size_t, _P, _P]),
+    "zr_reuse_plan": (ctypes.c_int, [_G, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                     _P, ctypes.c_size_t, _P]),
+    "zr_sparse_decode_attn_reuse": (ctypes.c_int, [_G, _P, _P, _P, _P, _P, ctypes.c_float,
+                                                   ctypes.c_int32, _P, _P, ctypes.c_size_t, _P]),
     "zr_sparse_decode_attn_cached": (ctypes.c_int, [_G, _P, _P, _P, _P, _P, ctypes.c_int32,
                                                     ctypes.c_float, ctypes.c_int32, _P, _P,
                                                     ctypes.c_size_t, _P]),
@@ -166,6 +170,19 @@ def zr_stage_selected(geom, k_pool, v_pool, block_table, seq_lens, th, sel, k, w
                                    ctypes.byref(th), sel, int(k), int(window), int(max_attended),
                                    workspace, int(ws_bytes), int(stage_blocks), k_stage, v_stage,
                                    stage_workspace, int(stage_ws_bytes), dropped, stream)
+
+
+def zr_reuse_plan(geom, block_table, seq_lens, window, horizon, max_attended, workspace, ws_bytes,
+                  stream=None) -> int:
+    return lib().zr_reuse_plan(ctypes.byref(geom), block_table, seq_lens, int(window), int(horizon),
+                               int(max_attended), workspace, int(ws_bytes), stream)
+
+
+def zr_sparse_decode_attn_reuse(geom, q, k_pool, v_pool, block_table, seq_lens, scale,
+                                max_attended, out, workspace, ws_bytes, stream=None) -> int:
+    return lib().zr_sparse_decode_attn_reuse(ctypes.byref(geom), q, k_pool, v_pool, block_table,
+                                             seq_lens, float(scale), int(max_attended), out,
+                                             workspace, int(ws_bytes), stream)
 
 
 def zr_sparse_decode_attn_cached(geom, q, k_pool, v_pool, block_table, seq_lens, window, scale,
@@ -356,6 +373,26 @@ class DeviceStep:
             self.geom, _ptr(q), self.kp, self.vp, _ptr(self.block_table),
             _ptr(seq_lens), int(window), self.scale, self.max_attended, _ptr(out),
             _ptr(ws), ws.numel(), _stream()))
+
+    def reuse_plan(self, horizon, window=None, seq_lens=None):
+        """Records of the split for the steps until the next semantic
+        boundary (zr_reuse_plan) on the lists the last boundary call left."""
+        window = self.window if window is None else int(window)
+        seq_lens = self.seq_lens if seq_lens is None else seq_lens
+        check("zr_reuse_plan", zr_reuse_plan(
+            self.geom, _ptr(self.block_table), _ptr(seq_lens), window, int(horizon),
+            self.max_attended, _ptr(self.workspace), self.workspace.numel(), _stream()))
+
+    def reuse_attn(self, seq_lens=None, q=None, out=None, partials=False):
+        """Attention on the records of reuse_plan at the current lengths
+        (zr_sparse_decode_attn_reuse); partials=True: the attention pass only."""
+        seq_lens = self.seq_lens if seq_lens is None else seq_lens
+        q = self.q if q is None else q
+        out = self.out if out is None else out
+        check("zr_sparse_decode_attn_reuse", zr_sparse_decode_attn_reuse(
+            self.geom, _ptr(q), self.kp, self.vp, _ptr(self.block_table), _ptr(seq_lens),
+            self.scale, self.max_attended, None if partials else _ptr(out),
+            _ptr(self.workspace), self.workspace.numel(), _stream()))
 
     def cached_partials(self, window, seq_lens=None, q=None, workspace=None):
         """The attention pass of cached_attn alone: partial softmax states

@@ -226,6 +226,47 @@ zr_status zr_sparse_decode_attn_cached(const zr_geom* geom, const void* q, const
                                        size_t ws_bytes, void* stream);
 
 /*
+ * Attention between semantic boundaries with the work split fixed at the
+ * boundary (ZoomR Sec. 3.4 and Appendix A.3: the attended set is rebuilt
+ * only at semantic boundaries; between them the selected spans stay and the
+ * recent window grows by one token per step).
+ *
+ * zr_reuse_plan, called once after the boundary call (zr_sparse_decode_attn,
+ * zr_sparse_decode_step or zr_zoom_decode_attn) that left its block lists in
+ * `workspace`, with that call's geom, window and max_attended and the
+ * lengths T0 = seq_lens at the boundary: it splits the attention over the
+ * lists' spans and the window [T0 - window, T0 + horizon) among the
+ * attention workgroups and keeps, per workgroup, a record of its share with
+ * the list entries resolved, in `workspace`.
+ * zr_sparse_decode_attn_reuse, called at every step after that with the
+ * current lengths T (T0 <= T <= T0 + horizon) and a new query: attention over
+ * the spans and [T0 - window, T), i.e. zr_sparse_decode_attn_cached with
+ * window + (T - T0), each workgroup starting from its record rather than
+ * planning (one memory round trip instead of three before its first K/V
+ * loads). Tokens past T0 + horizon are left out. out = NULL runs the
+ * attention pass only (its partial states stay in the workspace for
+ * zr_attn_combine, called with the same geom and max_attended).
+ * Block ids of the boundary's blocks are taken when the records are made;
+ * blocks appended later are read from the block table. Another
+ * zr_sparse_decode_attn, zr_sparse_decode_step or zr_zoom_decode_attn on the
+ * workspace replaces the lists: call zr_reuse_plan again (calls that only
+ * attend, such as zr_sparse_decode_attn_cached, leave the records valid).
+ * With horizon = 0 and T = T0 the output equals zr_sparse_decode_attn_cached
+ * with `window` bit for bit.
+ * Errors: ZR_E_NULL, ZR_E_SHAPE (window, horizon, max_attended < 0; horizon
+ * above 16 * max_blocks_per_seq), ZR_E_UNSUPPORTED, ZR_E_WORKSPACE, and for
+ * zr_sparse_decode_attn_reuse those of zr_sparse_decode_attn_cached.
+ */
+zr_status zr_reuse_plan(const zr_geom* geom, const int32_t* block_table, const int32_t* seq_lens,
+                        int32_t window, int32_t horizon, int32_t max_attended, void* workspace,
+                        size_t ws_bytes, void* stream);
+zr_status zr_sparse_decode_attn_reuse(const zr_geom* geom, const void* q, const void* k_pool,
+                                      const void* v_pool, const int32_t* block_table,
+                                      const int32_t* seq_lens, float scale, int32_t max_attended,
+                                      float* out, void* workspace, size_t ws_bytes,
+                                      void* stream);
+
+/*
  * The two passes of zr_sparse_decode_attn_cached as separate calls: the
  * split-K attention and the log-sum-exp combine (ZoomR Sec. 2 eq. A computed
  * as a sum over blocks, KV-cache management page eq. 4, in pieces whose

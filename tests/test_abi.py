@@ -30,6 +30,7 @@ def test_exports_every_declared_symbol(L):
                                "zr_dense_paged_decode_attn", "zr_append_kv", "zr_summary_keys",
                                "zr_consensus", "zr_zoom_decode_attn",
                                "zr_summary_prefetch_rule", "zr_stage_selected",
+                               "zr_reuse_plan", "zr_sparse_decode_attn_reuse",
                                "zr_workspace_bytes", "zr_status_string"])
     out = subprocess.run(["nm", "-D", "--defined-only", zr.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
@@ -65,15 +66,18 @@ def test_workspace_bytes(L):
     # per workgroup -> 33 workgroups; partial slots = workgroups + pairs.
     # Regions, each 16-byte aligned: first workgroup per pair [pairs + 1],
     # list length per pair [pairs], block lists [pairs][max_blocks] (8 bytes
-    # each), m and l [slots][G], acc [slots][G][128]
+    # each), m and l [slots][G], acc [slots][G][128], then for the calls
+    # between semantic boundaries one 1616-byte segment record per workgroup,
+    # the boundary's lengths [batch] and 16 bytes of settings
     up16 = lambda x: (x + 15) // 16 * 16
     nwg = -(-4 * (-(-1000 // 16) + 2) // 8)
     slots = nwg + 4
     lists = up16(5 * 4) + up16(4 * 4) + 4 * 4 * 8
-    assert n == lists + 2 * up16(slots * 4 * 4) + slots * 4 * 128 * 4
+    reuse = lambda nwg: nwg * 1616 + up16(2 * 4) + up16(5 * 4) + 16
+    assert n == lists + 2 * up16(slots * 4 * 4) + slots * 4 * 128 * 4 + reuse(nwg)
     # the grid is capped at 512 workgroups
     big = zr.zr_workspace_bytes(g, 10 ** 6)
-    assert big == lists + 2 * up16(516 * 16) + 516 * 4 * 128 * 4
+    assert big == lists + 2 * up16(516 * 16) + 516 * 4 * 128 * 4 + reuse(512)
     assert zr.zr_workspace_bytes(_geom(head_dim=96), 10) == 0
     assert zr.zr_workspace_bytes(g, -1) == 0
     assert zr.zr_workspace_bytes(_geom(batch=1024, n_q_heads=32, n_kv_heads=8), 10) == 0
@@ -302,3 +306,24 @@ def test_stage_selected_errors(L):
     assert f(stage_ws_bytes=16) == zr.ZR_E_WORKSPACE
     assert f(geom=_geom(head_dim=96)) == zr.ZR_E_UNSUPPORTED
     assert f(geom=_geom(batch=0)) == zr.ZR_OK
+
+
+def test_reuse_errors(L):
+    g = _geom()
+    f = lambda **kw: zr.zr_reuse_plan(**dict(dict(geom=g, block_table=FAKE, seq_lens=FAKE,
+                                                  window=16, horizon=32, max_attended=100,
+                                                  workspace=FAKE, ws_bytes=1 << 20), **kw))
+    assert f(window=-1) == zr.ZR_E_SHAPE
+    assert f(horizon=-1) == zr.ZR_E_SHAPE
+    assert f(horizon=4 * 16 + 1) == zr.ZR_E_SHAPE  # more than the table can hold
+    assert f(max_attended=-1) == zr.ZR_E_SHAPE
+    assert f(block_table=None) == zr.ZR_E_NULL
+    assert f(workspace=None) == zr.ZR_E_WORKSPACE
+    assert f(geom=_geom(batch=0)) == zr.ZR_OK
+    r = lambda **kw: zr.zr_sparse_decode_attn_reuse(**dict(dict(
+        geom=g, q=FAKE, k_pool=FAKE, v_pool=FAKE, block_table=FAKE, seq_lens=FAKE, scale=0.1,
+        max_attended=100, out=FAKE, workspace=FAKE, ws_bytes=1 << 20), **kw))
+    assert r(q=None) == zr.ZR_E_NULL
+    assert r(out=FAKE + 4) == zr.ZR_E_ALIGN
+    assert r(ws_bytes=16) == zr.ZR_E_WORKSPACE
+    assert r(scale=float("inf")) == zr.ZR_E_SHAPE

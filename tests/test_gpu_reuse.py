@@ -1,0 +1,137 @@
+"""GPU parity of the attention between semantic boundaries on records made
+once per boundary (zr_reuse_plan, zr_sparse_decode_attn_reuse) against the
+CPU oracle: the selection of the boundary step, new queries, lengths growing
+past the boundary (into blocks cached after it), window start kept (ZoomR
+Sec. 3.4; the cached call's reading of the window between boundaries)."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from hierarchical_sparse_kv_amd import synth, zr
+from oracle import zr_oracle as O
+from tests import parity_helpers as P
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    zr.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _boundary(w, back, max_attended=None):
+    """A DeviceStep at lengths T0 = T - back (the boundary) with its fused step run."""
+    T0 = np.maximum(w.seq_lens - back, 0).astype(np.int32)
+    ma = int(w.seq_lens.max()) if max_attended is None else max_attended
+    st = zr.DeviceStep(w.q, w.k_pool, w.v_pool, w.block_table, T0, w.seq_ptr, w.th_start,
+                       w.th_len, w.summary_keys, w.max_per_seq, w.k, w.window, w.scale, ma)
+    st.step()
+    torch.cuda.synchronize()
+    return st, T0
+
+
+def _check_steps(w, st, T0, steps, name, gen_seed=7):
+    sel = st.sel.cpu().numpy()
+    h = P.host(w)
+    gen = torch.Generator(device="cuda").manual_seed(gen_seed)
+    for i in steps:
+        Ti = torch.as_tensor(T0 + i, dtype=torch.int32, device="cuda")
+        qi = torch.randn(w.q.shape, generator=gen, device="cuda").to(w.q.dtype)
+        st.reuse_attn(seq_lens=Ti, q=qi)
+        torch.cuda.synchronize()
+        got = st.out.cpu().numpy()
+        ref = O.sparse_decode_step(synth.to_numpy_f32(qi), h["k_pool"], h["v_pool"],
+                                   w.block_table, T0 + i, w.seq_ptr, w.th_start, w.th_len,
+                                   h["kbar"], w.k, w.window + i, w.scale, sel=sel)
+        err = float(np.max(np.abs(got - ref["out"])))
+        say(f"[gpu] {name} step {i}: max|out - oracle| = {err:.3e}")
+        assert err <= P.TOL[w.dtype], (name, i)
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
+def test_reuse_steps_match_oracle(dtype, d):
+    """Records made at T0 with horizon 40; steps T0 + i for i up to 40 with new
+    queries (the window grows past T0 into blocks appended after it)."""
+    w = synth.make_workload(1, device="cuda", overrides=dict(
+        B=3, seq_len=("uniform", 700, 1200), thought=("uniform", 8, 120), k=4, window=32,
+        dtype=dtype, d=d))
+    st, T0 = _boundary(w, 41)
+    st.reuse_plan(40)
+    _check_steps(w, st, T0, [0, 1, 9, 17, 40], f"reuse-{dtype}")
+
+
+def test_reuse_at_the_boundary_equals_the_cached_call():
+    """Horizon 0, T = T0: the records give the cached call's split, hence its
+    output bit for bit; so do the attention pass then zr_attn_combine."""
+    w = synth.make_workload(1, device="cuda")
+    st = zr.step_from_workload(w)
+    st.step()
+    st.cached_attn(w.window)
+    torch.cuda.synchronize()
+    ref = st.out.clone()
+    st.reuse_plan(0)
+    st.out.fill_(float("nan"))
+    st.reuse_attn()
+    torch.cuda.synchronize()
+    assert torch.equal(st.out, ref)
+    st.out.fill_(float("nan"))
+    st.reuse_attn(partials=True)
+    st.combine()
+    torch.cuda.synchronize()
+    assert torch.equal(st.out, ref)
+    # an attention-only call in between leaves the records valid
+    st.cached_attn(w.window + 5)
+    st.reuse_attn()
+    torch.cuda.synchronize()
+    assert torch.equal(st.out, ref)
+
+
+def test_reuse_with_workgroups_that_plan_themselves():
+    """Shares that do not fit a record plan in the kernel on the boundary's
+    lengths: many short pairs (more than two segments per workgroup) and a
+    grid sized far below the attended tokens (hundreds of entries each)."""
+    lens = [20000] + [40] * 20 + [5000]  # every T0 + step stays within the cached tokens
+    w = synth.make_workload(1, device="cuda", seq_lens=lens,
+                            overrides=dict(B=len(lens), thought=("uniform", 8, 400), k=4))
+    st, T0 = _boundary(w, 20)
+    st.reuse_plan(24)
+    _check_steps(w, st, T0, [0, 3, 20], "reuse-short-pairs")
+    w2 = synth.make_workload(1, device="cuda", overrides=dict(
+        B=2, seq_len=("fixed", 12000), thought=("uniform", 100, 400), k=8))
+    st2, T02 = _boundary(w2, 10, max_attended=1)
+    st2.reuse_plan(16)
+    _check_steps(w2, st2, T02, [0, 10], "reuse-small-grid")
+
+
+def test_reuse_graph_replays_are_bit_identical():
+    w = synth.make_workload(1, device="cuda", overrides=dict(B=4, seq_len=("fixed", 4096)))
+    st, T0 = _boundary(w, 12)
+    st.reuse_plan(16)
+    Ti = torch.as_tensor(T0 + 9, dtype=torch.int32, device="cuda")
+    st.reuse_attn(seq_lens=Ti)
+    torch.cuda.synchronize()
+    eager = st.out.clone()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            st.reuse_attn(seq_lens=Ti)
+    torch.cuda.current_stream().wait_stream(s)
+    for _ in range(3):
+        st.out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(st.out, eager)
