@@ -298,9 +298,12 @@ def main():
 
     # selection reuse (ZoomR Sec. 3.4, Appendix A.3): the attended set is
     # rebuilt at semantic boundaries, about every 35 tokens. Each layer runs
-    # its own period: a full step at T0 = T - period + 1, then cached-selection
-    # attention at T0 + i with the window grown by i. Layers rotate call by
-    # call, as in the timed steps above.
+    # its own period: a full step at T0 = T - period + 1, then attention on
+    # the kept selection at T0 + i with the window start kept (window grown by
+    # i). Two ways between boundaries: zr_sparse_decode_attn_cached (the
+    # attention plans every call), and zr_reuse_plan once after the boundary
+    # step followed by zr_sparse_decode_attn_reuse (each workgroup starts from
+    # its record). Layers rotate call by call, as in the timed steps above.
     R = max(args.period, 1)
     T_full = int(w0.seq_lens[0])
     lens_i = [torch.full((w0.B,), T_full - R + 1 + i, dtype=torch.int32, device=dev)
@@ -313,10 +316,51 @@ def main():
         else:
             steps[l].cached_attn(w0.window + i, seq_lens=lens_i[i])
 
+    def period_reuse(c):
+        l, i = c % L, (c // L) % R
+        if i == 0:
+            steps[l].step(seq_lens=lens_i[0])
+            steps[l].reuse_plan(R - 1, seq_lens=lens_i[0])
+        else:
+            steps[l].reuse_attn(seq_lens=lens_i[i])
+
     g_period = capture(period_call, L * R)
     g_period.replay()
     torch.cuda.synchronize()
     period_us = timed(g_period, L * R)
+    g_period_r = capture(period_reuse, L * R)
+    g_period_r.replay()
+    torch.cuda.synchronize()
+    period_reuse_us = timed(g_period_r, L * R)
+    # the reuse call at T0 + i equals the cached call with window W + i (same
+    # attended set; other work split, so compared within the bf16 tolerance)
+    i_chk = R - 1
+    steps[0].step(seq_lens=lens_i[0])
+    steps[0].reuse_plan(R - 1, seq_lens=lens_i[0])
+    steps[0].cached_attn(w0.window + i_chk, seq_lens=lens_i[i_chk])
+    torch.cuda.synchronize()
+    ref_c = steps[0].out.clone()
+    steps[0].reuse_attn(seq_lens=lens_i[i_chk])
+    torch.cuda.synchronize()
+    reuse_diff = float(torch.max(torch.abs(ref_c - steps[0].out)).item())
+    assert reuse_diff <= 2e-3, f"reuse call differs from the cached call: {reuse_diff}"
+    # the attention kernel between boundaries alone: records of horizon 0 at
+    # the lengths of the timed steps (the attended set of the roofline figure)
+    for st in steps:
+        st.step()
+        st.reuse_plan(0)
+    torch.cuda.synchronize()
+    g_reuse_part = capture(lambda i: steps[i % L].reuse_attn(partials=True), args.steps)
+    g_reuse_part.replay()
+    reuse_kernel_us = timed(g_reuse_part, args.steps)
+    reuse_achieved = bytes_per_launch / (reuse_kernel_us * 1e-6) / 1e9
+    g_reuse_call = capture(lambda i: steps[i % L].reuse_attn(), args.steps)
+    g_reuse_call.replay()
+    reuse_call_us = timed(g_reuse_call, args.steps)
+    g_rplan = capture(lambda i: steps[i % L].reuse_plan(R - 1), L)
+    g_rplan.replay()
+    rplan_us = timed(g_rplan, L)
+    del g_reuse_part, g_reuse_call, g_rplan, g_period_r
 
     # append path: one token per sequence into a paged cache with on-demand
     # blocks (zr_append_kv), and mean summary keys of one completed thought per
@@ -368,12 +412,13 @@ def main():
             zs[0].zoom_attn(ss, sl, votes, cons, cz, npz)
             for st in zs[1:]:
                 st.cached_attn(wz.window, workspace=zs[0].workspace)
+            zs[0].reuse_plan(R - 1)  # records for the steps until the next boundary
 
         g_bound = capture(boundary, 1)
         g_bound.replay()
         torch.cuda.synchronize()
         bound_us = timed(g_bound, L)
-        g_between = capture(lambda i: zs[i % L].cached_attn(wz.window, workspace=zs[0].workspace),
+        g_between = capture(lambda i: zs[i % L].reuse_attn(workspace=zs[0].workspace),
                             args.steps)
         between_us = timed(g_between, args.steps)
         v_h, c_h = votes.cpu().numpy(), cons.cpu().numpy()
@@ -595,6 +640,15 @@ def main():
                                "on the block lists of zr_sparse_decode_attn)",
                      "avg_launch_us": round(kernel_us, 3),
                      "algorithmic_bytes_per_launch": int(bytes_per_launch)},
+        "roofline_between_boundaries": {
+            "bound": "hbm", "achieved": round(reuse_achieved, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(reuse_achieved / HBM_PEAK_GBS, 4),
+            "kernel": "attn_mfma_kernel on segment records (zr_sparse_decode_attn_reuse with "
+                      "out = NULL, records of zr_reuse_plan at the timed steps' lengths)",
+            "avg_launch_us": round(reuse_kernel_us, 3),
+            "algorithmic_bytes_per_launch": int(bytes_per_launch),
+            "reuse_call_us": round(reuse_call_us, 3),
+            "reuse_plan_us": round(rplan_us, 3)},
         "attn_and_combine": {"call": "zr_sparse_decode_attn_cached (attn_mfma_kernel + "
                                      "attn_combine_kernel)",
                              "avg_launch_us": round(gather_us, 3), "gbs": round(call_gbs, 1),
@@ -604,8 +658,12 @@ def main():
         "step_as_three_calls_us": round(calls_us, 3),
         "tokens_per_s": round(steps_per_s * w0.B, 1),
         "latency": latency,
-        "selection_reuse": {"period_steps": R, "us_per_step": round(period_us, 3),
-                            "steps_per_s": round(1e6 / period_us, 1)},
+        "selection_reuse": {"period_steps": R,
+                            "us_per_step": round(period_reuse_us, 3),
+                            "steps_per_s": round(1e6 / period_reuse_us, 1),
+                            "between_boundaries": "zr_reuse_plan + zr_sparse_decode_attn_reuse",
+                            "cached_calls_us_per_step": round(period_us, 3),
+                            "max_abs_diff_reuse_vs_cached": reuse_diff},
         "speedup_vs_dense_attention": round(dense_us / attn_us, 3),
         "other_workloads": others,
         "zoomr_consensus": zoom,

@@ -374,25 +374,30 @@ class DeviceStep:
             _ptr(seq_lens), int(window), self.scale, self.max_attended, _ptr(out),
             _ptr(ws), ws.numel(), _stream()))
 
-    def reuse_plan(self, horizon, window=None, seq_lens=None):
+    def reuse_plan(self, horizon, window=None, seq_lens=None, workspace=None):
         """Records of the split for the steps until the next semantic
-        boundary (zr_reuse_plan) on the lists the last boundary call left."""
+        boundary (zr_reuse_plan) on the lists the last boundary call left in
+        `workspace` (default: this step's)."""
         window = self.window if window is None else int(window)
         seq_lens = self.seq_lens if seq_lens is None else seq_lens
+        ws = self.workspace if workspace is None else workspace
         check("zr_reuse_plan", zr_reuse_plan(
             self.geom, _ptr(self.block_table), _ptr(seq_lens), window, int(horizon),
-            self.max_attended, _ptr(self.workspace), self.workspace.numel(), _stream()))
+            self.max_attended, _ptr(ws), ws.numel(), _stream()))
 
-    def reuse_attn(self, seq_lens=None, q=None, out=None, partials=False):
+    def reuse_attn(self, seq_lens=None, q=None, out=None, partials=False, workspace=None):
         """Attention on the records of reuse_plan at the current lengths
-        (zr_sparse_decode_attn_reuse); partials=True: the attention pass only."""
+        (zr_sparse_decode_attn_reuse); partials=True: the attention pass only.
+        `workspace`: another step's (same geometry), e.g. the
+        multi-granularity set that every layer shares."""
         seq_lens = self.seq_lens if seq_lens is None else seq_lens
         q = self.q if q is None else q
         out = self.out if out is None else out
+        ws = self.workspace if workspace is None else workspace
         check("zr_sparse_decode_attn_reuse", zr_sparse_decode_attn_reuse(
             self.geom, _ptr(q), self.kp, self.vp, _ptr(self.block_table), _ptr(seq_lens),
             self.scale, self.max_attended, None if partials else _ptr(out),
-            _ptr(self.workspace), self.workspace.numel(), _stream()))
+            _ptr(ws), ws.numel(), _stream()))
 
     def cached_partials(self, window, seq_lens=None, q=None, workspace=None):
         """The attention pass of cached_attn alone: partial softmax states

@@ -138,6 +138,17 @@ def test_zoom_attention_parity_and_cached_steps():
                                  w.window + i, w.scale)
         err = np.max(np.abs(st.out.cpu().numpy() - ref["out"]))
         assert err <= P.TOL[w.dtype], i
+    # the same steps on records made once at the boundary (zr_reuse_plan)
+    st.reuse_plan(4, seq_lens=_dev(T0))
+    for i in (0, 2, 4):
+        st.reuse_attn(seq_lens=_dev(T0 + i))
+        torch.cuda.synchronize()
+        ref = O.zoom_decode_step(h["q"], h["k_pool"], h["v_pool"], w.block_table, T0 + i,
+                                 w.seq_ptr, w.th_start, w.th_len, ss, sl, v_ref, c_ref, n_prompt,
+                                 w.window + i, w.scale)
+        err = np.max(np.abs(st.out.cpu().numpy() - ref["out"]))
+        say(f"[gpu] zoom set on records, step {i}: max err {err:.3e}")
+        assert err <= P.TOL[w.dtype], i
 
 
 def test_zoom_pipeline_two_layers():
