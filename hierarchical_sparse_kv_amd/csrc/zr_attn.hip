@@ -44,6 +44,12 @@
 // through LDS and each lane accumulates the values of its own dimensions.
 //
 // Exponentials are base 2 with the scale folded in (exp(x) = 2^(x log2 e)).
+//
+// The matrix-core kernel reads each key and value tile once per call, with
+// one 16-byte load per lane and line, so it loads them with the non-temporal
+// hint (measured: 5 to 10 % less time per call on the 16K x 8, 64K x 4 and
+// ragged workloads). The fp32 kernel keeps plain loads: it reads a value
+// column as four 16-byte pieces of one line, and there the hint cost 8 %.
 #include <math.h>
 
 #include <type_traits>
@@ -691,7 +697,7 @@ __device__ __forceinline__ void load_chunk(const AttnArgs& a, const SegCtx& sc, 
       const uint16_t* krow = kpool + (tile * kBlock + kslot) * D + 8 * lg;
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk)
-        ch.k[hf][kk] = *reinterpret_cast<const bf16x8*>(krow + 32 * kk);
+        ch.k[hf][kk] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(krow + 32 * kk));
     }
   }
   // values: lane group lg reads block lg >> 1, slots 8 (lg & 1) .. +7
@@ -701,7 +707,7 @@ __device__ __forceinline__ void load_chunk(const AttnArgs& a, const SegCtx& sc, 
     const uint16_t* vcol = vpool + tile * (D * kBlock) + l16 * kBlock + 8 * (lg & 1);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
-      ch.v[nt] = *reinterpret_cast<const bf16x8*>(vcol + nt * 16 * kBlock);
+      ch.v[nt] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(vcol + nt * 16 * kBlock));
   }
 }
 
