@@ -27,15 +27,21 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 
-# HBM bytes per launch of the attention kernel on this workload, from hardware
-# counters (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE, each scaled by the
-# counter's reading for a known-size copy).
+# Figures of the attention kernel on this workload taken with rocprofv3 on the
+# same bench (the summaries under profiles/ name the commands):
+# - HBM bytes per launch from hardware counters (--pmc FETCH_SIZE, then
+#   WRITE_SIZE, each scaled by the counter's reading for a known-size copy);
+# - average kernel durations from the kernel trace (--kernel-trace): the runs
+#   of back-to-back launches that the roofline figures time with HIP events.
 # Valid only for the kernel sources they were taken with: reported as null as
 # soon as any of these files changes.
 TRAFFIC_SOURCES = ("zr_internal.h", "zr_pair.hip", "zr_attn.hip")
 TRAFFIC = {
-    "sources_sha256": "3142d05632ddcc31876cd6c03b66266c54db52e00f017247880b8d5639bde3fb",
-    "bytes_per_call": 79654128,  # 78,566,229 fetched + 1,087,899 written
+    "sources_sha256": "a36f58980b0cad9a8aaa12ffe4c431f8a2ad8f85fe66bf9825ee97f306715cfb",
+    "bytes_per_call": 80519277,  # 79,432,828 fetched + 1,086,449 written
+    "bytes_per_call_reuse": 81290701,  # 80,202,089 fetched + 1,088,612 written
+    "rocprof_kernel_us": 19.86,  # 200 launches of the sparse attention kernel
+    "rocprof_kernel_us_reuse": 18.85,  # 401 launches of the kernel on segment records
 }
 
 
@@ -45,6 +51,24 @@ def sources_sha256():
         with open(os.path.join(ROOT, "hierarchical_sparse_kv_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
+
+
+def profiled(key):
+    """A TRAFFIC figure, or None once the kernel sources have changed."""
+    return TRAFFIC[key] if TRAFFIC["sources_sha256"] == sources_sha256() else None
+
+
+def rocprof_figure(key, bytes_per_launch):
+    """The roofline figure on the profiler's average kernel duration (no
+    launch gaps), or None once the kernel sources have changed."""
+    us = profiled(key)
+    if us is None:
+        return None
+    gbs = bytes_per_launch / (us * 1e-6) / 1e9
+    return {"avg_kernel_us": us, "achieved": round(gbs, 1),
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "source": "rocprofv3 --kernel-trace"}
+
+
 METRIC = "decode steps/s and effective KV GB/s (% of HBM peak), 16K tokens, batch 8"
 
 
@@ -633,13 +657,12 @@ def main():
                    "layers_rotated": L, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": (TRAFFIC["bytes_per_call"]
-                                 if TRAFFIC and TRAFFIC["sources_sha256"] == sources_sha256()
-                                 else None),
+                     "traffic": profiled("bytes_per_call"),
                      "kernel": "attn_mfma_kernel (one zr_sparse_decode_attn_partials call "
                                "on the block lists of zr_sparse_decode_attn)",
                      "avg_launch_us": round(kernel_us, 3),
-                     "algorithmic_bytes_per_launch": int(bytes_per_launch)},
+                     "algorithmic_bytes_per_launch": int(bytes_per_launch),
+                     "rocprof": rocprof_figure("rocprof_kernel_us", bytes_per_launch)},
         "roofline_between_boundaries": {
             "bound": "hbm", "achieved": round(reuse_achieved, 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(reuse_achieved / HBM_PEAK_GBS, 4),
@@ -647,6 +670,8 @@ def main():
                       "out = NULL, records of zr_reuse_plan at the timed steps' lengths)",
             "avg_launch_us": round(reuse_kernel_us, 3),
             "algorithmic_bytes_per_launch": int(bytes_per_launch),
+            "traffic": profiled("bytes_per_call_reuse"),
+            "rocprof": rocprof_figure("rocprof_kernel_us_reuse", bytes_per_launch),
             "reuse_call_us": round(reuse_call_us, 3),
             "reuse_plan_us": round(rplan_us, 3)},
         "attn_and_combine": {"call": "zr_sparse_decode_attn_cached (attn_mfma_kernel + "
