@@ -242,8 +242,9 @@ zr_status zr_sparse_decode_attn_cached(const zr_geom* geom, const void* q, const
  * current lengths T (T0 <= T <= T0 + horizon) and a new query: attention over
  * the spans and [T0 - window, T), i.e. zr_sparse_decode_attn_cached with
  * window + (T - T0), each workgroup starting from its record rather than
- * planning (one memory round trip instead of three before its first K/V
- * loads). Tokens past T0 + horizon are left out. out = NULL runs the
+ * planning: before its first K/V loads it reads the record's header and then
+ * the entries in it, instead of every pair's list length, the plan and then
+ * the list entries. Tokens past T0 + horizon are left out. out = NULL runs the
  * attention pass only (its partial states stay in the workspace for
  * zr_attn_combine, called with the same geom and max_attended).
  * Block ids of the boundary's blocks are taken when the records are made;
