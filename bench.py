@@ -496,15 +496,22 @@ def main():
             g_o = capture(lambda i: ss_[i % 4].cached_attn(ws_[i % 4].window), 40)
             g_o.replay()
             us_o = timed(g_o, 40)
+            g_k = capture(lambda i: ss_[i % 4].cached_partials(ws_[i % 4].window), 40)
+            g_k.replay()
+            us_k = timed(g_k, 40)
             g_s = capture(lambda i: ss_[i % 4].step(), 40)
             g_s.replay()
             us_s = timed(g_s, 40)
             gbs = float(np.mean(byts)) / (us_o * 1e-6) / 1e9
+            gbs_k = float(np.mean(byts)) / (us_k * 1e-6) / 1e9
             others[ws_[0].name] = {"workload": label, "gathered_bytes": int(np.mean(byts)),
                                    "attn_combine_us": round(us_o, 2), "gbs": round(gbs, 1),
                                    "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                   "attn_kernel_us": round(us_k, 2),
+                                   "attn_kernel_gbs": round(gbs_k, 1),
+                                   "attn_kernel_frac": round(gbs_k / HBM_PEAK_GBS, 4),
                                    "step_us": round(us_s, 2)}
-            del ws_, ss_, g_o, g_s
+            del ws_, ss_, g_o, g_k, g_s
             torch.cuda.empty_cache()
 
     # host-offloaded cache (ZoomR Sec. 3.4, "Decoding Stage"): pools in pinned
