@@ -1247,7 +1247,7 @@ attn_valu_kernel(AttnArgs a) {
 // of partials with independent 16-byte loads (slot indices clamped, so the
 // loads need no branches), merging tiles online.
 // ---------------------------------------------------------------------------
-constexpr int kCombineTile = 8;
+constexpr int kCombineThreads = 512;
 
 // Log-sum-exp merge state of one item (4 dims of one head).
 struct MergeState {
@@ -1255,18 +1255,18 @@ struct MergeState {
   float4 A;
 };
 
-// Merge slots [c0, s1) of one item, tiles of kCombineTile taken `stride`
+// Merge slots [c0, s1) of one item, tiles of TILE slots taken `stride`
 // slots apart, into st.
-template <int G, int D>
+template <int G, int D, int TILE>
 __device__ __forceinline__ void merge_slots(const AttnArgs& a, int h, int e4, int c0, int s1,
                                             int stride, MergeState& st) {
   constexpr int D4 = D / 4;
   const float4* acc4 = reinterpret_cast<const float4*>(a.ws_acc);
   for (; c0 < s1; c0 += stride) {
-    float ms[kCombineTile], ls[kCombineTile];
-    float4 vs[kCombineTile];
+    float ms[TILE], ls[TILE];
+    float4 vs[TILE];
 #pragma unroll
-    for (int u = 0; u < kCombineTile; ++u) {
+    for (int u = 0; u < TILE; ++u) {
       const size_t s = static_cast<size_t>(c0 + u < s1 ? c0 + u : s1 - 1);
       ms[u] = a.ws_m[s * G + h];
       ls[u] = a.ws_l[s * G + h];
@@ -1275,7 +1275,7 @@ __device__ __forceinline__ void merge_slots(const AttnArgs& a, int h, int e4, in
     }
     float mt = st.M;
 #pragma unroll
-    for (int u = 0; u < kCombineTile; ++u) mt = fmaxf(mt, ms[u]);
+    for (int u = 0; u < TILE; ++u) mt = fmaxf(mt, ms[u]);
     if (mt == kNegInf) continue;
     const float alpha = st.M == kNegInf ? 0.f : exp2f(st.M - mt);
     st.L *= alpha;
@@ -1284,7 +1284,7 @@ __device__ __forceinline__ void merge_slots(const AttnArgs& a, int h, int e4, in
     st.A.z *= alpha;
     st.A.w *= alpha;
 #pragma unroll
-    for (int u = 0; u < kCombineTile; ++u) {
+    for (int u = 0; u < TILE; ++u) {
       const float w = ms[u] != kNegInf ? exp2f(ms[u] - mt) : 0.f;
       st.L = fmaf(ls[u], w, st.L);
       st.A.x = fmaf(vs[u].x, w, st.A.x);
@@ -1298,12 +1298,21 @@ __device__ __forceinline__ void merge_slots(const AttnArgs& a, int h, int e4, in
 
 // One workgroup per pair. When a pair's items (G heads x D/4) leave threads
 // over, NGRP groups of threads take the tiles of partials in turn (so up to
-// NGRP tiles are loaded at once) and merge their states through LDS.
+// NGRP tiles are loaded at once) and merge their states through LDS. TILE
+// (slots per tile) is chosen per launch: the smaller tile when one round of
+// NGRP tiles still covers a pair's average slot count (fewer loads per
+// thread), else the larger one (fewer rounds).
 template <int G, int D>
-__global__ void __launch_bounds__(kThreads)
+constexpr int combine_groups() {
+  return G * (D / 4) < kCombineThreads ? kCombineThreads / (G * (D / 4)) : 1;
+}
+
+template <int G, int D, int TILE>
+__global__ void __launch_bounds__(kCombineThreads)
 attn_combine_kernel(AttnArgs a) {
-  constexpr int D4 = D / 4, ITEMS = G * D4, PER = (ITEMS + kThreads - 1) / kThreads;
-  constexpr int NGRP = ITEMS < kThreads ? kThreads / ITEMS : 1;
+  constexpr int D4 = D / 4, ITEMS = G * D4;
+  constexpr int PER = (ITEMS + kCombineThreads - 1) / kCombineThreads;
+  constexpr int NGRP = combine_groups<G, D>();
   __shared__ MergeState sh[NGRP > 1 ? (NGRP - 1) * ITEMS : 1];
   const int g = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
   const int p = b * a.Hkv + g;
@@ -1324,8 +1333,8 @@ attn_combine_kernel(AttnArgs a) {
     const int grp = t / ITEMS, idx = t - grp * ITEMS;
     const int h = idx / D4, e4 = idx % D4;
     MergeState st{kNegInf, 0.f, make_float4(0.f, 0.f, 0.f, 0.f)};
-    merge_slots<G, D>(a, h, e4, s0 + grp * kCombineTile, s1, NGRP * kCombineTile, st);
-    if (s1 - s0 <= kCombineTile) {  // one tile: group 0 holds everything (uniform)
+    merge_slots<G, D, TILE>(a, h, e4, s0 + grp * TILE, s1, NGRP * TILE, st);
+    if (s1 - s0 <= TILE) {  // one tile: group 0 holds everything (uniform)
       if (grp == 0) finish(idx, st);
       return;
     }
@@ -1349,10 +1358,10 @@ attn_combine_kernel(AttnArgs a) {
   } else {
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
-      const int idx = t + j * kThreads;
+      const int idx = t + j * kCombineThreads;
       if (idx >= ITEMS) continue;
       MergeState st{kNegInf, 0.f, make_float4(0.f, 0.f, 0.f, 0.f)};
-      merge_slots<G, D>(a, idx / D4, idx % D4, s0, s1, kCombineTile, st);
+      merge_slots<G, D, TILE>(a, idx / D4, idx % D4, s0, s1, TILE, st);
       finish(idx, st);
     }
   }
@@ -1484,8 +1493,14 @@ enum AttnParts { kAttnOnly = 1, kCombineOnly = 2, kAttnAndCombine = 3 };
 
 template <int G, int D>
 static hipError_t launch_combine_gd(const zr_geom& gm, const AttnArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((attn_combine_kernel<G, D>), dim3(gm.n_kv_heads, gm.batch), dim3(kThreads),
-                     0, s, a);
+  // a pair's partial slots: about nwg / P, plus one where ranges meet
+  const int pairs = gm.batch * gm.n_kv_heads;
+  const int per_pair = (a.nwg + 2 * pairs - 1) / pairs;
+  const dim3 grid(gm.n_kv_heads, gm.batch);
+  if (per_pair <= combine_groups<G, D>() * 4)
+    hipLaunchKernelGGL((attn_combine_kernel<G, D, 4>), grid, dim3(kCombineThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_combine_kernel<G, D, 8>), grid, dim3(kCombineThreads), 0, s, a);
   return hipGetLastError();
 }
 
