@@ -588,6 +588,7 @@ ZR_API zr_status zr_stage_selected(const zr_geom* geom, const void* k_pool, cons
   ga.s_counts = const_cast<int32_t*>(sa.counts);  // written by the stage kernel
   ga.s_entries = const_cast<int2*>(sa.entries);
   ga.dropped = dropped;
+  ga.B = geom->batch;
   ga.Hkv = geom->n_kv_heads;
   ga.max_blocks = geom->max_blocks_per_seq;
   ga.num_blocks = geom->num_blocks;

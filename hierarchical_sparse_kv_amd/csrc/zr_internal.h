@@ -280,8 +280,9 @@ struct StageArgs {
   int32_t* s_counts;          // [P] staged list lengths
   int2* s_entries;            // [P][max_blocks] staged lists
   int32_t* dropped;           // [P] entries that did not fit
-  int32_t Hkv, max_blocks, num_blocks, window, stage_blocks;
+  int32_t B, Hkv, max_blocks, num_blocks, window, stage_blocks;
   int32_t lg_pieces;          // log2(16-byte pieces per tile): tile = 16 * D * element bytes
+  int32_t item_chunks;        // work items per pair (set by the launcher)
 };
 
 // Host-side launchers (defined next to their kernels).
