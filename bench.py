@@ -37,11 +37,11 @@ HBM_PEAK_GBS = 8000.0
 # soon as any of these files changes.
 TRAFFIC_SOURCES = ("zr_internal.h", "zr_pair.hip", "zr_attn.hip")
 TRAFFIC = {
-    "sources_sha256": "a36f58980b0cad9a8aaa12ffe4c431f8a2ad8f85fe66bf9825ee97f306715cfb",
-    "bytes_per_call": 80519277,  # 79,432,828 fetched + 1,086,449 written
-    "bytes_per_call_reuse": 81290701,  # 80,202,089 fetched + 1,088,612 written
-    "rocprof_kernel_us": 19.86,  # 200 launches of the sparse attention kernel
-    "rocprof_kernel_us_reuse": 18.85,  # 401 launches of the kernel on segment records
+    "sources_sha256": "42a5569665e3543fb4c99cd94fac2a2b199f825b345979d2044064ce17aaba9f",
+    "bytes_per_call": 80499406,  # 79,412,958 fetched + 1,086,448 written
+    "bytes_per_call_reuse": 80524242,  # 79,435,633 fetched + 1,088,610 written
+    "rocprof_kernel_us": 19.91,  # 200 launches of the sparse attention kernel
+    "rocprof_kernel_us_reuse": 18.96,  # 401 launches of the kernel on segment records
 }
 
 
