@@ -120,6 +120,7 @@ void fill_plan(const zr_geom& g, const zr_thoughts& th, int k, int window,
   pa->block_table = block_table;
   pa->counts = const_cast<int32_t*>(a.counts);
   pa->entries = const_cast<int2*>(a.entries);
+  pa->list_tw = const_cast<int32_t*>(a.list_tw);
 }
 
 }  // namespace
@@ -586,6 +587,7 @@ ZR_API zr_status zr_stage_selected(const zr_geom* geom, const void* k_pool, cons
   ga.k_stage = k_stage;
   ga.v_stage = v_stage;
   ga.s_counts = const_cast<int32_t*>(sa.counts);  // written by the stage kernel
+  ga.s_list_tw = const_cast<int32_t*>(sa.list_tw);
   ga.s_entries = const_cast<int2*>(sa.entries);
   ga.dropped = dropped;
   ga.B = geom->batch;

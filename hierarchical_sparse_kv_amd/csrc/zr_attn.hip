@@ -121,6 +121,10 @@ __device__ __forceinline__ PairList pair_list(const AttnArgs& a, int p) {
   if (!DENSE) {
     const int c = a.counts[p];
     r.ncache = c < 0 ? 0 : (c > a.max_blocks ? a.max_blocks : c);
+    // the window starts no earlier than where the lists' spans stop, so a
+    // token is never attended twice
+    const int t0 = a.list_tw[p];
+    r.tw = r.tw > t0 ? r.tw : (t0 < Tp ? t0 : Tp);
   }
   const int wb = Tp > r.tw ? ((Tp - 1) >> 4) - (r.tw >> 4) + 1 : 0;
   r.n = r.ncache + wb;
@@ -1453,6 +1457,7 @@ size_t attn_workspace(const zr_geom& gm, int nwg, void* ws, AttnArgs* a) {
   auto up16 = [](size_t x) { return (x + 15) & ~static_cast<size_t>(15); };
   const size_t pref_b = up16((P + 1) * sizeof(int32_t));
   const size_t cnt_b = up16(P * sizeof(int32_t));
+  const size_t ltw_b = cnt_b;
   const size_t ent_b = P * static_cast<size_t>(gm.max_blocks_per_seq) * sizeof(int2);
   const size_t ml_b = up16(slots * G * sizeof(float));
   const size_t acc_b = slots * G * gm.head_dim * sizeof(float);
@@ -1467,6 +1472,8 @@ size_t attn_workspace(const zr_geom& gm, int nwg, void* ws, AttnArgs* a) {
     c += pref_b;
     a->counts = reinterpret_cast<int32_t*>(c);
     c += cnt_b;
+    a->list_tw = reinterpret_cast<int32_t*>(c);
+    c += ltw_b;
     a->entries = reinterpret_cast<int2*>(c);
     c += ent_b;
     a->ws_m = reinterpret_cast<float*>(c);
@@ -1484,7 +1491,7 @@ size_t attn_workspace(const zr_geom& gm, int nwg, void* ws, AttnArgs* a) {
     a->reuse_meta = reinterpret_cast<int32_t*>(c);
     a->nwg = nwg;
   }
-  return pref_b + cnt_b + ent_b + 2 * ml_b + acc_b + rec_b + rlen_b + rpref_b + meta_b;
+  return pref_b + cnt_b + ltw_b + ent_b + 2 * ml_b + acc_b + rec_b + rlen_b + rpref_b + meta_b;
 }
 
 // What a launch runs: the attention kernel (partials into the workspace), the

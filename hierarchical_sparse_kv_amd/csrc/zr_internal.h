@@ -173,6 +173,7 @@ struct PairArgs {
   const int32_t* block_table; // [B][max_blocks]                 (plan)
   int32_t* counts;            // [B * Hkv] list length per pair  (plan)
   int2* entries;              // [B * Hkv][max_blocks] (physical block, slot mask) (plan)
+  int32_t* list_tw;           // [B * Hkv] window start the spans are clipped at (plan)
   int32_t n_total, max_per_seq, Hq, Hkv, k, window, max_blocks, num_blocks;
   int32_t bt_per;             // block-table entries per thread (set by the launcher)
   int32_t G;                  // query heads per KV head (set by the launcher)
@@ -214,7 +215,8 @@ struct ReuseRecord {
 // Attention launch parameters (device pointers + sizes), passed by value.
 // Pair p = b * Hkv + g attends its counts[p] list entries entries[p][0..)
 // (sparse only) and then the blocks of its window [T - window, T) (dense:
-// [0, T)), read from the block table. Partial results are indexed by slot;
+// [0, T)), read from the block table; a sparse window starts no earlier than
+// list_tw[p], where the lists' spans were clipped. Partial results are indexed by slot;
 // slots [ws_pref[p], ws_pref[p + 1]) hold pair p's.
 struct AttnArgs {
   const void* q;
@@ -230,6 +232,7 @@ struct AttnArgs {
   int32_t* reuse_meta;       // {window, horizon, -, -} kept by zr_reuse_plan
   const int32_t* counts;     // [P] (sparse)
   const int2* entries;       // [P][max_blocks] (sparse)
+  const int32_t* list_tw;    // [P] window start of the call that wrote the lists (sparse)
   int32_t* ws_pref;          // [P + 1]: first partial slot of each pair
   float* ws_m;               // [nwg + P][G]
   float* ws_l;               // [nwg + P][G]
@@ -278,6 +281,7 @@ struct StageArgs {
   void* k_stage;              // [B * stage_blocks][Hkv][16][D]
   void* v_stage;              // [B * stage_blocks][Hkv][D][16]
   int32_t* s_counts;          // [P] staged list lengths
+  int32_t* s_list_tw;         // [P] their window start (the current length: window included)
   int2* s_entries;            // [P][max_blocks] staged lists
   int32_t* dropped;           // [P] entries that did not fit
   int32_t B, Hkv, max_blocks, num_blocks, window, stage_blocks;

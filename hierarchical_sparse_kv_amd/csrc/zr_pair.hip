@@ -645,6 +645,7 @@ pair_kernel(PairArgs a) {
       if (e > s) or_span(L.bmask, s, e, t & (tps - 1), tps);
     }
     __syncthreads();
+    if (t == 0) a.list_tw[p] = tw;
     emit_list(a, L, p, b, nb, btr, wtmp);
   }
 }
@@ -817,6 +818,7 @@ zoom_plan_kernel(PairArgs a) {
     if (e > s) or_span(L.bmask, s, e, 0, 1);
   }
   __syncthreads();
+  if (t == 0) a.list_tw[p] = tw;
   emit_list(a, L, p, b, nb, btr, wtmp);
 }
 

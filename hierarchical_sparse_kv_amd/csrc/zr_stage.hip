@@ -52,6 +52,7 @@ __device__ void stage_item(const StageArgs& a, int p, int j0, int* s_blk) {
   const int ns = n < a.stage_blocks ? n : a.stage_blocks;
   if (j0 == 0 && t == 0) {
     a.s_counts[p] = ns;
+    a.s_list_tw[p] = T;  // the staged lists hold the window: no window of their own
     a.dropped[p] = n - ns;
   }
   if (j0 >= ns) return;  // uniform

@@ -209,7 +209,10 @@ zr_status zr_sparse_decode_attn(const zr_geom* geom, const void* q, const void* 
  * zr_zoom_decode_attn that used it (same geom; the block-table rows of those spans unchanged):
  * the selected thoughts' spans, clipped below that call's window start
  * T0 - window0. This call attends those spans plus its own window
- * [T - window, T) of the current seq_lens. Between semantic boundaries pass
+ * [max(T - window, T0 - window0), T) of the current seq_lens: a window that
+ * would reach below T0 - window0 starts there instead, so that no token is
+ * attended twice (the lists keep T0 - window0 per (b, g) in the workspace).
+ * Between semantic boundaries pass
  * window = window0 + (T - T0), so that the window keeps the start it had at
  * the boundary and every token decoded since is attended (ZoomR Sec. 3.4:
  * the attended set is recomputed only at semantic boundaries); the result
@@ -235,7 +238,8 @@ zr_status zr_sparse_decode_attn_cached(const zr_geom* geom, const void* q, const
  * zr_sparse_decode_step or zr_zoom_decode_attn) that left its block lists in
  * `workspace`, with that call's geom, window and max_attended and the
  * lengths T0 = seq_lens at the boundary: it splits the attention over the
- * lists' spans and the window [T0 - window, T0 + horizon) among the
+ * lists' spans and the window [T0 - window, T0 + horizon) (starting no
+ * earlier than the lists' own window start) among the
  * attention workgroups and keeps, per workgroup, a record of its share with
  * the list entries resolved, in `workspace`.
  * zr_sparse_decode_attn_reuse, called at every step after that with the

@@ -65,14 +65,15 @@ def test_workspace_bytes(L):
     # 4 (sequence, KV head) pairs of at most ceil(1000/16) + 2 blocks, 8 blocks
     # per workgroup -> 33 workgroups; partial slots = workgroups + pairs.
     # Regions, each 16-byte aligned: first workgroup per pair [pairs + 1],
-    # list length per pair [pairs], block lists [pairs][max_blocks] (8 bytes
-    # each), m and l [slots][G], acc [slots][G][128], then for the calls
+    # list length per pair [pairs], the window start each pair's list was
+    # clipped at [pairs], block lists [pairs][max_blocks] (8 bytes each), m
+    # and l [slots][G], acc [slots][G][128], then for the calls
     # between semantic boundaries one 1616-byte segment record per workgroup,
     # the boundary's lengths [batch] and 16 bytes of settings
     up16 = lambda x: (x + 15) // 16 * 16
     nwg = -(-4 * (-(-1000 // 16) + 2) // 8)
     slots = nwg + 4
-    lists = up16(5 * 4) + up16(4 * 4) + 4 * 4 * 8
+    lists = up16(5 * 4) + 2 * up16(4 * 4) + 4 * 4 * 8
     reuse = lambda nwg: nwg * 1616 + up16(2 * 4) + up16(5 * 4) + 16
     assert n == lists + 2 * up16(slots * 4 * 4) + slots * 4 * 128 * 4 + reuse(nwg)
     # the grid is capped at 512 workgroups

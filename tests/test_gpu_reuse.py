@@ -135,3 +135,41 @@ def test_reuse_graph_replays_are_bit_identical():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(st.out, eager)
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
+def test_wider_window_never_counts_a_token_twice(dtype, d):
+    """A call on kept lists whose window would reach below the window start of
+    the call that built them starts its window there instead: the spans were
+    clipped at that point, so a wider window would otherwise attend their
+    tokens between the two starts twice. At the boundary's lengths any wider
+    window gives the boundary call's output bit for bit (cached call and
+    records alike); at later lengths T0 + i, window W + i + extra equals the
+    oracle with window W + i."""
+    w = synth.make_workload(1, device="cuda", overrides=dict(
+        B=3, seq_len=("uniform", 700, 1200), thought=("uniform", 8, 120), k=4, window=32,
+        dtype=dtype, d=d))
+    st, T0 = _boundary(w, 20)
+    ref = st.out.clone()
+    for extra in (1, 9, 300):
+        st.out.fill_(float("nan"))
+        st.cached_attn(w.window + extra, seq_lens=torch.as_tensor(T0, device="cuda"))
+        torch.cuda.synchronize()
+        assert torch.equal(st.out, ref), extra
+    st.reuse_plan(0, window=w.window + 50)
+    st.out.fill_(float("nan"))
+    st.reuse_attn()
+    torch.cuda.synchronize()
+    assert torch.equal(st.out, ref)
+    sel = st.sel.cpu().numpy()
+    h = P.host(w)
+    for i in (3, 20):
+        Ti = torch.as_tensor(T0 + i, dtype=torch.int32, device="cuda")
+        st.cached_attn(w.window + i + 40, seq_lens=Ti)
+        torch.cuda.synchronize()
+        ref_i = O.sparse_decode_step(h["q"], h["k_pool"], h["v_pool"], w.block_table, T0 + i,
+                                     w.seq_ptr, w.th_start, w.th_len, h["kbar"], w.k,
+                                     w.window + i, w.scale, sel=sel)
+        err = float(np.max(np.abs(st.out.cpu().numpy() - ref_i["out"])))
+        say(f"[gpu] wider window, step {i}: max|out - oracle| = {err:.3e}")
+        assert err <= P.TOL[w.dtype], i
