@@ -544,7 +544,7 @@ def main():
         g_offd = capture(lambda i: hs0.dense_attn(), 2)
         g_offd.replay()
         offd_us = timed(g_offd, 2)
-        stage_blocks = min(w0.max_blocks, -(-steps[0].max_attended // 16) + w0.k + 2)
+        stage_blocks = min(w0.max_blocks + 1, -(-steps[0].max_attended // 16) + 2 * w0.k + 2)
         bufs = [zr.Staging(hs0, stage_blocks) for _ in range(2)]
         n_lay = 32
 

@@ -548,7 +548,9 @@ ZR_API zr_status zr_stage_selected(const zr_geom* geom, const void* k_pool, cons
   st = check_thoughts(th, false);
   if (st != ZR_OK) return st;
   if (k < 0 || k > ZR_MAX_K || window < 0 || max_attended < 0) return ZR_E_SHAPE;
-  if (stage_blocks < 1 || stage_blocks > geom->max_blocks_per_seq) return ZR_E_SHAPE;
+  // a pair lists at most max_blocks_per_seq + 1 entries (every block, and
+  // the block where its spans stop and its window starts twice)
+  if (stage_blocks < 1 || stage_blocks > geom->max_blocks_per_seq + 1) return ZR_E_SHAPE;
   if (!k_pool || !v_pool || !block_table || !seq_lens || !k_stage || !v_stage || !dropped ||
       (k > 0 && !sel))
     return ZR_E_NULL;
@@ -564,8 +566,9 @@ ZR_API zr_status zr_stage_selected(const zr_geom* geom, const void* k_pool, cons
   zr::AttnArgs a{}, sa{};
   st = attention_workspace(geom, max_attended, workspace, ws_bytes, &a);
   if (st != ZR_OK) return st;
-  zr_geom gs = *geom;
+  zr_geom gs = *geom;  // the staged geometry: lists one entry longer
   gs.num_blocks = geom->batch > 0 ? geom->batch * stage_blocks : 1;
+  gs.max_blocks_per_seq = geom->max_blocks_per_seq + 1;
   st = attention_workspace(&gs, max_attended, stage_workspace, stage_ws_bytes, &sa);
   if (st != ZR_OK) return st;
   if (geom->batch == 0) return ZR_OK;
@@ -588,6 +591,7 @@ ZR_API zr_status zr_stage_selected(const zr_geom* geom, const void* k_pool, cons
   ga.v_stage = v_stage;
   ga.s_counts = const_cast<int32_t*>(sa.counts);  // written by the stage kernel
   ga.s_list_tw = const_cast<int32_t*>(sa.list_tw);
+  ga.s_stride = gs.max_blocks_per_seq;
   ga.s_entries = const_cast<int2*>(sa.entries);
   ga.dropped = dropped;
   ga.B = geom->batch;

@@ -282,11 +282,12 @@ struct StageArgs {
   void* v_stage;              // [B * stage_blocks][Hkv][D][16]
   int32_t* s_counts;          // [P] staged list lengths
   int32_t* s_list_tw;         // [P] their window start (the current length: window included)
-  int2* s_entries;            // [P][max_blocks] staged lists
+  int2* s_entries;            // [P][s_stride] staged lists
   int32_t* dropped;           // [P] entries that did not fit
   int32_t B, Hkv, max_blocks, num_blocks, window, stage_blocks;
   int32_t lg_pieces;          // log2(16-byte pieces per tile): tile = 16 * D * element bytes
   int32_t item_chunks;        // work items per pair (set by the launcher)
+  int32_t s_stride;           // staged list row length: max_blocks + 1
 };
 
 // Host-side launchers (defined next to their kernels).

@@ -79,7 +79,7 @@ __device__ void stage_item(const StageArgs& a, int p, int j0, int* s_blk) {
       m = 0u;
     }
     s_blk[t] = blk;
-    a.s_entries[static_cast<size_t>(p) * a.max_blocks + j] =
+    a.s_entries[static_cast<size_t>(p) * a.s_stride + j] =
         make_int2(b * a.stage_blocks + j, static_cast<int>(m));
   }
   __syncthreads();

@@ -519,7 +519,7 @@ class Staging:
     (zr_stage_selected): staging pools for `stage_blocks` blocks per
     sequence, their block lists and the per-pair count of entries that did
     not fit. `geom` is the staged geometry (num_blocks = batch *
-    stage_blocks)."""
+    stage_blocks, lists one entry longer than a block-table row)."""
 
     def __init__(self, step: "DeviceStep", stage_blocks: int):
         g = step.geom
@@ -530,7 +530,7 @@ class Staging:
         self.k_stage = torch.empty((nb, g.n_kv_heads, 16, g.head_dim), dtype=dt, device=dev)
         self.v_stage = torch.empty((nb, g.n_kv_heads, g.head_dim, 16), dtype=dt, device=dev)
         self.geom = zr_geom(g.batch, g.n_q_heads, g.n_kv_heads, g.head_dim, 16,
-                            g.max_blocks_per_seq, nb, g.dtype)
+                            g.max_blocks_per_seq + 1, nb, g.dtype)
         ws = zr_workspace_bytes(self.geom, step.max_attended)
         self.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=dev)
         self.dropped = torch.empty(max(g.batch * g.n_kv_heads, 1), dtype=torch.int32, device=dev)

@@ -341,17 +341,24 @@ zr_status zr_sparse_decode_step(const zr_geom* geom, const void* q, const void* 
  *   3. writes the pairs' lists again with staging block ids into
  *      `stage_workspace` (at least zr_workspace_bytes(geom_stage,
  *      max_attended) bytes, geom_stage = geom with num_blocks = batch *
- *      stage_blocks).
+ *      stage_blocks and max_blocks_per_seq + 1: a staged list also holds
+ *      the window's blocks, so it can be one entry longer than a row of the
+ *      block table).
  * zr_sparse_decode_attn_cached(geom_stage, q, k_stage, v_stage, block_table,
  * seq_lens, 0, scale, max_attended, out, stage_workspace, ...) then gives,
  * bit for bit, zr_sparse_decode_attn on the original pools with the same
- * sel and window. Entries past stage_blocks of a pair are not staged (that
- * attention then leaves them out): dropped[p] ([batch * n_kv_heads] int32)
- * receives their number, 0 when the pair fits. A pair lists at most
- * ceil(max_attended / 16) + k + 2 blocks when max_attended bounds its
- * attended tokens.
+ * sel and window (with window 0 it reads no block-table entry, so the
+ * original block_table serves). Entries past stage_blocks of a pair are not
+ * staged (that attention then leaves them out): dropped[p] ([batch *
+ * n_kv_heads] int32) receives their number, 0 when the pair fits. A pair
+ * lists at most ceil(max_attended / 16) + 2 k + 2 blocks when max_attended
+ * bounds its attended tokens (a span of L tokens can touch ceil(L / 16) + 1
+ * blocks, and so can the window), and never more than max_blocks_per_seq + 1
+ * (every block attended, the block where the spans stop and the window
+ * starts listed for both), so stage_blocks = max_blocks_per_seq + 1 never
+ * drops an entry.
  * Errors: ZR_E_NULL, ZR_E_SHAPE (k, window, max_attended < 0; k > ZR_MAX_K;
- * stage_blocks outside [1, max_blocks_per_seq]), ZR_E_ALIGN, ZR_E_WORKSPACE
+ * stage_blocks outside [1, max_blocks_per_seq + 1]), ZR_E_ALIGN, ZR_E_WORKSPACE
  * (either workspace), ZR_E_UNSUPPORTED, ZR_E_LAUNCH.
  */
 zr_status zr_stage_selected(const zr_geom* geom, const void* k_pool, const void* v_pool,

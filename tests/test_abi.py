@@ -295,7 +295,7 @@ def test_stage_selected_errors(L):
         k_stage=FAKE, v_stage=FAKE, stage_workspace=FAKE, stage_ws_bytes=1 << 20,
         dropped=FAKE), **kw))
     assert f(stage_blocks=0) == zr.ZR_E_SHAPE
-    assert f(stage_blocks=5) == zr.ZR_E_SHAPE   # more than max_blocks_per_seq
+    assert f(stage_blocks=6) == zr.ZR_E_SHAPE   # more than max_blocks_per_seq + 1
     assert f(k=-1) == zr.ZR_E_SHAPE
     assert f(window=-1) == zr.ZR_E_SHAPE
     assert f(sel=None) == zr.ZR_E_NULL

@@ -403,8 +403,8 @@ def test_staged_attended_set_from_host_pools(dtype, d):
     kp, vp = w.k_pool.cpu().pin_memory(), w.v_pool.cpu().pin_memory()
     hs = zr.DeviceStep(w.q, kp, vp, w.block_table, w.seq_lens, w.seq_ptr, w.th_start, w.th_len,
                        w.summary_keys, w.max_per_seq, w.k, w.window, w.scale, st.max_attended)
-    blocks = -(-st.max_attended // 16) + w.k + 2
-    sg = zr.Staging(hs, min(blocks, w.max_blocks))
+    blocks = -(-st.max_attended // 16) + 2 * w.k + 2
+    sg = zr.Staging(hs, min(blocks, w.max_blocks + 1))
     h = P.host(w)
     sel = st.sel.clone()
     for win in (w.window, w.window + 7):
@@ -457,6 +457,37 @@ def test_staging_reports_entries_that_do_not_fit():
             assert got[b * w.Hkv + g] == max(0, n - 3), (b, g, n)
     assert got.sum() > 0
 
+
+
+def test_staging_a_full_block_table_with_every_block_attended():
+    """k covers every thought and the block table holds exactly the longest
+    sequence: its pairs list every block, and the block where the spans stop
+    and the window starts twice, one entry more than a block-table row. A
+    staging pool of max_blocks_per_seq + 1 blocks per sequence holds them all
+    (bit for bit the attention on device pools, and the oracle); one block
+    fewer drops exactly that entry and reports it."""
+    w = synth.make_workload(1, device="cuda", seq_lens=[169, 100, 40], overrides=dict(
+        B=3, thought=("uniform", 1, 30), k=60, window=92))
+    assert w.max_blocks == 11  # ceil(169 / 16): the table is exactly full
+    st = zr.step_from_workload(w)
+    st.step()
+    torch.cuda.synchronize()
+    kp, vp = w.k_pool.cpu().pin_memory(), w.v_pool.cpu().pin_memory()
+    hs = zr.DeviceStep(w.q, kp, vp, w.block_table, w.seq_lens, w.seq_ptr, w.th_start, w.th_len,
+                       w.summary_keys, w.max_per_seq, w.k, w.window, w.scale, st.max_attended)
+    roomy = zr.Staging(hs, w.max_blocks + 1)
+    hs.stage(roomy, sel=st.sel)
+    hs.attend_staged(roomy)
+    torch.cuda.synchronize()
+    assert int(roomy.dropped.sum().item()) == 0
+    assert torch.equal(hs.out, st.out)
+    ref = P.oracle_step(w, P.host(w), sel=st.sel.cpu().numpy())
+    assert float(np.max(np.abs(hs.out.cpu().numpy() - ref["out"]))) <= P.TOL[w.dtype]
+    tight = zr.Staging(hs, w.max_blocks)
+    hs.stage(tight, sel=st.sel)
+    torch.cuda.synchronize()
+    dropped = tight.dropped.cpu().numpy().reshape(w.B, w.Hkv)
+    assert np.all(dropped[0] == 1) and np.all(dropped[1:] == 0), dropped
 
 def test_many_pairs_and_largest_k():
     """320 (sequence, KV head) pairs (each workgroup's threads own two pairs in
