@@ -33,6 +33,18 @@
  *   zr_append_kv and zr_summary_keys are the append path that precedes a
  *   step: the new token's K/V into the paged cache (with on-demand block
  *   allocation) and the mean summary key of a thought once it is complete.
+ *   zr_score_topk is steps 1-2 as one call (a semantic boundary's per-layer
+ *   work before the consensus step).
+ *   zr_reuse_plan and zr_sparse_decode_attn_reuse are step 3 between
+ *   semantic boundaries with the work split made once per boundary (segment
+ *   records), instead of planned by every call.
+ *   zr_stage_selected moves a step's attended tiles from pools in pinned host
+ *   memory into a device staging pool (ZoomR Sec. 3.4, the cache kept in
+ *   host memory and only I_f loaded per step).
+ *   zr_sparse_decode_step_noalloc is zr_sparse_decode_step on a device array
+ *   built into the library, for callers that cannot allocate.
+ *   zr_summary_prefetch_rule reports how the step kernel loads summary-key
+ *   rows for a geometry (ahead of the thought range or not), for tests.
  *
  * Conventions shared by every entry point
  *   - All array arguments are DEVICE pointers (memory of the current HIP
