@@ -90,3 +90,45 @@ def test_graph_replays_of_cached_and_zoom_calls():
         torch.cuda.synchronize()
         for a, b in zip((votes, cons, agree, outz, outc), ref):
             assert torch.equal(a, b), rep
+
+
+def test_graph_replays_of_staging_from_host_pools():
+    """zr_stage_selected and the attention on the staging pool, captured in a
+    graph (as the bench runs them): every replay, with other eager work in
+    between, gives the eager output bit for bit."""
+    w = synth.make_workload(1, device="cuda", overrides=dict(B=3, seq_len=("uniform", 800, 3000)))
+    other = synth.make_workload(3, device="cuda", overrides=dict(B=2, seq_len=("fixed", 1500)))
+    st, st2 = zr.step_from_workload(w), zr.step_from_workload(other)
+    st.step()
+    torch.cuda.synchronize()
+    kp, vp = w.k_pool.cpu().pin_memory(), w.v_pool.cpu().pin_memory()
+    hs = zr.DeviceStep(w.q, kp, vp, w.block_table, w.seq_lens, w.seq_ptr, w.th_start, w.th_len,
+                       w.summary_keys, w.max_per_seq, w.k, w.window, w.scale, st.max_attended)
+    sg = zr.Staging(hs, w.max_blocks + 1)
+    sel = st.sel.clone()
+
+    def run():
+        hs.stage(sg, sel=sel)
+        hs.attend_staged(sg)
+
+    run()
+    torch.cuda.synchronize()
+    ref = hs.out.clone()
+    assert torch.equal(ref, st.out)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            run()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        hs.out.fill_(float("nan"))
+        sg.k_stage.zero_()
+        st2.step()              # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(hs.out, ref), rep
+        assert int(sg.dropped.sum().item()) == 0

@@ -68,6 +68,36 @@ def test_noalloc_step_equals_step_twice_then_smaller():
     assert err <= P.TOL[small.dtype]
 
 
+def test_noalloc_step_in_a_graph():
+    """The entry point's purpose: capture under a HIP graph. The captured call
+    gives on every replay, with other eager work in between, the eager
+    result bit for bit (the scratch is rewritten by every replay)."""
+    w = synth.make_workload(1, seed=4, device="cuda",
+                            overrides=dict(B=4, seq_len=("uniform", 1000, 4000)))
+    other = synth.make_workload(3, device="cuda", overrides=dict(B=2, seq_len=("fixed", 1500)))
+    st, st2 = zr.step_from_workload(w), zr.step_from_workload(other)
+    st.step_noalloc()
+    torch.cuda.synchronize()
+    ref = (st.scores.clone(), st.sel.clone(), st.out.clone())
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            st.step_noalloc()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        st.out.fill_(float("nan"))
+        st.sel.fill_(-7)
+        st2.step()              # eager work between replays (its own workspace)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(st.sel, ref[1]), rep
+        assert torch.equal(st.out, ref[2]), rep
+
+
 def test_noalloc_rejects_requests_beyond_the_scratch():
     """A geometry whose workspace exceeds the scratch: ZR_E_SCRATCH, and the
     outputs are untouched."""
