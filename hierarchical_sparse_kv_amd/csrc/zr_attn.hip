@@ -721,7 +721,20 @@ struct MfmaState {
   bool first;
 };
 
-template <int D, int NBW>
+// The larger of x and its copies in lanes l ^ 16 and l ^ 32 (the four lane
+// groups that hold one head), with the row-swap permutes of this GPU: a swap
+// of a register with itself gives each lane the values of lanes l & ~16 and
+// l | 16 (then l & ~32 and l | 32), no LDS round trip.
+__device__ __forceinline__ float max_over_lane_groups(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto s16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+  const uint32_t v = __float_as_uint(x);
+  const auto s32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
+}
+
+template <int G, int D, int NBW>
 __device__ __forceinline__ void compute_chunk(const AttnArgs& a, Chunk<D, NBW>& ch,
                                               const bf16x8 (&qop)[D / 32], f32x4 (&o)[D / 16],
                                               MfmaState& stt) {
@@ -730,8 +743,8 @@ __device__ __forceinline__ void compute_chunk(const AttnArgs& a, Chunk<D, NBW>& 
   // this lane group's 8 slots of its block
   const uint32_t m8 = (((lg >> 1) ? ch.msk[1] : ch.msk[0]) >> (8 * (lg & 1))) & 0xffu;
   // clear value slots outside the set (never trust their bits): one 16-bit
-  // lane mask per slot
-  {
+  // lane mask per slot; nothing to clear when both blocks are whole (uniform)
+  if ((ch.msk[0] & ch.msk[1]) != 0xffffu) {
     typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
     u32x4 keep;
 #pragma unroll
@@ -762,16 +775,19 @@ __device__ __forceinline__ void compute_chunk(const AttnArgs& a, Chunk<D, NBW>& 
       mc = fmaxf(mc, z[hf][r]);
     }
   }
-  mc = fmaxf(mc, __shfl_xor(mc, 16));
-  mc = fmaxf(mc, __shfl_xor(mc, 32));
+  mc = max_over_lane_groups(mc);
   const float m_new = fmaxf(stt.m_run, mc);
-  if (!stt.first) {
-    // rescale what this wave accumulated under the old maximum
+  // rescale what this wave accumulated under the old maximum; where no
+  // head's maximum moved every factor is exactly 1 (uniform skip)
+  if (!stt.first && __ballot(m_new != stt.m_run) != 0ull) {
     const float alpha = m_new == kNegInf ? 1.f : exp2f(stt.m_run - m_new);
     stt.l_run *= alpha;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float ar = __shfl(alpha, lg * 16 + 4 * lg + r);
+      // O row r of lane group lg is head 4 lg + r; with G <= 4 only lane
+      // group 0's rows are heads, and head r's factor is lane r's
+      const float ar = G <= 4 ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), r))
+                              : __shfl(alpha, lg * 16 + 4 * lg + r);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) o[nt][r] *= ar;
     }
@@ -992,12 +1008,12 @@ attn_mfma_kernel(AttnArgs a) {
         switch_at(c);
         if (c + 1 < nck)
           load_chunk<D, NBW>(a, c0 + c + 1 < iB ? xA : xB, from_rec, c + 1, pb_l, msk_l, cB);
-        compute_chunk<D, NBW>(a, cA, qop, o, stt);
+        compute_chunk<G, D, NBW>(a, cA, qop, o, stt);
         if (c + 1 < nck) {
           switch_at(c + 1);
           if (c + 2 < nck)
             load_chunk<D, NBW>(a, c0 + c + 2 < iB ? xA : xB, from_rec, c + 2, pb_l, msk_l, cA);
-          compute_chunk<D, NBW>(a, cB, qop, o, stt);
+          compute_chunk<G, D, NBW>(a, cB, qop, o, stt);
         }
       }
     }
@@ -1041,7 +1057,7 @@ attn_mfma_kernel(AttnArgs a) {
       for (int c = 0; c < nck; ++c) {
         Chunk<D, NBW> ch;
         load_chunk<D, NBW>(a, SegCtx{g, b, as.tw, as.T}, false, c, pb_l, msk_l, ch);
-        compute_chunk<D, NBW>(a, ch, qop, o, stt);
+        compute_chunk<G, D, NBW>(a, ch, qop, o, stt);
       }
     }
     flush_state<G, D>(stt, o, red_m[0], red_l[0], red_o[0]);
