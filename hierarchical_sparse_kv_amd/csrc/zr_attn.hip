@@ -744,7 +744,8 @@ __device__ __forceinline__ void compute_chunk(const AttnArgs& a, Chunk<D, NBW>& 
   const uint32_t m8 = (((lg >> 1) ? ch.msk[1] : ch.msk[0]) >> (8 * (lg & 1))) & 0xffu;
   // clear value slots outside the set (never trust their bits): one 16-bit
   // lane mask per slot; nothing to clear when both blocks are whole (uniform)
-  if ((ch.msk[0] & ch.msk[1]) != 0xffffu) {
+  const bool whole = (ch.msk[0] & ch.msk[1]) == 0xffffu;
+  if (!whole) {
     typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
     u32x4 keep;
 #pragma unroll
@@ -761,7 +762,6 @@ __device__ __forceinline__ void compute_chunk(const AttnArgs& a, Chunk<D, NBW>& 
   // S^T = K . Q^T: product hf gives this lane slots 8 (lg & 1) + 4 hf + r of
   // block lg >> 1, head l16
   float z[2][4];
-  float mc = kNegInf;
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
     f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -769,12 +769,16 @@ __device__ __forceinline__ void compute_chunk(const AttnArgs& a, Chunk<D, NBW>& 
     for (int kk = 0; kk < KS; ++kk)
       sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ch.k[hf][kk], qop[kk], sacc, 0, 0, 0);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const bool on = (m8 >> (4 * hf + r)) & 1u;
-      z[hf][r] = on ? sacc[r] * a.scale_log2 : kNegInf;
-      mc = fmaxf(mc, z[hf][r]);
-    }
+    for (int r = 0; r < 4; ++r) z[hf][r] = sacc[r] * a.scale_log2;
   }
+  if (!whole) {  // slots outside the set take no weight
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (!((m8 >> i) & 1u)) z[i >> 2][i & 3] = kNegInf;
+  }
+  float mc = kNegInf;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) mc = fmaxf(mc, z[i >> 2][i & 3]);
   mc = max_over_lane_groups(mc);
   const float m_new = fmaxf(stt.m_run, mc);
   // rescale what this wave accumulated under the old maximum; where no
@@ -794,13 +798,17 @@ __device__ __forceinline__ void compute_chunk(const AttnArgs& a, Chunk<D, NBW>& 
   }
   stt.m_run = m_new;
   stt.first = false;
+  // 2^(z - m) with the hardware exponential (a weight below 2^-126 of the
+  // largest may flush to 0): a slot outside the set (z = -inf) gives exactly
+  // 0; while no slot of the head has been seen (m = -inf) subtract 0 instead,
+  // so that every p is 0 and none is NaN
+  const float m_sub = m_new == kNegInf ? 0.f : m_new;
   float pr[8];
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float zz = z[hf][r];
-      pr[4 * hf + r] = zz != kNegInf ? exp2f(zz - m_new) : 0.f;
+      pr[4 * hf + r] = __builtin_amdgcn_exp2f(z[hf][r] - m_sub);
       stt.l_run += pr[4 * hf + r];
     }
   // P as bf16 hi + lo parts (about 16 significant bits), slots in the order
