@@ -37,11 +37,11 @@ HBM_PEAK_GBS = 8000.0
 # soon as any of these files changes.
 TRAFFIC_SOURCES = ("zr_internal.h", "zr_pair.hip", "zr_attn.hip")
 TRAFFIC = {
-    "sources_sha256": "5a73402066889126983fe909bc29c81d346d2b3484f53dbbb4d58081e9b455f3",
-    "bytes_per_call": 80516744,  # 79,430,297 fetched + 1,086,447 written
-    "bytes_per_call_reuse": 80487062,  # 79,398,449 fetched + 1,088,613 written
-    "rocprof_kernel_us": 19.84,  # 200 launches of the sparse attention kernel
-    "rocprof_kernel_us_reuse": 18.55,  # 401 launches of the kernel on segment records
+    "sources_sha256": "20394e3a6c8e7bfe9da7dd38d169f2c530e3987014166d9a566df86e54860950",
+    "bytes_per_call": 80738037,  # 79,651,589 fetched + 1,086,448 written
+    "bytes_per_call_reuse": 80641426,  # 79,552,814 fetched + 1,088,612 written
+    "rocprof_kernel_us": 19.16,  # 200 launches of the sparse attention kernel
+    "rocprof_kernel_us_reuse": 18.14,  # 401 launches of the kernel on segment records
 }
 
 
