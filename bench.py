@@ -473,16 +473,18 @@ def main():
                 "between_us_per_layer": round(between_us, 3),
                 "between_gbs": round(zbytes / (between_us * 1e-6) / 1e9, 1)}
 
-    # the same attention + combine kernels on the other scope workloads (4
-    # layer caches each, rotated): ragged batch 32 and 64K tokens x batch 4
+    # the same attention + combine kernels on the other scope workloads, each
+    # rotating over enough layer caches that one rotation gathers several times
+    # the 256 MB Infinity Cache (ragged batch 32: 4 layers, 2.2 GB; 64K tokens
+    # x batch 4: 12 layers, 1.4 GB), so that the tiles come from HBM
     others = None
     if not args.no_others:
         others = {}
-        for cid, label in ((3, "ragged-b32: batch 32, T ~ U[4096, 32768], thoughts U[32, 1024], "
-                               "top-8 + 128 window, interleaved blocks"),
-                           (4, "long-64k-b4: batch 4, 65536 tokens, thoughts log-U[32, 2048], "
-                               "top-16 + 256 window")):
-            ws_ = [synth.make_workload(cid, value_seed=3000 + l, device=dev) for l in range(4)]
+        for cid, nlay, label in ((3, 4, "ragged-b32: batch 32, T ~ U[4096, 32768], thoughts "
+                                        "U[32, 1024], top-8 + 128 window, interleaved blocks"),
+                                 (4, 12, "long-64k-b4: batch 4, 65536 tokens, thoughts "
+                                         "log-U[32, 2048], top-16 + 256 window")):
+            ws_ = [synth.make_workload(cid, value_seed=3000 + l, device=dev) for l in range(nlay)]
             ss_ = []
             for w in ws_:
                 ss_.append(zr.step_from_workload(w, meta=ss_[0] if ss_ else None))
@@ -493,18 +495,19 @@ def main():
                 a_ = attended_counts(st.sel.cpu().numpy(), w.seq_lens, w.seq_ptr, w.th_start,
                                         w.th_len, w.window)
                 byts.append(int(a_.sum()) * 2 * w.d * synth.ELEM_BYTES[w.dtype])
-            g_o = capture(lambda i: ss_[i % 4].cached_attn(ws_[i % 4].window), 40)
+            g_o = capture(lambda i: ss_[i % nlay].cached_attn(ws_[i % nlay].window), 48)
             g_o.replay()
-            us_o = timed(g_o, 40)
-            g_k = capture(lambda i: ss_[i % 4].cached_partials(ws_[i % 4].window), 40)
+            us_o = timed(g_o, 48)
+            g_k = capture(lambda i: ss_[i % nlay].cached_partials(ws_[i % nlay].window), 48)
             g_k.replay()
-            us_k = timed(g_k, 40)
-            g_s = capture(lambda i: ss_[i % 4].step(), 40)
+            us_k = timed(g_k, 48)
+            g_s = capture(lambda i: ss_[i % nlay].step(), 48)
             g_s.replay()
-            us_s = timed(g_s, 40)
+            us_s = timed(g_s, 48)
             gbs = float(np.mean(byts)) / (us_o * 1e-6) / 1e9
             gbs_k = float(np.mean(byts)) / (us_k * 1e-6) / 1e9
-            others[ws_[0].name] = {"workload": label, "gathered_bytes": int(np.mean(byts)),
+            others[ws_[0].name] = {"workload": label, "layers_rotated": nlay,
+                                   "gathered_bytes": int(np.mean(byts)),
                                    "attn_combine_us": round(us_o, 2), "gbs": round(gbs, 1),
                                    "frac": round(gbs / HBM_PEAK_GBS, 4),
                                    "attn_kernel_us": round(us_k, 2),
