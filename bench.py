@@ -38,10 +38,10 @@ HBM_PEAK_GBS = 8000.0
 TRAFFIC_SOURCES = ("zr_internal.h", "zr_pair.hip", "zr_attn.hip")
 TRAFFIC = {
     "sources_sha256": "20394e3a6c8e7bfe9da7dd38d169f2c530e3987014166d9a566df86e54860950",
-    "bytes_per_call": 80738037,  # 79,651,589 fetched + 1,086,448 written
-    "bytes_per_call_reuse": 80641426,  # 79,552,814 fetched + 1,088,612 written
-    "rocprof_kernel_us": 19.16,  # 200 launches of the sparse attention kernel
-    "rocprof_kernel_us_reuse": 18.14,  # 401 launches of the kernel on segment records
+    "bytes_per_call": 80718223,  # 79,631,766 fetched + 1,086,457 written
+    "bytes_per_call_reuse": 80637948,  # 79,549,337 fetched + 1,088,611 written
+    "rocprof_kernel_us": 19.10,  # 200 launches of the sparse attention kernel
+    "rocprof_kernel_us_reuse": 18.22,  # 401 launches of the kernel on segment records
 }
 
 
