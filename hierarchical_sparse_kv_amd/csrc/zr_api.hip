@@ -130,7 +130,7 @@ ZR_API const char* zr_status_string(zr_status s) {
     case ZR_OK: return "ok";
     case ZR_E_NULL: return "a required pointer is NULL";
     case ZR_E_SHAPE: return "sizes are inconsistent or out of range";
-    case ZR_E_UNSUPPORTED: return "this build has no kernel for the requested shape or dtype";
+    case ZR_E_UNSUPPORTED: return "the library has no kernel for the requested shape or dtype";
     case ZR_E_WORKSPACE: return "workspace missing, misaligned or smaller than zr_workspace_bytes()";
     case ZR_E_LAUNCH: return "the HIP runtime reported a launch error";
     case ZR_E_ALIGN: return "q, pools, out or summary keys are not 16-byte aligned";

@@ -103,7 +103,7 @@ typedef enum {
   ZR_OK = 0,
   ZR_E_NULL = 1,        /* a required pointer is NULL */
   ZR_E_SHAPE = 2,       /* sizes inconsistent or out of range */
-  ZR_E_UNSUPPORTED = 3, /* valid request this build has no kernel for */
+  ZR_E_UNSUPPORTED = 3, /* valid request the library has no kernel for */
   ZR_E_WORKSPACE = 4,   /* workspace NULL or smaller than zr_workspace_bytes() */
   ZR_E_LAUNCH = 5,      /* the HIP runtime reported an error */
   ZR_E_ALIGN = 6,       /* q, pools, out or summary keys not 16-byte aligned */
