@@ -316,7 +316,10 @@ ZR_API zr_status zr_reuse_plan(const zr_geom* geom, const int32_t* block_table,
   zr_status st = check_geom(geom);
   if (st != ZR_OK) return st;
   if (window < 0 || horizon < 0 || max_attended < 0) return ZR_E_SHAPE;
-  if (horizon > geom->max_blocks_per_seq * ZR_BLOCK_SIZE) return ZR_E_SHAPE;
+  // a window cannot reach past the table's last slot: a longer horizon plans
+  // the same split (and T0 + horizon stays within int32)
+  const int32_t cap = geom->max_blocks_per_seq * ZR_BLOCK_SIZE;
+  if (horizon > cap) horizon = cap;
   if (!block_table || !seq_lens) return ZR_E_NULL;
   if (static_cast<int64_t>(geom->batch) * geom->n_kv_heads *
           (2 * static_cast<int64_t>(geom->max_blocks_per_seq) + 1) > INT32_MAX)

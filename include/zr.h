@@ -270,9 +270,11 @@ zr_status zr_sparse_decode_attn_cached(const zr_geom* geom, const void* q, const
  * attend, such as zr_sparse_decode_attn_cached, leave the records valid).
  * With horizon = 0 and T = T0 the output equals zr_sparse_decode_attn_cached
  * with `window` bit for bit.
- * Errors: ZR_E_NULL, ZR_E_SHAPE (window, horizon, max_attended < 0; horizon
- * above 16 * max_blocks_per_seq), ZR_E_UNSUPPORTED, ZR_E_WORKSPACE, and for
- * zr_sparse_decode_attn_reuse those of zr_sparse_decode_attn_cached.
+ * A horizon above 16 * max_blocks_per_seq (the table's capacity) plans the
+ * same records as that capacity: no window reaches past it.
+ * Errors: ZR_E_NULL, ZR_E_SHAPE (window, horizon, max_attended < 0),
+ * ZR_E_UNSUPPORTED, ZR_E_WORKSPACE, and for zr_sparse_decode_attn_reuse those
+ * of zr_sparse_decode_attn_cached.
  */
 zr_status zr_reuse_plan(const zr_geom* geom, const int32_t* block_table, const int32_t* seq_lens,
                         int32_t window, int32_t horizon, int32_t max_attended, void* workspace,

@@ -316,7 +316,9 @@ def test_reuse_errors(L):
                                                   workspace=FAKE, ws_bytes=1 << 20), **kw))
     assert f(window=-1) == zr.ZR_E_SHAPE
     assert f(horizon=-1) == zr.ZR_E_SHAPE
-    assert f(horizon=4 * 16 + 1) == zr.ZR_E_SHAPE  # more than the table can hold
+    # more than the table can hold: clamped to its capacity, not an error
+    assert f(horizon=4 * 16 + 1, geom=_geom(batch=0)) == zr.ZR_OK
+    assert f(horizon=2 ** 31 - 1, workspace=None) == zr.ZR_E_WORKSPACE
     assert f(max_attended=-1) == zr.ZR_E_SHAPE
     assert f(block_table=None) == zr.ZR_E_NULL
     assert f(workspace=None) == zr.ZR_E_WORKSPACE

@@ -114,6 +114,34 @@ def test_reuse_with_workgroups_that_plan_themselves():
     _check_steps(w2, st2, T02, [0, 10], "reuse-small-grid")
 
 
+def test_reuse_horizon_past_the_table_is_its_capacity():
+    """A horizon longer than the block table holds (a fixed period on a small
+    cache) plans what the table's capacity plans: the same records, so the
+    same output bit for bit, and the oracle's at the last cached lengths."""
+    w = synth.make_workload(1, device="cuda", overrides=dict(
+        B=2, seq_len=("uniform", 20, 60), thought=("uniform", 2, 12), k=1, window=16))
+    st, T0 = _boundary(w, 12)
+    cap = w.block_table.shape[1] * 16
+    assert int(T0.max()) + 40 > cap
+    Ti = torch.as_tensor(w.seq_lens, dtype=torch.int32, device="cuda")
+    outs = []
+    for horizon in (cap, 40 + cap, 2 ** 31 - 1):
+        st.reuse_plan(horizon)
+        st.out.fill_(float("nan"))
+        st.reuse_attn(seq_lens=Ti)
+        torch.cuda.synchronize()
+        outs.append(st.out.clone())
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+    h = P.host(w)
+    assert np.all(w.seq_lens - T0 == 12)
+    ref = O.sparse_decode_step(h["q"], h["k_pool"], h["v_pool"], w.block_table, w.seq_lens,
+                               w.seq_ptr, w.th_start, w.th_len, h["kbar"], w.k,
+                               w.window + 12, w.scale, sel=st.sel.cpu().numpy())
+    err = float(np.max(np.abs(outs[0].cpu().numpy() - ref["out"])))
+    say(f"[gpu] horizon past the table: max|out - oracle| = {err:.3e}")
+    assert err <= P.TOL[w.dtype]
+
+
 def test_reuse_graph_replays_are_bit_identical():
     w = synth.make_workload(1, device="cuda", overrides=dict(B=4, seq_len=("fixed", 4096)))
     st, T0 = _boundary(w, 12)
