@@ -22,6 +22,7 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "zr.h")
 (ZR_OK, ZR_E_NULL, ZR_E_SHAPE, ZR_E_UNSUPPORTED, ZR_E_WORKSPACE, ZR_E_LAUNCH, ZR_E_ALIGN,
  ZR_E_SCRATCH) = range(8)
 ZR_NOALLOC_SCRATCH_BYTES = 16 << 20
+ZR_BLOCK_SIZE, ZR_MAX_K, ZR_MAX_THOUGHTS_PER_SEQ, ZR_MAX_PAIRS = 16, 1024, 8192, 4096
 ZR_APPEND_OK, ZR_APPEND_NO_FREE_BLOCK, ZR_APPEND_TABLE_FULL, ZR_APPEND_BAD_BLOCK = range(4)
 ZR_F32, ZR_BF16 = 0, 1
 DTYPE_CODE = {torch.float32: ZR_F32, torch.bfloat16: ZR_BF16}

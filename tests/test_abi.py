@@ -3,6 +3,7 @@ and rejects bad host-side arguments before enqueuing anything (these calls
 return during validation, so they need no GPU)."""
 import ctypes
 import os
+import re
 import subprocess
 
 import pytest
@@ -38,6 +39,20 @@ def test_exports_every_declared_symbol(L):
     assert exported == declared
     for name in declared:
         assert hasattr(L, name)
+
+
+def test_header_constants_match_the_binding():
+    """Every #define ZR_* of include/zr.h that the binding mirrors has its value."""
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    hdr = open(os.path.join(root, "include", "zr.h")).read()
+    defs = {}
+    for name, val, shift in re.findall(r"#define (ZR_[A-Z_0-9]+) \(?(\d+)u?(?: << (\d+))?", hdr):
+        defs[name] = int(val) << (int(shift) if shift else 0)
+    mirrored = [n for n in defs if hasattr(zr, n)]
+    assert {"ZR_BLOCK_SIZE", "ZR_MAX_K", "ZR_MAX_THOUGHTS_PER_SEQ", "ZR_MAX_PAIRS",
+            "ZR_NOALLOC_SCRATCH_BYTES", "ZR_APPEND_BAD_BLOCK"} <= set(mirrored)
+    for n in mirrored:
+        assert getattr(zr, n) == defs[n], n
 
 
 def test_status_strings(L):

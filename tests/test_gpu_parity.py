@@ -501,6 +501,22 @@ def test_many_pairs_and_largest_k():
     run_and_check(w, "k-1024")
 
 
+def test_built_maxima_of_pairs_and_thoughts():
+    """The largest batch the attention takes (512 sequences x 8 KV heads =
+    ZR_MAX_PAIRS pairs, short ragged sequences) and the most thoughts a
+    sequence may have (ZR_MAX_THOUGHTS_PER_SEQ one-token thoughts, k = 1024)."""
+    w = synth.make_workload(1, device="cuda", overrides=dict(
+        B=zr.ZR_MAX_PAIRS // 8, seq_len=("uniform", 0, 200), thought=("uniform", 2, 20), k=4,
+        window=32))
+    assert w.B * w.Hkv == zr.ZR_MAX_PAIRS
+    run_and_check(w, "max-pairs")
+    w = synth.make_workload(1, device="cuda", overrides=dict(
+        B=1, Hq=8, Hkv=2, seq_len=("fixed", zr.ZR_MAX_THOUGHTS_PER_SEQ), thought=("uniform", 1, 1),
+        k=1024))
+    assert w.max_per_seq == zr.ZR_MAX_THOUGHTS_PER_SEQ
+    run_and_check(w, "max-thoughts")
+
+
 @pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
 def test_ranges_crossing_many_short_pairs(dtype, d):
     """One long sequence among very short ones (64 pairs): the attention
