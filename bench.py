@@ -476,15 +476,20 @@ def main():
     # the same attention + combine kernels on the other scope workloads, each
     # rotating over enough layer caches that one rotation gathers several times
     # the 256 MB Infinity Cache (ragged batch 32: 4 layers, 2.2 GB; 64K tokens
-    # x batch 4: 12 layers, 1.4 GB), so that the tiles come from HBM
+    # x batch 4: 12 layers, 1.4 GB; the 16K x 8 step with fp32 caches: 8
+    # layers, 1.2 GB), so that the tiles come from HBM
     others = None
     if not args.no_others:
         others = {}
-        for cid, nlay, label in ((3, 4, "ragged-b32: batch 32, T ~ U[4096, 32768], thoughts "
-                                        "U[32, 1024], top-8 + 128 window, interleaved blocks"),
-                                 (4, 12, "long-64k-b4: batch 4, 65536 tokens, thoughts "
-                                         "log-U[32, 2048], top-16 + 256 window")):
-            ws_ = [synth.make_workload(cid, value_seed=3000 + l, device=dev) for l in range(nlay)]
+        for cid, nlay, ov, label in (
+                (3, 4, None, "ragged-b32: batch 32, T ~ U[4096, 32768], thoughts U[32, 1024], "
+                             "top-8 + 128 window, interleaved blocks"),
+                (4, 12, None, "long-64k-b4: batch 4, 65536 tokens, thoughts log-U[32, 2048], "
+                              "top-16 + 256 window"),
+                (1, 8, dict(dtype="f32"), "llama8b-16k-b8-f32: the 16K x 8 step with fp32 "
+                                          "queries and caches (fp32 matrix-core products)")):
+            ws_ = [synth.make_workload(cid, value_seed=3000 + l, device=dev, overrides=ov)
+                   for l in range(nlay)]
             ss_ = []
             for w in ws_:
                 ss_.append(zr.step_from_workload(w, meta=ss_[0] if ss_ else None))
@@ -506,7 +511,7 @@ def main():
             us_s = timed(g_s, 48)
             gbs = float(np.mean(byts)) / (us_o * 1e-6) / 1e9
             gbs_k = float(np.mean(byts)) / (us_k * 1e-6) / 1e9
-            others[ws_[0].name] = {"workload": label, "layers_rotated": nlay,
+            others[ws_[0].name + ("-f32" if ov else "")] = {"workload": label, "layers_rotated": nlay,
                                    "gathered_bytes": int(np.mean(byts)),
                                    "attn_combine_us": round(us_o, 2), "gbs": round(gbs, 1),
                                    "frac": round(gbs / HBM_PEAK_GBS, 4),

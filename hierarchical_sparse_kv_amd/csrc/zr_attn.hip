@@ -39,17 +39,20 @@
 // (p - hi rounded again), so the probabilities keep ~16 significant bits;
 // products accumulate in fp32.
 //
-// fp32 kernel (vector ALU): key rows are read with 16-byte loads, LPR lanes per
-// row, logits reduced across the row's lanes with shuffles; probabilities go
-// through LDS and each lane accumulates the values of its own dimensions.
+// fp32 inputs run the same kernel on v_mfma_f32_16x16x4_f32, one block per
+// chunk (16 slots, the same 16 KB of keys and values as a bf16 chunk):
+// S^T and P.V take their operands from one 16-byte load per lane each (keys
+// by row, values dimension-major), P needs no splitting, and S^T and O keep
+// the bf16 kernel's head layout, so the running states, the rescaling and
+// the merges are shared. The query of each segment is read from LDS rather
+// than held in registers.
 //
 // Exponentials are base 2 with the scale folded in (exp(x) = 2^(x log2 e)).
 //
-// The matrix-core kernel reads each key and value tile once per call, with
-// one 16-byte load per lane and line, so it loads them with the non-temporal
-// hint (measured: 5 to 10 % less time per call on the 16K x 8, 64K x 4 and
-// ragged workloads). The fp32 kernel keeps plain loads: it reads a value
-// column as four 16-byte pieces of one line, and there the hint cost 8 %.
+// Each key and value tile is read once per call, with one 16-byte load per
+// lane, so both kernels load them with the non-temporal hint (measured on
+// bf16: 5 to 10 % less time per call on the 16K x 8, 64K x 4 and ragged
+// workloads).
 #include <math.h>
 
 #include <type_traits>
@@ -870,22 +873,170 @@ __device__ __forceinline__ void load_q(const AttnArgs& a, int p, bf16x8 (&qop)[D
   }
 }
 
+// ---------------------------------------------------------------------------
+// fp32 inputs on the matrix cores (v_mfma_f32_16x16x4_f32): one block per
+// chunk. S^T = K . Q^T takes, at step (t, j), d = 16 t + 4 lg + j: the lane
+// (lg, l16) gives K[slot l16][d] (A) and Q[head l16][d] (B), so each lane's
+// operands are the components of one 16-byte load per t, and S^T lands with
+// slots 4 lg + r of head l16 in the lane (the bf16 layout's head mapping).
+// P.V then takes slot 4 lg + s at step s: the lane's own weights are the A
+// operand, and its value operand, 4 consecutive slots of one dimension of
+// the dimension-major tile, is again one 16-byte load; O rows are heads
+// 4 lg + r, as in the bf16 kernel, so states, rescaling and merging are
+// shared.
+// ---------------------------------------------------------------------------
+template <int D>
+struct ChunkF32 {
+  f32x4 k[D / 16];  // K: lane holds slot l16, dims 16 t + 4 lg .. +3
+  f32x4 v[D / 16];  // V: lane holds dim 16 nt + l16, slots 4 lg .. +3
+  uint32_t msk;     // slot mask (uniform)
+  int pb;           // physical block (uniform)
+};
+
+template <int D>
+__device__ __forceinline__ void load_chunk(const AttnArgs& a, const SegCtx& sc, bool from_rec,
+                                           int c, int pb_l, uint32_t msk_l, ChunkF32<D>& ch) {
+  const int lane = threadIdx.x & 63, l16 = lane & 15, lg = lane >> 4;
+  const float* kpool = static_cast<const float*>(a.k_pool);
+  int pb;
+  uint32_t m;
+  chunk_entry(a, sc, from_rec, pb_l, msk_l, c, &pb, &m);
+  ch.msk = m;
+  ch.pb = pb;
+  // a key row outside the set re-reads the block's first attended row
+  const int kslot = ((m >> l16) & 1u) ? l16 : (m ? __builtin_ctz(m) : 0);
+  const float* krow =
+      kpool + ((static_cast<size_t>(pb) * a.Hkv + sc.g) * kBlock + kslot) * D + 4 * lg;
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t)
+    ch.k[t] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(krow + 16 * t));
+  const float* vcol = static_cast<const float*>(a.v_pool) +
+                      (static_cast<size_t>(pb) * a.Hkv + sc.g) * (D * kBlock) + l16 * kBlock +
+                      4 * lg;
+#pragma unroll
+  for (int nt = 0; nt < D / 16; ++nt)
+    ch.v[nt] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(vcol + nt * 16 * kBlock));
+}
+
+// The query operand is read from LDS (q[t][lane], written by this lane):
+// 32 registers less over the chunk pipeline than holding it.
+template <int G, int D>
+__device__ __forceinline__ void compute_chunk(const AttnArgs& a, ChunkF32<D>& ch,
+                                              const f32x4 (*q)[64], f32x4 (&o)[D / 16],
+                                              MfmaState& stt) {
+  constexpr int NT = D / 16;
+  const int lane = threadIdx.x & 63, lg = lane >> 4;
+  const uint32_t m4 = (ch.msk >> (4 * lg)) & 0xfu;  // this lane's slots 4 lg .. +3
+  const bool whole = ch.msk == 0xffffu;              // uniform
+  f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) {
+    const f32x4 qv = q[t][lane];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(ch.k[t][j], qv[j], sacc, 0, 0, 0);
+  }
+  float z[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) z[r] = sacc[r] * a.scale_log2;
+  if (!whole) {  // slots outside the set take no weight
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (!((m4 >> r) & 1u)) z[r] = kNegInf;
+  }
+  float mc = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+  mc = max_over_lane_groups(mc);
+  const float m_new = fmaxf(stt.m_run, mc);
+  if (!stt.first && __ballot(m_new != stt.m_run) != 0ull) {
+    const float alpha = m_new == kNegInf ? 1.f : exp2f(stt.m_run - m_new);
+    stt.l_run *= alpha;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float ar = G <= 4 ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), r))
+                              : __shfl(alpha, lg * 16 + 4 * lg + r);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) o[nt][r] *= ar;
+    }
+  }
+  stt.m_run = m_new;
+  stt.first = false;
+  const float m_sub = m_new == kNegInf ? 0.f : m_new;
+  float pr[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    pr[r] = __builtin_amdgcn_exp2f(z[r] - m_sub);
+    stt.l_run += pr[r];
+  }
+  if (!whole) {  // value slots outside the set are cleared (never trust their bits)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (!((m4 >> r) & 1u)) ch.v[nt][r] = 0.f;
+  }
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      o[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(pr[r], ch.v[nt][r], o[nt], 0, 0, 0);
+}
+
+// Q^T of pair p as the B operand: lane holds head l16, dims 16 t + 4 lg .. +3.
+template <int G, int D>
+__device__ __forceinline__ void load_q(const AttnArgs& a, int p, f32x4 (&qop)[D / 16]) {
+  const int lane = threadIdx.x & 63, l16 = lane & 15, lg = lane >> 4;
+  const int b = div_small(p, a.Hkv), g = p - b * a.Hkv;
+  const float* qrow = static_cast<const float*>(a.q) +
+                      (static_cast<size_t>(b) * a.Hq + g * G + (l16 < G ? l16 : 0)) * D;
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) qop[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (l16 < G) {
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) qop[t] = *reinterpret_cast<const f32x4*>(qrow + 16 * t + 4 * lg);
+  }
+}
+
+// The matrix-core kernel's per-element-type pieces: chunk registers, query
+// operand, blocks per chunk.
+template <typename E, int D>
+struct MfmaTypes;
+template <int D>
+struct MfmaTypes<BF16, D> {
+  using CK = Chunk<D, 2>;
+  using QV = bf16x8;
+  static constexpr int QN = D / 32, NBW = 2;
+};
+template <int D>
+struct MfmaTypes<F32, D> {
+  using CK = ChunkF32<D>;
+  using QV = f32x4;
+  static constexpr int QN = D / 16, NBW = 1;
+};
+
 // One or two segments (A, then B) streamed as one sequence of chunks: the
 // chunks of A, then those of B, dealt round-robin to the waves, so both
 // segments share one pipeline and the waves stay balanced. A wave that
 // crosses from A to B stores its A state to LDS slot 0 and starts B with
 // B's query (kept in LDS: each lane reads back what it wrote itself). Three
 // or more segments (short pairs) are taken one after the other.
-template <int G, int D, int NBW, bool DENSE, bool REUSE>
+template <typename E, int G, int D, int NBW, bool DENSE, bool REUSE>
 __global__ void __launch_bounds__(kThreads, 2)
 attn_mfma_kernel(AttnArgs a) {
-  constexpr int KS = D / 32, NT = D / 16;
+  using CK = typename MfmaTypes<E, D>::CK;
+  static_assert(NBW == MfmaTypes<E, D>::NBW, "blocks per chunk of the element type");
+  using QV = typename MfmaTypes<E, D>::QV;
+  constexpr int KS = MfmaTypes<E, D>::QN, NT = D / 16;
   constexpr int EPB = 64;         // entries resolved per batch (one per lane)
   constexpr int CPB = EPB / NBW;  // chunks per batch
   __shared__ float red_m[2][kWaves][G];
   __shared__ float red_l[2][kWaves][G];
   __shared__ float red_o[2][kWaves][G][D];
-  __shared__ bf16x8 q_b[KS][64];
+  // fp32: the queries stay in LDS (segment A's in q_a, B's in q_b; every
+  // wave that writes one writes the same values); bf16 keeps its query in
+  // registers and only B's in LDS, for a wave that crosses into B
+  constexpr bool kQLds = std::is_same<E, F32>::value;
+  __shared__ QV q_a[kQLds ? KS : 1][64];
+  __shared__ QV q_b[KS][64];
   __shared__ PlanLds psm;
 
   const int lane = threadIdx.x & 63, wave = wave_id();
@@ -980,10 +1131,25 @@ attn_mfma_kernel(AttnArgs a) {
     // the entries first: the first K/V loads wait for them, the queries are
     // needed only once those loads have returned
     resolve_batch(0);
-    bf16x8 qop[KS], qb[KS];
-    load_q<G, D>(a, iB > 0 ? sa.p : sb.p, qop);
+    QV qop[KS], qb[KS];
     const bool keep_b = iB > 0 && nck_all > iB;  // this wave crosses from A to B
-    if (keep_b) load_q<G, D>(a, sb.p, qb);
+    const QV(*qsrc)[64] = q_a;
+    if constexpr (kQLds) {
+      if (iB > 0) load_q<G, D>(a, sa.p, qop);
+      if (nck_all > iB) load_q<G, D>(a, sb.p, qb);
+      if (iB > 0) {
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) q_a[kk][lane] = qop[kk];
+      }
+      if (nck_all > iB) {
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) q_b[kk][lane] = qb[kk];
+      }
+      qsrc = iB > 0 ? q_a : q_b;
+    } else {
+      load_q<G, D>(a, iB > 0 ? sa.p : sb.p, qop);
+      if (keep_b) load_q<G, D>(a, sb.p, qb);
+    }
     f32x4 o[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -999,29 +1165,39 @@ attn_mfma_kernel(AttnArgs a) {
       auto switch_at = [&](int c) {
         if (c0 + c == iB && iB > 0) {
           flush_state<G, D>(stt, o, red_m[0], red_l[0], red_o[0]);
+          if constexpr (kQLds) {
+            qsrc = q_b;
+          } else {
 #pragma unroll
-          for (int kk = 0; kk < KS; ++kk) qop[kk] = q_b[kk][lane];
+            for (int kk = 0; kk < KS; ++kk) qop[kk] = q_b[kk][lane];
+          }
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
           stt = MfmaState{kNegInf, 0.f, true};
         }
       };
-      Chunk<D, NBW> cA, cB;
-      load_chunk<D, NBW>(a, c0 < iB ? xA : xB, from_rec, 0, pb_l, msk_l, cA);
-      if (c0 == 0 && keep_b) {  // B's query to LDS once the first loads are out
+      auto compute = [&](CK& ch) {
+        if constexpr (kQLds)
+          compute_chunk<G, D>(a, ch, qsrc, o, stt);
+        else
+          compute_chunk<G, D>(a, ch, qop, o, stt);
+      };
+      CK cA, cB;
+      load_chunk(a, c0 < iB ? xA : xB, from_rec, 0, pb_l, msk_l, cA);
+      if (!kQLds && c0 == 0 && keep_b) {  // B's query to LDS once the first loads are out
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) q_b[kk][lane] = qb[kk];
       }
       for (int c = 0; c < nck; c += 2) {
         switch_at(c);
         if (c + 1 < nck)
-          load_chunk<D, NBW>(a, c0 + c + 1 < iB ? xA : xB, from_rec, c + 1, pb_l, msk_l, cB);
-        compute_chunk<G, D, NBW>(a, cA, qop, o, stt);
+          load_chunk(a, c0 + c + 1 < iB ? xA : xB, from_rec, c + 1, pb_l, msk_l, cB);
+        compute(cA);
         if (c + 1 < nck) {
           switch_at(c + 1);
           if (c + 2 < nck)
-            load_chunk<D, NBW>(a, c0 + c + 2 < iB ? xA : xB, from_rec, c + 2, pb_l, msk_l, cA);
-          compute_chunk<G, D, NBW>(a, cB, qop, o, stt);
+            load_chunk(a, c0 + c + 2 < iB ? xA : xB, from_rec, c + 2, pb_l, msk_l, cA);
+          compute(cB);
         }
       }
     }
@@ -1053,8 +1229,12 @@ attn_mfma_kernel(AttnArgs a) {
       resolve_entry<DENSE>(a, as, b, wave_entry<NBW>(as, wave, c0 * NBW + lane), &pb_l, &msk_l);
     };
     resolve_batch(0);  // the entries before the query, as in the streamed path
-    bf16x8 qop[KS];
+    QV qop[KS];
     load_q<G, D>(a, as.p, qop);
+    if constexpr (kQLds) {  // (every wave writes the segment's query: same values)
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) q_a[kk][lane] = qop[kk];
+    }
     f32x4 o[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1063,207 +1243,17 @@ attn_mfma_kernel(AttnArgs a) {
       if (c0 > 0) resolve_batch(c0);
       const int nck = nck_all - c0 < CPB ? nck_all - c0 : CPB;
       for (int c = 0; c < nck; ++c) {
-        Chunk<D, NBW> ch;
-        load_chunk<D, NBW>(a, SegCtx{g, b, as.tw, as.T}, false, c, pb_l, msk_l, ch);
-        compute_chunk<G, D, NBW>(a, ch, qop, o, stt);
+        CK ch;
+        load_chunk(a, SegCtx{g, b, as.tw, as.T}, false, c, pb_l, msk_l, ch);
+        if constexpr (kQLds)
+          compute_chunk<G, D>(a, ch, q_a, o, stt);
+        else
+          compute_chunk<G, D, NBW>(a, ch, qop, o, stt);
       }
     }
     flush_state<G, D>(stt, o, red_m[0], red_l[0], red_o[0]);
     __syncthreads();
     write_partial<G, D>(a, as.slot, red_m[0], red_l[0], red_o[0]);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Vector-ALU kernel (fp32 inputs), G <= 8.
-// ---------------------------------------------------------------------------
-template <int LPR>
-__device__ __forceinline__ float row_sum(float v) {
-#pragma unroll
-  for (int o = LPR / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-
-template <typename E, int G, int D, bool DENSE, bool REUSE>
-__global__ void __launch_bounds__(kThreads)
-attn_valu_kernel(AttnArgs a) {
-  using St = typename E::storage;
-  constexpr int NBW = 2;
-  constexpr int VPL = 16 / E::kBytes;  // values per 16-byte load
-  constexpr int LPR = D / VPL;         // lanes per key row
-  constexpr int RPW = 64 / LPR;        // key rows per wave load
-  constexpr int NL = kBlock / RPW;     // key loads per block per lane
-  constexpr int DPL = D / 64;          // value dimensions per lane
-  constexpr int VCH = kBlock / VPL;    // 16-byte chunks per value column
-  constexpr int CPB = 64 / NBW;
-  __shared__ float red_m[kWaves][G];
-  __shared__ float red_l[kWaves][G];
-  __shared__ float red_o[kWaves][G][D];
-  __shared__ float p_lds[kWaves][NBW * kBlock][G];
-  __shared__ PlanLds psm;
-
-  const int lane = threadIdx.x & 63, wave = wave_id();
-  auto segment = [&](const Assign& as) {
-    const int b = as.p / a.Hkv, g = as.p % a.Hkv;
-
-    const St* kpool = static_cast<const St*>(a.k_pool);
-    const St* vpool = static_cast<const St*>(a.v_pool);
-    const int cl = lane % LPR, rs = lane / LPR;
-    float qf[G][VPL];
-    {
-      const St* qb = static_cast<const St*>(a.q) + (static_cast<size_t>(b) * a.Hq + g * G) * D;
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        unpack16<E>(*reinterpret_cast<const uint4*>(qb + h * D + cl * VPL), qf[h]);
-#pragma unroll
-        for (int v = 0; v < VPL; ++v) qf[h][v] *= a.scale_log2;
-      }
-    }
-    float m_run[G], l_part[G], acc[G][DPL];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      m_run[h] = kNegInf;
-      l_part[h] = 0.f;
-#pragma unroll
-      for (int dd = 0; dd < DPL; ++dd) acc[h][dd] = 0.f;
-    }
-
-    const int nck_all = wave_chunks<NBW>(as, wave);
-    for (int c0 = 0; c0 < nck_all; c0 += CPB) {
-      int pb_l;
-      uint32_t msk_l;
-      resolve_entry<DENSE>(a, as, b, wave_entry<NBW>(as, wave, c0 * NBW + lane), &pb_l, &msk_l);
-      const int nck = nck_all - c0 < CPB ? nck_all - c0 : CPB;
-      for (int c = 0; c < nck; ++c) {
-        int pb[NBW];
-        uint32_t msk[NBW];
-#pragma unroll
-        for (int i = 0; i < NBW; ++i) {
-          pb[i] = __shfl(pb_l, c * NBW + i);
-          msk[i] = __shfl(msk_l, c * NBW + i);
-        }
-        float z[NBW][NL][G];
-        float mc[G];
-#pragma unroll
-        for (int h = 0; h < G; ++h) mc[h] = kNegInf;
-#pragma unroll
-        for (int i = 0; i < NBW; ++i) {
-          const size_t tile = static_cast<size_t>(pb[i]) * a.Hkv + g;
-#pragma unroll
-          for (int t = 0; t < NL; ++t) {
-            const int slot = rs + RPW * t;
-            const bool on = (msk[i] >> slot) & 1u;
-            uint4 u = make_uint4(0, 0, 0, 0);
-            if (on)
-              u = *reinterpret_cast<const uint4*>(kpool + (tile * kBlock + slot) * D + cl * VPL);
-            float x[VPL];
-            unpack16<E>(u, x);
-#pragma unroll
-            for (int h = 0; h < G; ++h) {
-              float s = 0.f;
-#pragma unroll
-              for (int v = 0; v < VPL; ++v) s = fmaf(qf[h][v], x[v], s);
-              s = row_sum<LPR>(s);
-              z[i][t][h] = on ? s : kNegInf;
-              mc[h] = fmaxf(mc[h], z[i][t][h]);
-            }
-          }
-        }
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-#pragma unroll
-          for (int o = LPR; o < 64; o <<= 1) mc[h] = fmaxf(mc[h], __shfl_xor(mc[h], o));
-          const float mn = fmaxf(m_run[h], mc[h]);
-          const float alpha = mn == kNegInf ? 1.f : exp2f(m_run[h] - mn);
-          l_part[h] *= alpha;
-#pragma unroll
-          for (int dd = 0; dd < DPL; ++dd) acc[h][dd] *= alpha;
-          m_run[h] = mn;
-        }
-        // probabilities of the wave's slots -> LDS (one writer lane per row)
-#pragma unroll
-        for (int i = 0; i < NBW; ++i)
-#pragma unroll
-          for (int t = 0; t < NL; ++t)
-#pragma unroll
-            for (int h = 0; h < G; ++h) {
-              const float pv = z[i][t][h] != kNegInf ? exp2f(z[i][t][h] - m_run[h]) : 0.f;
-              if (cl == 0) {
-                p_lds[wave][i * kBlock + rs + RPW * t][h] = pv;
-                l_part[h] += pv;
-              }
-            }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-        // values: lane owns dims lane + 64 dd; a value column holds 16 slots
-#pragma unroll
-        for (int i = 0; i < NBW; ++i) {
-          if (msk[i] == 0u) continue;
-          const size_t tile = static_cast<size_t>(pb[i]) * a.Hkv + g;
-#pragma unroll
-          for (int dd = 0; dd < DPL; ++dd) {
-            const St* col = vpool + (tile * D + lane + 64 * dd) * kBlock;
-#pragma unroll
-            for (int c2 = 0; c2 < VCH; ++c2) {
-              float x[VPL];
-              unpack16<E>(*reinterpret_cast<const uint4*>(col + c2 * VPL), x);
-#pragma unroll
-              for (int v = 0; v < VPL; ++v) {
-                const int slot = c2 * VPL + v;
-                if ((msk[i] >> slot) & 1u) {
-#pragma unroll
-                  for (int h = 0; h < G; ++h)
-                    acc[h][dd] = fmaf(p_lds[wave][i * kBlock + slot][h], x[v], acc[h][dd]);
-                }
-              }
-            }
-          }
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-      }
-    }
-
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float l = l_part[h];
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) l += __shfl_xor(l, o);
-      if (lane == 0) {
-        red_m[wave][h] = m_run[h];
-        red_l[wave][h] = l;
-      }
-#pragma unroll
-      for (int dd = 0; dd < DPL; ++dd) red_o[wave][h][lane + 64 * dd] = acc[h][dd];
-    }
-    __syncthreads();
-    write_partial<G, D>(a, as.slot, red_m, red_l, red_o);
-  };
-
-  if constexpr (REUSE) {  // the plan of zr_reuse_plan, on the boundary's lengths and settings
-    if (blockIdx.x == 0)  // the slot bases of that split, for the combine kernel
-      for (int i = threadIdx.x; i <= a.B * a.Hkv; i += kThreads) a.ws_pref[i] = a.reuse_pref[i];
-    __syncthreads();
-    a.ws_pref = a.reuse_pref;
-    a.plan_lens = a.reuse_lens;
-    a.window = __builtin_amdgcn_readfirstlane(a.reuse_meta[0]);
-    a.horizon = __builtin_amdgcn_readfirstlane(a.reuse_meta[1]);
-  }
-  Assign sa, sb;
-  const int nseg = plan_work<DENSE>(a, psm, true, &sa, &sb);
-  if (nseg == 0) return;  // uniform over the workgroup
-  int nrec = psm.nrec, ri = 0;
-  for (int si = 0; si < nseg; ++si) {
-    if (si > 0) __syncthreads();  // the previous segment's LDS results have been read
-    if (ri == nrec) {  // uniform
-      nrec = plan_next<DENSE>(a, psm);
-      ri = 0;
-    }
-    Assign as;
-    get_record(psm, ri++, &as);
-    segment(as);
   }
 }
 
@@ -1463,7 +1453,6 @@ reuse_plan_kernel(AttnArgs a) {
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
-constexpr int kMfmaNBW = 2;
 
 int attn_workgroups(const zr_geom& gm, int32_t max_attended) {
   const int64_t pairs = static_cast<int64_t>(gm.batch) * gm.n_kv_heads;
@@ -1539,38 +1528,21 @@ static hipError_t launch_combine_gd(const zr_geom& gm, const AttnArgs& a, hipStr
 // sparse between semantic boundaries (segment records).
 enum AttnKind { kSparse = 0, kDense = 1, kReuse = 2 };
 
-template <int G, int D>
+template <typename E, int G, int D>
 static hipError_t launch_mfma(const zr_geom& gm, const AttnArgs& a, int kind, int parts,
                               hipStream_t s) {
+  constexpr int NBW = MfmaTypes<E, D>::NBW;
   if (parts & kAttnOnly) {
     const dim3 grid(a.nwg);
     if (kind == kDense)
-      hipLaunchKernelGGL((attn_mfma_kernel<G, D, kMfmaNBW, true, false>), grid, dim3(kThreads), 0,
+      hipLaunchKernelGGL((attn_mfma_kernel<E, G, D, NBW, true, false>), grid, dim3(kThreads), 0,
                          s, a);
     else if (kind == kReuse)
-      hipLaunchKernelGGL((attn_mfma_kernel<G, D, kMfmaNBW, false, true>), grid, dim3(kThreads), 0,
+      hipLaunchKernelGGL((attn_mfma_kernel<E, G, D, NBW, false, true>), grid, dim3(kThreads), 0,
                          s, a);
     else
-      hipLaunchKernelGGL((attn_mfma_kernel<G, D, kMfmaNBW, false, false>), grid, dim3(kThreads),
-                         0, s, a);
-    const hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-  }
-  return (parts & kCombineOnly) ? launch_combine_gd<G, D>(gm, a, s) : hipSuccess;
-}
-
-template <typename E, int G, int D>
-static hipError_t launch_valu(const zr_geom& gm, const AttnArgs& a, int kind, int parts,
-                              hipStream_t s) {
-  if (parts & kAttnOnly) {
-    const dim3 grid(a.nwg);
-    if (kind == kDense)
-      hipLaunchKernelGGL((attn_valu_kernel<E, G, D, true, false>), grid, dim3(kThreads), 0, s, a);
-    else if (kind == kReuse)
-      hipLaunchKernelGGL((attn_valu_kernel<E, G, D, false, true>), grid, dim3(kThreads), 0, s, a);
-    else
-      hipLaunchKernelGGL((attn_valu_kernel<E, G, D, false, false>), grid, dim3(kThreads), 0, s,
-                         a);
+      hipLaunchKernelGGL((attn_mfma_kernel<E, G, D, NBW, false, false>), grid, dim3(kThreads), 0,
+                         s, a);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
@@ -1583,19 +1555,19 @@ static hipError_t launch_d(const zr_geom& gm, const AttnArgs& a, int kind, int p
   const int G = gm.n_q_heads / gm.n_kv_heads;
   if (gm.dtype == ZR_BF16) {
     switch (G) {
-      case 1: return launch_mfma<1, D>(gm, a, kind, parts, s);
-      case 2: return launch_mfma<2, D>(gm, a, kind, parts, s);
-      case 4: return launch_mfma<4, D>(gm, a, kind, parts, s);
-      case 8: return launch_mfma<8, D>(gm, a, kind, parts, s);
-      case 16: return launch_mfma<16, D>(gm, a, kind, parts, s);
+      case 1: return launch_mfma<BF16, 1, D>(gm, a, kind, parts, s);
+      case 2: return launch_mfma<BF16, 2, D>(gm, a, kind, parts, s);
+      case 4: return launch_mfma<BF16, 4, D>(gm, a, kind, parts, s);
+      case 8: return launch_mfma<BF16, 8, D>(gm, a, kind, parts, s);
+      case 16: return launch_mfma<BF16, 16, D>(gm, a, kind, parts, s);
       default: return hipErrorInvalidValue;
     }
   }
   switch (G) {
-    case 1: return launch_valu<F32, 1, D>(gm, a, kind, parts, s);
-    case 2: return launch_valu<F32, 2, D>(gm, a, kind, parts, s);
-    case 4: return launch_valu<F32, 4, D>(gm, a, kind, parts, s);
-    case 8: return launch_valu<F32, 8, D>(gm, a, kind, parts, s);
+    case 1: return launch_mfma<F32, 1, D>(gm, a, kind, parts, s);
+    case 2: return launch_mfma<F32, 2, D>(gm, a, kind, parts, s);
+    case 4: return launch_mfma<F32, 4, D>(gm, a, kind, parts, s);
+    case 8: return launch_mfma<F32, 8, D>(gm, a, kind, parts, s);
     default: return hipErrorInvalidValue;
   }
 }
