@@ -22,7 +22,6 @@ zr_status check_geom(const zr_geom* g) {
   if (g->n_q_heads % g->n_kv_heads != 0) return ZR_E_SHAPE;
   const int G = g->n_q_heads / g->n_kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return ZR_E_UNSUPPORTED;
-  if (G == 16 && g->dtype != ZR_BF16) return ZR_E_UNSUPPORTED;
   if (g->head_dim != 64 && g->head_dim != 128) return ZR_E_UNSUPPORTED;
   if (g->block_size != ZR_BLOCK_SIZE) return ZR_E_UNSUPPORTED;
   if (g->dtype != ZR_F32 && g->dtype != ZR_BF16) return ZR_E_UNSUPPORTED;

@@ -1568,6 +1568,7 @@ static hipError_t launch_d(const zr_geom& gm, const AttnArgs& a, int kind, int p
     case 2: return launch_mfma<F32, 2, D>(gm, a, kind, parts, s);
     case 4: return launch_mfma<F32, 4, D>(gm, a, kind, parts, s);
     case 8: return launch_mfma<F32, 8, D>(gm, a, kind, parts, s);
+    case 16: return launch_mfma<F32, 16, D>(gm, a, kind, parts, s);
     default: return hipErrorInvalidValue;
   }
 }

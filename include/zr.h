@@ -128,7 +128,7 @@ typedef enum { ZR_F32 = 0, ZR_BF16 = 1 } zr_dtype;
 typedef struct {
   int32_t batch;              /* B >= 0 (B = 0: every call is a no-op) */
   int32_t n_q_heads;          /* Hq > 0, multiple of n_kv_heads */
-  int32_t n_kv_heads;         /* Hkv > 0; Hq / Hkv in {1, 2, 4, 8, 16} (16: bf16 only) */
+  int32_t n_kv_heads;         /* Hkv > 0; Hq / Hkv in {1, 2, 4, 8, 16} */
   int32_t head_dim;           /* 64 or 128 */
   int32_t block_size;         /* must be ZR_BLOCK_SIZE (16) */
   int32_t max_blocks_per_seq; /* columns of block_table, >= 1 */

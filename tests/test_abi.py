@@ -102,7 +102,7 @@ def test_workspace_bytes(L):
 @pytest.mark.parametrize("kw,code", [
     (dict(n_q_heads=6, n_kv_heads=4), zr.ZR_E_SHAPE),
     (dict(n_q_heads=48, n_kv_heads=2), zr.ZR_E_UNSUPPORTED),
-    (dict(n_q_heads=32, n_kv_heads=2, dtype=zr.ZR_F32), zr.ZR_E_UNSUPPORTED),
+    (dict(n_q_heads=64, n_kv_heads=2, dtype=zr.ZR_F32), zr.ZR_E_UNSUPPORTED),
     (dict(head_dim=96), zr.ZR_E_UNSUPPORTED),
     (dict(block_size=32), zr.ZR_E_UNSUPPORTED),
     (dict(dtype=7), zr.ZR_E_UNSUPPORTED),

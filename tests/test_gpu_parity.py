@@ -163,7 +163,8 @@ def _small(cfg, **over):
                                              ("bf16", 128, 16, 8), ("f32", 128, 8, 1),
                                              ("f32", 64, 16, 2), ("bf16", 64, 4, 2),
                                              ("bf16", 128, 32, 2), ("bf16", 64, 16, 1),
-                                             ("f32", 128, 16, 4)])
+                                             ("f32", 128, 16, 4), ("f32", 128, 32, 2),
+                                             ("f32", 64, 16, 1)])
 def test_shapes_and_dtypes(dtype, d, Hq, Hkv):
     w = _small(1, dtype=dtype, d=d, Hq=Hq, Hkv=Hkv)
     run_and_check(w, f"shape-{dtype}-d{d}-G{Hq // Hkv}", check_dense=True)

@@ -43,7 +43,7 @@ def _dev(x):
 def _geometry(rng, g16=True):
     dtype = ["bf16", "f32"][rng.integers(0, 2)]
     Hkv = int([1, 2, 4, 8][rng.integers(0, 4)])
-    Gs = [1, 2, 4, 8, 16] if (dtype == "bf16" and g16) else [1, 2, 4, 8]
+    Gs = [1, 2, 4, 8, 16] if g16 else [1, 2, 4, 8]
     G = int(Gs[rng.integers(0, len(Gs))])
     d = int([64, 128][rng.integers(0, 2)])
     return dtype, Hkv, G, d
