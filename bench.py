@@ -37,11 +37,11 @@ HBM_PEAK_GBS = 8000.0
 # soon as any of these files changes.
 TRAFFIC_SOURCES = ("zr_internal.h", "zr_pair.hip", "zr_attn.hip")
 TRAFFIC = {
-    "sources_sha256": "1a2ff53a43d7ccedfa7b789d68972bcc52e05a3551ae432694d4576af1e478b8",
-    "bytes_per_call": 80701330,  # 79,614,881 fetched + 1,086,449 written
-    "bytes_per_call_reuse": 80654847,  # 79,566,233 fetched + 1,088,614 written
-    "rocprof_kernel_us": 19.13,  # 200 launches of the sparse attention kernel
-    "rocprof_kernel_us_reuse": 18.49,  # 401 launches of the kernel on segment records
+    "sources_sha256": "8c1c17eb874d74165d3c41e0dbaa0183944c017887ddf2403b9e14de9de787f2",
+    "bytes_per_call": 80649117,  # 79,562,665 fetched + 1,086,452 written
+    "bytes_per_call_reuse": 80626932,  # 79,538,318 fetched + 1,088,613 written
+    "rocprof_kernel_us": 19.00,  # 200 launches of the sparse attention kernel
+    "rocprof_kernel_us_reuse": 18.29,  # 401 launches of the kernel on segment records
 }
 
 
