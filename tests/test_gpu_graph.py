@@ -15,9 +15,10 @@ def _gpu():
     zr.lib()
 
 
-@pytest.mark.parametrize("fused", [True, False])
-def test_graph_replays_match_eager(fused):
-    w = synth.make_workload(1, device="cuda", overrides=dict(B=4, seq_len=("fixed", 4096)))
+@pytest.mark.parametrize("fused,dtype", [(True, "bf16"), (False, "bf16"), (True, "f32")])
+def test_graph_replays_match_eager(fused, dtype):
+    w = synth.make_workload(1, device="cuda", overrides=dict(B=4, seq_len=("fixed", 4096),
+                                                             dtype=dtype))
     other = synth.make_workload(3, device="cuda",
                                 overrides=dict(B=3, seq_len=("uniform", 500, 3000)))
     st, st2 = zr.step_from_workload(w), zr.step_from_workload(other)

@@ -127,10 +127,12 @@ def test_long_output_near_ties():
     run_and_check(w, "cfg4")
 
 
-def test_physical_block_permutation_is_bit_identical():
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_physical_block_permutation_is_bit_identical(dtype):
     """Same logical cache, different physical placement: identical outputs
     (partition boundaries depend on logical positions only)."""
-    w = synth.make_workload(1, device="cuda", overrides=dict(B=2, seq_len=("fixed", 4096)))
+    w = synth.make_workload(1, device="cuda", overrides=dict(B=2, seq_len=("fixed", 4096),
+                                                             dtype=dtype))
     st = zr.step_from_workload(w)
     st.step()
     out1 = st.out.clone()

@@ -71,10 +71,12 @@ def test_reuse_steps_match_oracle(dtype, d):
     _check_steps(w, st, T0, [0, 1, 9, 17, 40], f"reuse-{dtype}")
 
 
-def test_reuse_at_the_boundary_equals_the_cached_call():
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_reuse_at_the_boundary_equals_the_cached_call(dtype):
     """Horizon 0, T = T0: the records give the cached call's split, hence its
     output bit for bit; so do the attention pass then zr_attn_combine."""
-    w = synth.make_workload(1, device="cuda")
+    w = synth.make_workload(1, device="cuda", overrides=dict(dtype=dtype) if dtype != "bf16"
+                            else None)
     st = zr.step_from_workload(w)
     st.step()
     st.cached_attn(w.window)
